@@ -1,0 +1,12 @@
+"""fp64 CPU oracle for block-sparse attention (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import
+this package; the product path never does.
+"""
+from .sparge_oracle import (  # noqa: F401
+    NEG_INF, attend, block_map, block_mean, block_self_similarity,
+    block_sparse_attention, cdf_count, combine, dense_attention,
+    lut_from_selection, pool_and_gate, pooled_scores, row_softmax,
+    select_from_probs, select_row, selection_order, token_list_attention,
+    topk_count,
+)

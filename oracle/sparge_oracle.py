@@ -1,0 +1,399 @@
+"""Plain fp64 CPU oracle for SpargeAttn-style block-sparse attention (forward).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The product path (the
+HIP library and its Python binding) never calls it and shares no code with it.
+
+Every function works in float64 on NumPy arrays and follows the pages'
+description step by step, with no blocking, fusion or reordering:
+
+* "Sparge Attention (Composable Kernel)" page, "Status vs Upstream" list: the
+  block-map pipeline is per-block mean-pool, cosine similarity, pooled QK, then
+  top-k / cdfthreshd block selection into a BlockMap LUT, with per-head
+  topk / simthreshd1 / cdfthreshd.
+* "Updating Log -- Speculative Sparse Attention" page, Stage 1: attention with a
+  natural-log LSE, the online-softmax combine of two partials
+  (FA(A u B) = Combine(FA(A), FA(B))) and the empty partial (LSE = -inf).
+  Stage 3: a row that selects no block writes O = 0 and LSE = -inf.
+* aiter pull request 6841 page (sorted-sparse MHA v4 LSE): an empty LUT row
+  exports LSE = -inf.
+* aiter pull request 4919 page (gfx950 sparse decode): -1 entries in an index
+  list are skipped; the reduce masks partials whose maximum is -inf.
+* llama.cpp pull request 10 page (Vulkan sparse prefill): index lists are
+  ascending; ties at a top-k threshold are emitted in ascending index order.
+
+Where the pages leave a step open, the reading taken is stated at the function
+(readings R1..R14 in the design notes).  Parity of these readings with the
+upstream SpargeAttn code is unpinned (no upstream code is available); the GPU
+path is pinned against this oracle.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+NEG_INF = -math.inf
+
+
+# ----------------------------------------------------------------------------
+# Stage 1: block map
+# ----------------------------------------------------------------------------
+
+def block_mean(x_blk: np.ndarray) -> np.ndarray:
+    """Mean token of one block: (1/n) * sum_i x_i.
+
+    CK page, "Status vs Upstream": per-block mean-pool.  Reading R1: a plain
+    mean over the block's tokens (every supported length is a multiple of the
+    block size, so there is no partial block).
+    """
+    x = np.asarray(x_blk, dtype=np.float64)
+    return x.sum(axis=0) / x.shape[0]
+
+
+def block_self_similarity(x_blk: np.ndarray) -> float:
+    """Mean pairwise cosine similarity of the block's tokens, diagonal included.
+
+    CK page, "Status vs Upstream": cosine similarity, gated by simthreshd1.
+    Reading R2: the average of all n*n cosines cos(x_i, x_j), i = j included.
+    A zero-norm token has no direction and contributes the zero vector.  The
+    average of the Gram matrix of unit vectors equals |sum_i xhat_i|^2 / n^2,
+    which is what is computed here.
+    """
+    x = np.asarray(x_blk, dtype=np.float64)
+    n = x.shape[0]
+    norms = np.sqrt((x * x).sum(axis=1))
+    xhat = np.zeros_like(x)
+    nz = norms > 0.0
+    xhat[nz] = x[nz] / norms[nz, None]
+    s = xhat.sum(axis=0)
+    return float(s @ s) / float(n * n)
+
+
+def pool_and_gate(x: np.ndarray, blk: int, simthreshd1: float):
+    """Pool one (b, h) slice x [s, d] into blocks of `blk` tokens.
+
+    Returns (means [nb, d], sims [nb], flags [nb] bool) where
+    flag = sim > simthreshd1 (reading R3: strict comparison).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    s, _ = x.shape
+    if s % blk != 0:
+        raise ValueError("sequence length must be a multiple of the block size")
+    nb = s // blk
+    means = np.stack([block_mean(x[i * blk:(i + 1) * blk]) for i in range(nb)])
+    sims = np.array([block_self_similarity(x[i * blk:(i + 1) * blk]) for i in range(nb)])
+    flags = sims > float(simthreshd1)
+    return means, sims, flags
+
+
+def pooled_scores(qbar: np.ndarray, kbar: np.ndarray, sim_k: np.ndarray,
+                  scale: float) -> np.ndarray:
+    """S[qb, kb] = scale * <qbar[qb], kbar[kb]>, and -inf on non-similar K blocks.
+
+    CK page, "Status vs Upstream": pooled QK.  Reading R4: the attention
+    softmax scale (1/sqrt(d) by default).  Reading R5: a K block that fails the
+    similarity gate is kept out of the pooled softmax (its column is -inf) and
+    is forced on later, in `select_row`.
+    """
+    s = float(scale) * (np.asarray(qbar, np.float64) @ np.asarray(kbar, np.float64).T)
+    s[:, ~np.asarray(sim_k, bool)] = NEG_INF
+    return s
+
+
+def row_softmax(scores: np.ndarray) -> np.ndarray:
+    """Softmax over the last axis in fp64; a row of all -inf maps to all zeros.
+
+    Reading R6: a row with every pooled score at -inf has no distribution; it is
+    set to zero (and every block of that row is then forced on by the gate).
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    out = np.zeros_like(s)
+    for idx in np.ndindex(*s.shape[:-1]):
+        row = s[idx]
+        m = row.max()
+        if m == NEG_INF:
+            continue
+        e = np.exp(row - m)
+        out[idx] = e / e.sum()
+    return out
+
+
+def topk_count(topk: float, nk: int) -> int:
+    """Number of blocks a top-k fraction selects: clamp(floor(topk * nk), 1, nk).
+
+    CK page, "Performance" and "Usage": topk is a fraction of the row (e.g.
+    -topk=0.4).  Reading R7: the fraction arrives as fp32; it is widened to
+    fp64, multiplied by nk and truncated.
+    """
+    n = int(math.floor(float(np.float32(topk)) * nk))
+    return min(max(n, 1), nk)
+
+
+def selection_order(prob_row: np.ndarray) -> np.ndarray:
+    """Block indices ordered by pooled probability, largest first.
+
+    Equal probabilities are ordered by ascending block index (the lower index
+    wins), as the Vulkan page emits ties at a top-k threshold in ascending index
+    order.
+    """
+    p = np.asarray(prob_row, dtype=np.float64)
+    kb = np.arange(p.shape[0])
+    return np.lexsort((kb, -p))
+
+
+def cdf_count(prob_row: np.ndarray, order: np.ndarray, cdfthreshd: float) -> int:
+    """Fewest leading blocks of `order` whose summed probability reaches the threshold.
+
+    CK page, "Status vs Upstream": cdfthreshd block selection.  Reading R8: the
+    running sum is accumulated one block at a time in fp64 in `order`; the
+    count is the first n >= 1 with sum >= cdfthreshd, else every block.
+    """
+    thr = float(np.float32(cdfthreshd))
+    c = 0.0
+    for n, kb in enumerate(order, start=1):
+        c = c + float(prob_row[kb])
+        if c >= thr:
+            return n
+    return len(order)
+
+
+def select_row(prob_row: np.ndarray, sim_q_flag: bool, sim_k: np.ndarray,
+               topk: float, cdfthreshd: Optional[float]) -> np.ndarray:
+    """Selected K blocks of one Q-tile row, ascending.
+
+    * If the Q block fails the similarity gate, every K block is selected
+      (reading R5: its mean does not stand for the block).
+    * Otherwise take the first n blocks of `selection_order`: n from
+      `topk_count` when topk > 0, else from `cdf_count` (reading R8: top-k wins
+      when both are set).
+    * Then add every K block that failed the gate (reading R9: these are
+      added after the count, so a row may hold more than n blocks).
+    """
+    nk = prob_row.shape[0]
+    if not sim_q_flag:
+        return np.arange(nk, dtype=np.int64)
+    order = selection_order(prob_row)
+    if topk is not None and float(np.float32(topk)) > 0.0:
+        n = topk_count(topk, nk)
+    else:
+        if cdfthreshd is None:
+            raise ValueError("either topk > 0 or cdfthreshd must be given")
+        n = cdf_count(prob_row, order, cdfthreshd)
+    chosen = set(int(kb) for kb in order[:n])
+    chosen |= set(int(kb) for kb in np.nonzero(~np.asarray(sim_k, bool))[0])
+    return np.array(sorted(chosen), dtype=np.int64)
+
+
+def lut_from_selection(rows: Sequence[np.ndarray], nk: int):
+    """Encode per-row selections as (lut [rows, nk] int32 ascending, -1 padded,
+    count [rows] int32, bitmap [rows, nk] uint8).  Reading R10."""
+    nrows = len(rows)
+    lut = np.full((nrows, nk), -1, dtype=np.int32)
+    count = np.zeros(nrows, dtype=np.int32)
+    bitmap = np.zeros((nrows, nk), dtype=np.uint8)
+    for r, sel in enumerate(rows):
+        sel = np.asarray(sel, dtype=np.int64)
+        lut[r, :len(sel)] = sel
+        count[r] = len(sel)
+        bitmap[r, sel] = 1
+    return lut, count, bitmap
+
+
+def select_from_probs(prob: np.ndarray, sim_q: np.ndarray, sim_k: np.ndarray,
+                      topk: Sequence[float], cdfthreshd: Optional[Sequence[float]]):
+    """Selection steps applied to given pooled probabilities and gate flags.
+
+    prob [b, h, nq, nk]; sim_q [b, h, nq]; sim_k [b, h, nk]; topk / cdfthreshd
+    per head.  Returns (lut, count, bitmap) shaped [b, h, nq, nk] / [b, h, nq].
+    Used both by `block_map` and to re-run the selection on probabilities and
+    flags produced elsewhere.
+    """
+    prob = np.asarray(prob, dtype=np.float64)
+    b, h, nq, nk = prob.shape
+    lut = np.full((b, h, nq, nk), -1, dtype=np.int32)
+    count = np.zeros((b, h, nq), dtype=np.int32)
+    bitmap = np.zeros((b, h, nq, nk), dtype=np.uint8)
+    for ib in range(b):
+        for ih in range(h):
+            cdf = None if cdfthreshd is None else cdfthreshd[ih]
+            rows = [select_row(prob[ib, ih, qb], bool(sim_q[ib, ih, qb]),
+                               sim_k[ib, ih], topk[ih], cdf) for qb in range(nq)]
+            l, c, m = lut_from_selection(rows, nk)
+            lut[ib, ih], count[ib, ih], bitmap[ib, ih] = l, c, m
+    return lut, count, bitmap
+
+
+def block_map(q: np.ndarray, k: np.ndarray, topk: Sequence[float],
+              simthreshd1: Sequence[float], cdfthreshd: Optional[Sequence[float]] = None,
+              blk_q: int = 64, blk_k: int = 64, scale: Optional[float] = None) -> dict:
+    """Whole stage 1 for q [b, h, s_q, d] and k [b, h, s_k, d].
+
+    Returns a dict with q_mean, k_mean, sim_q_val, sim_k_val, sim_q, sim_k,
+    scores, prob, lut, count, bitmap.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    b, h, s_q, d = q.shape
+    s_k = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nq, nk = s_q // blk_q, s_k // blk_k
+    q_mean = np.zeros((b, h, nq, d))
+    k_mean = np.zeros((b, h, nk, d))
+    sim_q_val = np.zeros((b, h, nq))
+    sim_k_val = np.zeros((b, h, nk))
+    sim_q = np.zeros((b, h, nq), dtype=bool)
+    sim_k = np.zeros((b, h, nk), dtype=bool)
+    scores = np.zeros((b, h, nq, nk))
+    for ib in range(b):
+        for ih in range(h):
+            q_mean[ib, ih], sim_q_val[ib, ih], sim_q[ib, ih] = pool_and_gate(
+                q[ib, ih], blk_q, simthreshd1[ih])
+            k_mean[ib, ih], sim_k_val[ib, ih], sim_k[ib, ih] = pool_and_gate(
+                k[ib, ih], blk_k, simthreshd1[ih])
+            scores[ib, ih] = pooled_scores(q_mean[ib, ih], k_mean[ib, ih],
+                                           sim_k[ib, ih], scale)
+    prob = row_softmax(scores)
+    lut, count, bitmap = select_from_probs(prob, sim_q, sim_k, topk, cdfthreshd)
+    return dict(q_mean=q_mean, k_mean=k_mean, sim_q_val=sim_q_val, sim_k_val=sim_k_val,
+               sim_q=sim_q, sim_k=sim_k, scores=scores, prob=prob,
+               lut=lut, count=count, bitmap=bitmap)
+
+
+# ----------------------------------------------------------------------------
+# Stage 2: attention over the selected keys, and the LSE combine
+# ----------------------------------------------------------------------------
+
+def attend(qi: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float):
+    """Exact softmax attention of query rows qi [m, d] over keys/values [n, d].
+
+    LSE is the natural log of sum_j exp(scale * q.k_j) (reading R11: the scale is
+    inside the LSE).  With no keys, O = 0 and LSE = -inf (Updating Log page,
+    Stage 3; aiter 6841 page; reading R12).
+    """
+    qi = np.asarray(qi, np.float64)
+    m_rows = qi.shape[0]
+    if keys.shape[0] == 0:
+        return np.zeros((m_rows, values.shape[1])), np.full(m_rows, NEG_INF)
+    s = float(scale) * (qi @ np.asarray(keys, np.float64).T)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    lse = (m + np.log(l))[:, 0]
+    o = (e @ np.asarray(values, np.float64)) / l
+    return o, lse
+
+
+def block_sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                           lut: Optional[np.ndarray], count: Optional[np.ndarray],
+                           blk_q: int = 64, blk_k: int = 64,
+                           scale: Optional[float] = None, lut_per_kv_head: bool = False):
+    """Attention of every Q-tile over the K blocks its LUT row lists.
+
+    q [b, h_q, s_q, d]; k, v [b, h_kv, s_k, d]; query head j reads KV head
+    j // (h_q / h_kv) (aiter 6841 page, GQA mapping).  lut [b, h_lut, nq, L]
+    with count [b, h_lut, nq]; h_lut = h_kv when `lut_per_kv_head`, else h_q.
+    lut = None means every block (dense).  Returns O [b, h_q, s_q, d], LSE
+    [b, h_q, s_q].
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    b, h_q, s_q, d = q.shape
+    h_kv, s_k = k.shape[1], k.shape[2]
+    ratio = h_q // h_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nq, nk = s_q // blk_q, s_k // blk_k
+    o = np.zeros((b, h_q, s_q, v.shape[3]))
+    lse = np.zeros((b, h_q, s_q))
+    for ib in range(b):
+        for ih in range(h_q):
+            hk = ih // ratio
+            hl = hk if lut_per_kv_head else ih
+            for qb in range(nq):
+                if lut is None:
+                    blocks = np.arange(nk)
+                else:
+                    n = int(count[ib, hl, qb])
+                    blocks = np.asarray(lut[ib, hl, qb, :n], dtype=np.int64)
+                idx = (blocks[:, None] * blk_k + np.arange(blk_k)[None, :]).reshape(-1)
+                rows = slice(qb * blk_q, (qb + 1) * blk_q)
+                o[ib, ih, rows], lse[ib, ih, rows] = attend(
+                    q[ib, ih, rows], k[ib, hk, idx], v[ib, hk, idx], scale)
+    return o, lse
+
+
+def token_list_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                         lists: np.ndarray, scale: Optional[float] = None):
+    """Decode-style attention over per-(b, KV head) token index lists.
+
+    q [b, h_q, s_q, d] (s_q usually 1); k, v [b, h_kv, s_k, d]; lists
+    [b, h_kv, L] int with -1 = skip (aiter 4919 page: -1 sentinels; reading
+    R14: one list per KV head, shared by its query-head group, applied to
+    every query position).  Query head j reads KV head j // (h_q / h_kv).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    b, h_q, s_q, d = q.shape
+    h_kv = k.shape[1]
+    ratio = h_q // h_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = np.zeros((b, h_q, s_q, v.shape[3]))
+    lse = np.zeros((b, h_q, s_q))
+    for ib in range(b):
+        for ih in range(h_q):
+            hk = ih // ratio
+            row = np.asarray(lists[ib, hk], dtype=np.int64)
+            idx = row[row >= 0]
+            o[ib, ih], lse[ib, ih] = attend(q[ib, ih], k[ib, hk, idx], v[ib, hk, idx], scale)
+    return o, lse
+
+
+def combine(o_parts: Sequence[np.ndarray], lse_parts: Sequence[np.ndarray]):
+    """Merge partial attention results by their LSE.
+
+    Updating Log page, Stage 1: Combine(FA(A), FA(B)) = FA(A u B) with the
+    running-max trick; an empty partial (LSE = -inf) is the identity.  aiter
+    4919 page: partials whose maximum is -inf are masked before the
+    exponential.  Reading R13: when every partial is -inf the result is O = 0,
+    LSE = -inf.
+
+    o_parts: n arrays [..., d]; lse_parts: n arrays [...].
+    """
+    lse = np.stack([np.asarray(x, np.float64) for x in lse_parts])   # [n, ...]
+    o = np.stack([np.asarray(x, np.float64) for x in o_parts])       # [n, ..., d]
+    m = lse.max(axis=0)                                              # [...]
+    finite = lse > NEG_INF
+    safe_m = np.where(m > NEG_INF, m, 0.0)
+    w = np.where(finite, np.exp(np.where(finite, lse, 0.0) - safe_m), 0.0)
+    total = w.sum(axis=0)
+    empty = ~(total > 0.0)
+    denom = np.where(empty, 1.0, total)
+    out = (w[..., None] * o).sum(axis=0) / denom[..., None]
+    out[empty] = 0.0
+    lse_out = np.where(empty, NEG_INF, safe_m + np.log(denom))
+    return out, lse_out
+
+
+def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                    scale: Optional[float] = None):
+    """softmax(scale * Q K^T) V and its LSE over every key, per (b, h); the
+    definition the sparse path reduces to when every block is selected."""
+    q = np.asarray(q, np.float64)
+    b, h_q, s_q, d = q.shape
+    h_kv = k.shape[1]
+    ratio = h_q // h_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = np.zeros((b, h_q, s_q, v.shape[3]))
+    lse = np.zeros((b, h_q, s_q))
+    for ib in range(b):
+        for ih in range(h_q):
+            o[ib, ih], lse[ib, ih] = attend(q[ib, ih], np.asarray(k[ib, ih // ratio], np.float64),
+                                            np.asarray(v[ib, ih // ratio], np.float64), scale)
+    return o, lse

@@ -1,0 +1,274 @@
+// Host entry points of the C ABI declared in include/sparge.h.
+//
+// Every call validates its arguments on the host first; on any error nothing is
+// enqueued, the status is returned and the message is kept per thread for
+// sparge_last_error().  Valid calls only enqueue kernels on the caller's stream:
+// the library never allocates, frees or synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace sparge;
+
+namespace {
+
+thread_local std::string g_error;
+
+sparge_status fail(sparge_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+sparge_status ok() {
+  g_error.clear();
+  return SPARGE_OK;
+}
+
+sparge_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(SPARGE_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+  return ok();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Strides of a [b, h, s, d] tensor: non-negative, rows 16-byte aligned.
+sparge_status check_strides(const char* name, const int64_t* st) {
+  if (!st) return fail(SPARGE_ERR_INVALID, "%s strides are null", name);
+  for (int i = 0; i < 3; ++i) {
+    if (st[i] < 0) return fail(SPARGE_ERR_INVALID, "%s stride %d is negative", name, i);
+    if (st[i] % 8 != 0)
+      return fail(SPARGE_ERR_INVALID, "%s stride %d (%lld elements) does not keep rows 16-byte aligned",
+                  name, i, (long long)st[i]);
+  }
+  return SPARGE_OK;
+}
+
+bool is_half(sparge_dtype dt) { return dt == SPARGE_F16 || dt == SPARGE_BF16; }
+
+struct BlockMapLayout {
+  size_t q_mean, k_mean, sim_q, sim_k, total;
+};
+
+BlockMapLayout block_map_layout(int b, int h, int s_q, int s_k, int d) {
+  const size_t nq = (size_t)s_q / 64, nk = (size_t)s_k / 64, bh = (size_t)b * h;
+  BlockMapLayout l;
+  size_t off = 0;
+  l.q_mean = off; off = align256(off + bh * nq * d * sizeof(float));
+  l.k_mean = off; off = align256(off + bh * nk * d * sizeof(float));
+  l.sim_q = off;  off = align256(off + bh * nq);
+  l.sim_k = off;  off = align256(off + bh * nk);
+  l.total = off;
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparge_abi_version(void) { return 1; }
+
+const char* sparge_last_error(void) { return g_error.c_str(); }
+
+size_t sparge_build_block_map_workspace(int b, int h, int s_q, int s_k, int d, int blk_q, int blk_k) {
+  if (b <= 0 || h <= 0 || s_q <= 0 || s_k <= 0 || (d != 64 && d != 128)) return 0;
+  if (blk_q != 64 || blk_k != 64 || s_q % 64 || s_k % 64) return 0;
+  return block_map_layout(b, h, s_q, s_k, d).total;
+}
+
+sparge_status sparge_build_block_map(
+    const void* q, const void* k, sparge_dtype dt, int b, int h, int s_q, int s_k, int d,
+    const int64_t q_strides[3], const int64_t k_strides[3], int blk_q, int blk_k,
+    const float* topk, const float* cdfthreshd, const float* simthreshd1, float softmax_scale,
+    int32_t* lut, int32_t* lut_count, uint8_t* block_map, float* pooled_prob, uint8_t* sim_q,
+    uint8_t* sim_k, float* q_mean, float* k_mean, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  if (!q || !k) return fail(SPARGE_ERR_INVALID, "q and k must be non-null");
+  if (!lut || !lut_count) return fail(SPARGE_ERR_INVALID, "lut and lut_count must be non-null");
+  if (!topk || !simthreshd1) return fail(SPARGE_ERR_INVALID, "topk and simthreshd1 must be non-null");
+  if (!is_half(dt)) return fail(SPARGE_ERR_UNSUPPORTED, "q/k dtype must be F16 or BF16");
+  if (b <= 0 || h <= 0 || s_q <= 0 || s_k <= 0 || d <= 0)
+    return fail(SPARGE_ERR_INVALID, "sizes must be positive (b=%d h=%d s_q=%d s_k=%d d=%d)", b, h, s_q, s_k, d);
+  if (d != 64 && d != 128) return fail(SPARGE_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", d);
+  if (blk_q != 64 || blk_k != 64)
+    return fail(SPARGE_ERR_UNSUPPORTED, "block map needs blk_q = blk_k = 64 (got %d, %d)", blk_q, blk_k);
+  if (s_q % 64 || s_k % 64)
+    return fail(SPARGE_ERR_UNSUPPORTED, "ragged sequence (s_q=%d, s_k=%d) is not a multiple of 64", s_q, s_k);
+  if (h > SPARGE_MAX_HEADS) return fail(SPARGE_ERR_UNSUPPORTED, "h=%d exceeds %d", h, SPARGE_MAX_HEADS);
+  const int nq = s_q / 64, nk = s_k / 64;
+  if (nk > SPARGE_MAX_KBLOCKS)
+    return fail(SPARGE_ERR_UNSUPPORTED, "nk=%d K blocks exceeds %d", nk, SPARGE_MAX_KBLOCKS);
+  sparge_status st;
+  if ((st = check_strides("q", q_strides)) != SPARGE_OK) return st;
+  if ((st = check_strides("k", k_strides)) != SPARGE_OK) return st;
+  if (!aligned16(q) || !aligned16(k)) return fail(SPARGE_ERR_INVALID, "q/k must be 16-byte aligned");
+  if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale))
+    return fail(SPARGE_ERR_INVALID, "softmax_scale must be finite and >= 0");
+  const BlockMapLayout lay = block_map_layout(b, h, s_q, s_k, d);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(SPARGE_ERR_INVALID, "workspace of %zu bytes needed (got %zu)", lay.total, workspace_bytes);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(SPARGE_ERR_INVALID, "workspace must be 256-byte aligned");
+  if ((q_mean && ((uintptr_t)q_mean & 15u)) || (k_mean && ((uintptr_t)k_mean & 15u)))
+    return fail(SPARGE_ERR_INVALID, "q_mean/k_mean must be 16-byte aligned");
+
+  PoolArgs pa;
+  SelectArgs sa;
+  for (int i = 0; i < h; ++i) {
+    const float tk = topk[i], thr = simthreshd1[i];
+    if (!isfinite(tk) || tk > 1.f) return fail(SPARGE_ERR_INVALID, "topk[%d]=%g must be finite and <= 1", i, tk);
+    if (!isfinite(thr)) return fail(SPARGE_ERR_INVALID, "simthreshd1[%d] is not finite", i);
+    pa.thr[i] = thr;
+    if (tk > 0.f) {
+      long n = (long)floor((double)tk * (double)nk);
+      if (n < 1) n = 1;
+      if (n > nk) n = nk;
+      sa.nsel[i] = (int)n;
+      sa.cdf[i] = 0.f;
+    } else {
+      if (!cdfthreshd) return fail(SPARGE_ERR_INVALID, "topk[%d] <= 0 needs cdfthreshd", i);
+      const float c = cdfthreshd[i];
+      if (!isfinite(c) || !(c > 0.f) || c > 1.f)
+        return fail(SPARGE_ERR_INVALID, "cdfthreshd[%d]=%g must be in (0, 1]", i, c);
+      sa.nsel[i] = 0;
+      sa.cdf[i] = c;
+    }
+  }
+  for (int i = h; i < SPARGE_MAX_HEADS; ++i) { pa.thr[i] = 0.f; sa.nsel[i] = 1; sa.cdf[i] = 0.f; }
+
+  char* ws = reinterpret_cast<char*>(workspace);
+  pa.q = q;
+  pa.k = k;
+  for (int i = 0; i < 3; ++i) { pa.qs[i] = q_strides[i]; pa.ks[i] = k_strides[i]; }
+  pa.b = b; pa.h = h; pa.nq = nq; pa.nk = nk;
+  pa.q_mean = q_mean ? q_mean : reinterpret_cast<float*>(ws + lay.q_mean);
+  pa.k_mean = k_mean ? k_mean : reinterpret_cast<float*>(ws + lay.k_mean);
+  pa.sim_q = sim_q ? sim_q : reinterpret_cast<uint8_t*>(ws + lay.sim_q);
+  pa.sim_k = sim_k ? sim_k : reinterpret_cast<uint8_t*>(ws + lay.sim_k);
+
+  sa.q_mean = pa.q_mean; sa.k_mean = pa.k_mean; sa.sim_q = pa.sim_q; sa.sim_k = pa.sim_k;
+  sa.b = b; sa.h = h; sa.nq = nq; sa.nk = nk;
+  sa.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
+  sa.lut = lut; sa.count = lut_count; sa.bmap = block_map; sa.prob = pooled_prob;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_pool_sim(pa, dt, d, s);
+  if (e != hipSuccess) return hip_status(e, "pool_sim launch");
+  e = launch_score_select(sa, d, s);
+  return hip_status(e, "score_select launch");
+}
+
+sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                              sparge_dtype dt, sparge_dtype o_dt, int b, int h_q, int h_kv, int s_q,
+                              int s_k, int d, const int64_t q_strides[3], const int64_t k_strides[3],
+                              const int64_t v_strides[3], const int64_t o_strides[3], int blk_q,
+                              int blk_k, const int32_t* lut, const int32_t* lut_count, int lut_row_len,
+                              int lut_heads, float softmax_scale, int num_splits,
+                              int64_t o_split_stride, void* stream) {
+  if (!q || !k || !v || !o) return fail(SPARGE_ERR_INVALID, "q, k, v and o must be non-null");
+  if (!is_half(dt)) return fail(SPARGE_ERR_UNSUPPORTED, "input dtype must be F16 or BF16");
+  if (o_dt != dt && o_dt != SPARGE_F32)
+    return fail(SPARGE_ERR_UNSUPPORTED, "output dtype must equal the input dtype or be F32");
+  if (b <= 0 || h_q <= 0 || h_kv <= 0 || s_q <= 0 || s_k <= 0 || d <= 0)
+    return fail(SPARGE_ERR_INVALID, "sizes must be positive");
+  if (h_q % h_kv != 0) return fail(SPARGE_ERR_INVALID, "h_q=%d is not a multiple of h_kv=%d", h_q, h_kv);
+  if (d != 64 && d != 128) return fail(SPARGE_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", d);
+  sparge_status st;
+  if ((st = check_strides("q", q_strides)) != SPARGE_OK) return st;
+  if ((st = check_strides("k", k_strides)) != SPARGE_OK) return st;
+  if ((st = check_strides("v", v_strides)) != SPARGE_OK) return st;
+  if ((st = check_strides("o", o_strides)) != SPARGE_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(SPARGE_ERR_INVALID, "q/k/v/o must be 16-byte aligned");
+  if (num_splits < 1 || num_splits > 1024) return fail(SPARGE_ERR_INVALID, "num_splits=%d out of [1, 1024]", num_splits);
+  if (num_splits > 1 && !lse) return fail(SPARGE_ERR_INVALID, "split partials need an lse output");
+  if (num_splits > 1 && (o_split_stride <= 0 || o_split_stride % 8))
+    return fail(SPARGE_ERR_INVALID, "o_split_stride must be a positive multiple of 8 elements");
+  if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale))
+    return fail(SPARGE_ERR_INVALID, "softmax_scale must be finite and >= 0");
+  const bool token_mode = blk_q == 1 && blk_k == 1;
+  const bool block_mode = blk_q == 64 && blk_k == 64;
+  if (!token_mode && !block_mode)
+    return fail(SPARGE_ERR_UNSUPPORTED, "blocks (%d, %d) not built: use (64, 64) or (1, 1)", blk_q, blk_k);
+  if (lut) {
+    if (lut_row_len <= 0) return fail(SPARGE_ERR_INVALID, "lut_row_len must be positive");
+    if (lut_heads != h_q && lut_heads != h_kv)
+      return fail(SPARGE_ERR_INVALID, "lut_heads=%d must be h_q=%d or h_kv=%d", lut_heads, h_q, h_kv);
+  }
+
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
+  FmhaArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = q_strides[i]; a.ks[i] = k_strides[i]; a.vs[i] = v_strides[i]; a.os[i] = o_strides[i];
+  }
+  a.b = b; a.hq = h_q; a.hkv = h_kv; a.sq = s_q; a.sk = s_k;
+  a.ratio = h_q / h_kv;
+  a.lut = lut; a.cnt = lut_count; a.lut_row_len = lut_row_len; a.lut_heads = lut_heads;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.splits = num_splits;
+  a.o_split_stride = num_splits > 1 ? o_split_stride : 0;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  if (block_mode) {
+    if (s_q % 64 || s_k % 64)
+      return fail(SPARGE_ERR_UNSUPPORTED, "ragged sequence (s_q=%d, s_k=%d) is not a multiple of 64", s_q, s_k);
+    a.nqt = s_q / 64;
+    a.nkb = s_k / 64;
+    if (!lut && lut_count) return fail(SPARGE_ERR_INVALID, "lut_count given without lut");
+    return hip_status(launch_fmha_block(a, dt, o_dt, d, s), "sparse_fmha launch");
+  }
+  // token-list mode
+  if (!lut) return fail(SPARGE_ERR_INVALID, "token-list mode needs an index list");
+  if (lut_count) return fail(SPARGE_ERR_INVALID, "token-list mode takes no lut_count");
+  if (lut_heads != h_kv)
+    return fail(SPARGE_ERR_UNSUPPORTED, "token-list mode needs one list per KV head (lut_heads = h_kv)");
+  const int rows = a.ratio * s_q;
+  if (rows > 8)
+    return fail(SPARGE_ERR_UNSUPPORTED, "token-list mode serves at most 8 query rows per KV head (got %d)", rows);
+  a.nqt = s_q;
+  a.nkb = s_k;
+  return hip_status(launch_fmha_tokens(a, dt, o_dt, d, rows, s), "sparse_fmha token launch");
+}
+
+sparge_status attn_combine(const void* o_parts, sparge_dtype part_dt, const float* lse_parts, int n_parts,
+                           int b, int h, int s, int d, int64_t part_stride, void* o, sparge_dtype out_dt,
+                           float* lse_out, void* stream) {
+  if (!o_parts || !lse_parts || !o) return fail(SPARGE_ERR_INVALID, "o_parts, lse_parts and o must be non-null");
+  if (n_parts < 1 || n_parts > 256) return fail(SPARGE_ERR_INVALID, "n_parts=%d out of [1, 256]", n_parts);
+  if (b <= 0 || h <= 0 || s <= 0 || d <= 0) return fail(SPARGE_ERR_INVALID, "sizes must be positive");
+  if (d != 64 && d != 128) return fail(SPARGE_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", d);
+  if (part_dt != SPARGE_F32 && !is_half(part_dt)) return fail(SPARGE_ERR_INVALID, "bad part dtype");
+  if (out_dt != SPARGE_F32 && !is_half(out_dt)) return fail(SPARGE_ERR_INVALID, "bad output dtype");
+  const int64_t rows = (int64_t)b * h * s;
+  if (part_stride < rows * d) return fail(SPARGE_ERR_INVALID, "part_stride smaller than one part");
+  if (part_stride % 8) return fail(SPARGE_ERR_INVALID, "part_stride must be a multiple of 8 elements");
+  if (!aligned16(o_parts) || !aligned16(o)) return fail(SPARGE_ERR_INVALID, "o_parts/o must be 16-byte aligned");
+  CombineArgs a;
+  a.parts = o_parts; a.lse_parts = lse_parts; a.n_parts = n_parts; a.rows = rows;
+  a.part_stride = part_stride; a.o = o; a.lse_out = lse_out;
+  return hip_status(launch_combine(a, part_dt, out_dt, d, reinterpret_cast<hipStream_t>(stream)),
+                    "attn_combine launch");
+}
+
+sparge_status sparge_validate_lut(const int32_t* lut, const int32_t* lut_count, int64_t rows, int row_len,
+                                  int n_blocks, int32_t* bad_rows, void* stream) {
+  if (!lut || !bad_rows) return fail(SPARGE_ERR_INVALID, "lut and bad_rows must be non-null");
+  if (rows <= 0 || row_len <= 0 || n_blocks <= 0) return fail(SPARGE_ERR_INVALID, "sizes must be positive");
+  return hip_status(launch_validate_lut(lut, lut_count, rows, row_len, n_blocks, bad_rows,
+                                        reinterpret_cast<hipStream_t>(stream)),
+                    "validate_lut launch");
+}
+
+}  // extern "C"

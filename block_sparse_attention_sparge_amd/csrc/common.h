@@ -1,0 +1,93 @@
+// Device helpers shared by the gfx950 kernels of the block-sparse attention
+// library: element types, conversions, 64-lane wavefront reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sparge.h"
+
+namespace sparge {
+
+typedef _Float16 half_t;
+typedef __bf16 bf16_t;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// Input element types: 16-bit storage with fp32 arithmetic.
+struct F16 {
+  typedef half_t T;
+  typedef half8 V8;
+  static __device__ __forceinline__ float to_f(T x) { return (float)x; }
+  static __device__ __forceinline__ T from_f(float x) { return (T)x; }
+  // Convert the low / high 16-bit lane of a packed word.
+  static __device__ __forceinline__ float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(half_t, (uint16_t)(w & 0xFFFFu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(half_t, (uint16_t)(w >> 16));
+  }
+  // Pack two floats (round to nearest even) into one word, a in the low half.
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    uint16_t ua = __builtin_bit_cast(uint16_t, (half_t)a);
+    uint16_t ub = __builtin_bit_cast(uint16_t, (half_t)b);
+    return (uint32_t)ua | ((uint32_t)ub << 16);
+  }
+};
+
+struct BF16 {
+  typedef bf16_t T;
+  typedef bf16x8 V8;
+  static __device__ __forceinline__ float to_f(T x) { return (float)x; }
+  static __device__ __forceinline__ T from_f(float x) { return (T)x; }
+  static __device__ __forceinline__ float lo(uint32_t w) {
+    return __builtin_bit_cast(float, w << 16);
+  }
+  static __device__ __forceinline__ float hi(uint32_t w) {
+    return __builtin_bit_cast(float, w & 0xFFFF0000u);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    uint16_t ua = __builtin_bit_cast(uint16_t, (bf16_t)a);
+    uint16_t ub = __builtin_bit_cast(uint16_t, (bf16_t)b);
+    return (uint32_t)ua | ((uint32_t)ub << 16);
+  }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int t = __shfl_up(v, off, kWave);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void store16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+}  // namespace sparge

@@ -1,0 +1,533 @@
+// Stage 2 of SpargeAttn-style block-sparse attention on gfx950: sparse flash
+// attention forward over a per-Q-tile list of K/V blocks, with LSE export.
+//
+// What is computed ("Updating Log -- Speculative Sparse Attention" page,
+// Stage 3, and the aiter 6841 page): for each query row, an online softmax
+// over the keys of the listed blocks; O = sum_j softmax_j v_j and the
+// natural-log LSE; a list with no block writes O = 0 and LSE = -inf.
+//
+// Block kernel (blk_q = blk_k = 64), one workgroup of two wavefronts per
+// (Q-tile, head, batch, split).  Each wavefront owns 32 query rows and works
+// in the transposed orientation S^T = K Q^T, O^T += V^T P^T on the
+// 32x32x16 fp16/bf16 MFMA:
+//   * Q^T stays in registers as the B operand for the whole row;
+//   * the K block is staged row-major in LDS (A operand of S^T, 16-byte
+//     reads); the V block is staged transposed (V^T, A operand of O^T) with
+//     its key order permuted so that each lane's 8 keys are one 16-byte read;
+//   * the S^T accumulator already has the layout of the P^T B operand, so P
+//     goes from softmax to the PV MFMA without leaving registers, and every
+//     row reduction is in-lane plus one exchange with the partner half-wave;
+//   * the softmax runs in base 2 with the scale folded in once (aiter 4919
+//     page: one FMA per score, exp2), and the row sum is finished only at the
+//     end (one reciprocal per row);
+//   * the next block's K/V loads are issued into registers before the current
+//     block's MFMAs, so global latency overlaps compute;
+//   * workgroups are renumbered so that consecutive rows of one head land on
+//     one XCD and share its L2 (aiter 4919 page: workgroups round-robin over
+//     the 8 XCDs by linear id).
+//
+// Token-list kernel (blk_q = blk_k = 1, decode): one workgroup per (batch, KV
+// head, split) serves the query heads of that KV head (aiter 6841 page: query
+// head j reads KV head j / ratio) over an index list in which -1 entries are
+// skipped (aiter 4919 page).  Keys are gathered 64 at a time; scores and the
+// PV update run on the vector ALUs in fp32.
+#include "common.h"
+#include "kernels.h"
+
+namespace sparge {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Workgroups are dispatched to the 8 XCDs round-robin by linear id; give every
+// XCD a contiguous range of logical ids (grid is a multiple of 8).
+__device__ __forceinline__ int64_t xcd_remap(int64_t pid, int64_t grid) {
+  const int64_t per = grid >> 3;
+  return (pid & 7) * per + (pid >> 3);
+}
+
+// Index of the first negative entry of a LUT row (or its length), by one wave.
+__device__ __forceinline__ int first_negative(const int32_t* row, int len, int lane) {
+  int first = len;
+  for (int i = lane; i < len; i += kWave) {
+    if (row[i] < 0) { first = i; break; }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) first = min(first, __shfl_xor(first, m, kWave));
+  return first;
+}
+
+// Position of key kappa (0..63) inside a V^T row: the 8 keys lane-half h uses
+// in PV k-step ks (keys 16ks + 8(e/4) + 4h + e%4, e = 0..7) become contiguous.
+__device__ __forceinline__ int vt_pos(int kappa) {
+  return 16 * (kappa >> 4) + 8 * ((kappa >> 2) & 1) + 4 * ((kappa >> 3) & 1) + (kappa & 3);
+}
+
+template <class E>
+__device__ __forceinline__ floatx16 mfma32(const u32x4& a, const u32x4& b, const floatx16& c);
+
+template <>
+__device__ __forceinline__ floatx16 mfma32<F16>(const u32x4& a, const u32x4& b, const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a),
+                                                __builtin_bit_cast(half8, b), c, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ floatx16 mfma32<BF16>(const u32x4& a, const u32x4& b, const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <class E, bool OUT_F32>
+__device__ __forceinline__ void store4(void* base, int64_t off, float x0, float x1, float x2, float x3) {
+  if constexpr (OUT_F32) {
+    floatx4 v = {x0, x1, x2, x3};
+    *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(base) + off) = v;
+  } else {
+    u32x2 v = {E::pack2(x0, x1), E::pack2(x2, x3)};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<typename E::T*>(base) + off) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// block-LUT kernel
+// ---------------------------------------------------------------------------
+template <class E, int D, bool OUT_F32>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void fmha_block_kernel(FmhaArgs a) {
+  typedef typename E::T T;
+  constexpr int KP = D + 8;          // K tile pitch (elements)
+  constexpr int VP = 64 + 8;         // V^T tile pitch (elements)
+  constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
+  constexpr int RPP = 128 / CPR;     // K rows per staging pass
+  constexpr int NPASS = 64 / RPP;    // K staging passes
+  constexpr int NUV = D / 64;        // V units (4 keys x 8 d) per thread
+  constexpr int NKK = D / 16;        // k-steps of S^T
+  constexpr int NMD = D / 32;        // M-tiles of O^T
+  __shared__ __attribute__((aligned(16))) T sK[64 * KP];
+  __shared__ __attribute__((aligned(16))) T sV[D * VP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+
+  const int64_t G = (int64_t)a.nqt * a.hq * a.b * a.splits;
+  int64_t lin = xcd_remap(blockIdx.x, gridDim.x);
+  if (lin >= G) return;
+  const int qt = (int)(lin % a.nqt);
+  lin /= a.nqt;
+  const int hh = (int)(lin % a.hq);
+  lin /= a.hq;
+  const int bb = (int)(lin % a.b);
+  const int split = (int)(lin / a.b);
+  const int hk = hh / a.ratio;
+
+  int n;
+  const int32_t* list = nullptr;
+  if (a.lut) {
+    const int hlut = a.lut_heads == a.hq ? hh : hk;
+    const int64_t row = ((int64_t)bb * a.lut_heads + hlut) * a.nqt + qt;
+    list = a.lut + row * a.lut_row_len;
+    n = a.cnt ? a.cnt[row] : first_negative(list, a.lut_row_len, lane);
+  } else {
+    n = a.nkb;
+  }
+  const int chunk = (n + a.splits - 1) / a.splits;
+  const int beg = split * chunk;
+  const int nloc = max(0, min(n, beg + chunk) - beg);
+
+  const int q0 = qt * 64 + wave * 32;
+  const int64_t orow = (int64_t)split * a.o_split_stride + bb * a.os[0] + hh * a.os[1] +
+                       (int64_t)(q0 + l32) * a.os[2];
+  float* lse_row = a.lse ? a.lse + (((int64_t)split * a.b + bb) * a.hq + hh) * a.sq : nullptr;
+
+  if (nloc == 0) {
+    for (int d0 = hl * (D / 2); d0 < (hl + 1) * (D / 2); d0 += 4)
+      store4<E, OUT_F32>(a.o, orow + d0, 0.f, 0.f, 0.f, 0.f);
+    if (lse_row && hl == 0) lse_row[q0 + l32] = -INFINITY;
+    return;
+  }
+
+  // Q^T fragments (B operand): lane (query l32, half hl) holds d = 16kk + 8hl .. +7.
+  const T* qp = reinterpret_cast<const T*>(a.q) + bb * a.qs[0] + hh * a.qs[1] +
+                (int64_t)(q0 + l32) * a.qs[2] + 8 * hl;
+  u32x4 qf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) qf[kk] = load16(qp + 16 * kk);
+
+  const T* kbase = reinterpret_cast<const T*>(a.k) + bb * a.ks[0] + hk * a.ks[1];
+  const T* vbase = reinterpret_cast<const T*>(a.v) + bb * a.vs[0] + hk * a.vs[1];
+  const int64_t ks2 = a.ks[2], vs2 = a.vs[2];
+  const int kc = tid % CPR, kr = tid / CPR;
+
+  u32x4 kreg[NPASS];
+  u32x4 vreg[4 * NUV];
+  auto load_block = [&](int kb) {
+    const T* kp = kbase + (int64_t)kb * 64 * ks2 + kc * 8;
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) kreg[p] = load16(kp + (int64_t)(kr + p * RPP) * ks2);
+    const T* vp = vbase + (int64_t)kb * 64 * vs2;
+#pragma unroll
+    for (int i = 0; i < NUV; ++i) {
+      const int u = tid + 128 * i;
+      const int c = u % CPR, g = u / CPR;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vreg[4 * i + j] = load16(vp + (int64_t)(4 * g + j) * vs2 + c * 8);
+    }
+  };
+  auto store_block = [&]() {
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p)
+      *reinterpret_cast<u32x4*>(&sK[(kr + p * RPP) * KP + kc * 8]) = kreg[p];
+#pragma unroll
+    for (int i = 0; i < NUV; ++i) {
+      const int u = tid + 128 * i;
+      const int c = u % CPR, g = u / CPR;
+      const int pos = vt_pos(4 * g);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t k0 = vreg[4 * i][w], k1 = vreg[4 * i + 1][w];
+        const uint32_t k2 = vreg[4 * i + 2][w], k3 = vreg[4 * i + 3][w];
+        const u32x2 ev = {(k0 & 0xFFFFu) | (k1 << 16), (k2 & 0xFFFFu) | (k3 << 16)};
+        const u32x2 od = {(k0 >> 16) | (k1 & 0xFFFF0000u), (k2 >> 16) | (k3 & 0xFFFF0000u)};
+        *reinterpret_cast<u32x2*>(&sV[(c * 8 + 2 * w) * VP + pos]) = ev;
+        *reinterpret_cast<u32x2*>(&sV[(c * 8 + 2 * w + 1) * VP + pos]) = od;
+      }
+    }
+  };
+
+  floatx16 acc_o[NMD];
+#pragma unroll
+  for (int i = 0; i < NMD; ++i) acc_o[i] = floatx16{};
+  float m_run = -INFINITY;   // running row maximum, already times scale*log2(e)
+  float l_run = 0.f;         // this half-wave's share of the row sum
+  const float c2 = a.scale_log2;
+
+  int kb_next = list ? list[beg] : beg;
+  load_block(kb_next);
+#pragma unroll 1
+  for (int it = 0; it < nloc; ++it) {
+    if (it > 0) __syncthreads();
+    store_block();
+    __syncthreads();
+    if (it + 1 < nloc) {
+      kb_next = list ? list[beg + it + 1] : beg + it + 1;
+      load_block(kb_next);
+    }
+
+    // S^T = K Q^T : two 32-key M-tiles.
+    floatx16 s[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      s[mt] = floatx16{};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const u32x4 af = *reinterpret_cast<const u32x4*>(&sK[(32 * mt + l32) * KP + 16 * kk + 8 * hl]);
+        s[mt] = mfma32<E>(af, qf[kk], s[mt]);
+      }
+    }
+
+    // Online softmax in base 2; this lane holds 32 of the row's 64 scores.
+    float rmax = s[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) rmax = fmaxf(rmax, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[1][r]);
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 32, kWave));
+    const float m_new = fmaxf(m_run, rmax * c2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[mt][r], c2, -m_new));
+        s[mt][r] = p;
+        psum += p;
+      }
+    }
+    l_run = fmaf(l_run, alpha, psum);
+#pragma unroll
+    for (int i = 0; i < NMD; ++i) acc_o[i] *= alpha;
+
+    // P^T fragments: k-step ks uses registers 8(ks%2)..+7 of tile ks/2.
+    u32x4 pf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        pf[ks][w] = E::pack2(s[ks >> 1][8 * (ks & 1) + 2 * w], s[ks >> 1][8 * (ks & 1) + 2 * w + 1]);
+    }
+
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int md = 0; md < NMD; ++md) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 af = *reinterpret_cast<const u32x4*>(&sV[(32 * md + l32) * VP + 16 * ks + 8 * hl]);
+        acc_o[md] = mfma32<E>(af, pf[ks], acc_o[md]);
+      }
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+#pragma unroll
+  for (int md = 0; md < NMD; ++md) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * md + 8 * g + 4 * hl;
+      store4<E, OUT_F32>(a.o, orow + d0, acc_o[md][4 * g] * inv, acc_o[md][4 * g + 1] * inv,
+                         acc_o[md][4 * g + 2] * inv, acc_o[md][4 * g + 3] * inv);
+    }
+  }
+  if (lse_row && hl == 0) lse_row[q0 + l32] = (m_run + __log2f(l_tot)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// token-list kernel (decode)
+// ---------------------------------------------------------------------------
+template <class E, int D, int R, bool OUT_F32>
+__global__ __launch_bounds__(256) void fmha_tokens_kernel(FmhaArgs a) {
+  typedef typename E::T T;
+  constexpr int QW = D / 4;          // d values per quarter (QK phase)
+  constexpr int CPR = D / 8;         // 16-byte chunks per row
+  constexpr int NS = 256 / CPR;      // key subsets (PV phase)
+  constexpr int KPS = 64 / NS;       // keys per subset per chunk
+  __shared__ float s_q[R][D];
+  __shared__ int s_tok[64];
+  __shared__ float s_p[R][64];
+  __shared__ float s_alpha[R];
+  __shared__ float s_ml[R][2];
+  __shared__ __attribute__((aligned(16))) float s_red[NS][R * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  // (b, kv head, split)
+  int64_t lin = blockIdx.x;
+  const int hk = (int)(lin % a.hkv);
+  lin /= a.hkv;
+  const int bb = (int)(lin % a.b);
+  const int split = (int)(lin / a.b);
+  const int sq = a.sq;
+
+  const int hlut = a.lut_heads == a.hq ? hk * a.ratio : hk;   // rows are per KV head
+  const int32_t* list = a.lut + ((int64_t)bb * a.lut_heads + hlut) * a.lut_row_len;
+  const int L = a.lut_row_len;
+  const int chunk = (L + a.splits - 1) / a.splits;
+  const int beg = split * chunk;
+  const int end = min(L, beg + chunk);
+
+  // Query rows r = g * sq + sp for query head hk*ratio + g, position sp; the
+  // template row count R may exceed the real one (rows), whose rows stay zero.
+  const int rows = a.ratio * sq;
+  for (int i = tid; i < R * D; i += 256) {
+    const int r = i / D, d = i % D;
+    float x = 0.f;
+    if (r < rows) {
+      const int g = r / sq, sp = r % sq;
+      const T* qp = reinterpret_cast<const T*>(a.q) + bb * a.qs[0] + (int64_t)(hk * a.ratio + g) * a.qs[1] +
+                    (int64_t)sp * a.qs[2] + d;
+      x = E::to_f(*qp);
+    }
+    s_q[r][d] = x;
+  }
+  float m_run[2], l_run[2];    // rows wave and wave + 4 (R <= 8)
+#pragma unroll
+  for (int i = 0; i < 2; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.f; }
+  float acc[R][8];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
+
+  const T* kbase = reinterpret_cast<const T*>(a.k) + bb * a.ks[0] + hk * a.ks[1];
+  const T* vbase = reinterpret_cast<const T*>(a.v) + bb * a.vs[0] + hk * a.vs[1];
+  const float c2 = a.scale_log2;
+  const int qj = tid >> 2, qq = tid & 3;        // QK phase: key slot, quarter
+  const int pc = tid % CPR, ps = tid / CPR;     // PV phase: d chunk, key subset
+
+#pragma unroll 1
+  for (int pos0 = beg; pos0 < end; pos0 += 64) {
+    __syncthreads();
+    if (tid < 64) s_tok[tid] = pos0 + tid < end ? list[pos0 + tid] : -1;
+    __syncthreads();
+
+    // Issue the K and V gathers of this chunk together.
+    const int tk = s_tok[qj];
+    u32x4 kr[QW / 8];
+#pragma unroll
+    for (int i = 0; i < QW / 8; ++i)
+      kr[i] = tk >= 0 ? load16(kbase + (int64_t)tk * a.ks[2] + qq * QW + 8 * i) : u32x4{0u, 0u, 0u, 0u};
+    u32x4 vr[KPS];
+#pragma unroll
+    for (int i = 0; i < KPS; ++i) {
+      const int tv = s_tok[ps + NS * i];
+      vr[i] = tv >= 0 ? load16(vbase + (int64_t)tv * a.vs[2] + pc * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    // Scores: each thread dots a quarter of one key with every query row.
+    float part[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) part[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < QW / 8; ++i) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float x0 = E::lo(kr[i][w]), x1 = E::hi(kr[i][w]);
+        const int d = qq * QW + 8 * i + 2 * w;
+#pragma unroll
+        for (int r = 0; r < R; ++r) part[r] = fmaf(s_q[r][d + 1], x1, fmaf(s_q[r][d], x0, part[r]));
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      part[r] += __shfl_xor(part[r], 1, kWave);
+      part[r] += __shfl_xor(part[r], 2, kWave);
+    }
+    if (qq == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) s_p[r][qj] = tk >= 0 ? part[r] * c2 : -INFINITY;
+    }
+    __syncthreads();
+
+    // Online softmax: wave w owns rows w and w + 4.
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = wave + 4 * i;
+      if (r < R) {
+        const float x = s_p[r][lane];
+        const float cm = wave_max(x);
+        const float m_new = fmaxf(m_run[i], cm);
+        float alpha, p;
+        if (m_new == -INFINITY) {
+          alpha = 1.f;
+          p = 0.f;
+        } else {
+          alpha = __builtin_amdgcn_exp2f(m_run[i] - m_new);
+          p = __builtin_amdgcn_exp2f(x - m_new);
+        }
+        m_run[i] = m_new;
+        l_run[i] = fmaf(l_run[i], alpha, wave_sum(p));
+        s_p[r][lane] = p;
+        if (lane == 0) s_alpha[r] = alpha;
+      }
+    }
+    __syncthreads();
+
+    // PV: thread (d chunk pc, key subset ps) accumulates its keys.
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float al = s_alpha[r];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[r][e] *= al;
+    }
+#pragma unroll
+    for (int i = 0; i < KPS; ++i) {
+      const int j = ps + NS * i;
+      float v[8];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        v[2 * w] = E::lo(vr[i][w]);
+        v[2 * w + 1] = E::hi(vr[i][w]);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float p = s_p[r][j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(p, v[e], acc[r][e]);
+      }
+    }
+  }
+
+  // Publish each row's (max, sum), then reduce the PV partials over key subsets.
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = wave + 4 * i;
+    if (r < R && lane == 0) {
+      s_ml[r][0] = m_run[i];
+      s_ml[r][1] = l_run[i];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    floatx4 lo4 = {acc[r][0], acc[r][1], acc[r][2], acc[r][3]};
+    floatx4 hi4 = {acc[r][4], acc[r][5], acc[r][6], acc[r][7]};
+    *reinterpret_cast<floatx4*>(&s_red[ps][r * D + pc * 8]) = lo4;
+    *reinterpret_cast<floatx4*>(&s_red[ps][r * D + pc * 8 + 4]) = hi4;
+  }
+  __syncthreads();
+  for (int i = tid; i < rows * D; i += 256) {
+    const int r = i / D, d = i % D;
+    float sum = 0.f;
+#pragma unroll 8
+    for (int j = 0; j < NS; ++j) sum += s_red[j][i];
+    const float m = s_ml[r][0], l = s_ml[r][1];
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const int g = r / sq, sp = r % sq;
+    const int hq = hk * a.ratio + g;
+    const int64_t off = (int64_t)split * a.o_split_stride + bb * a.os[0] + (int64_t)hq * a.os[1] +
+                        (int64_t)sp * a.os[2] + d;
+    const float val = l > 0.f ? sum * inv : 0.f;
+    if constexpr (OUT_F32) reinterpret_cast<float*>(a.o)[off] = val;
+    else reinterpret_cast<T*>(a.o)[off] = E::from_f(val);
+    if (d == 0 && a.lse) {
+      a.lse[(((int64_t)split * a.b + bb) * a.hq + hq) * sq + sp] =
+          l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <class E, int D>
+static hipError_t launch_block_t(const FmhaArgs& a, bool out_f32, hipStream_t st) {
+  const int64_t G = (int64_t)a.nqt * a.hq * a.b * a.splits;
+  const dim3 grid((unsigned)(((G + 7) / 8) * 8));
+  if (out_f32) hipLaunchKernelGGL((fmha_block_kernel<E, D, true>), grid, dim3(128), 0, st, a);
+  else hipLaunchKernelGGL((fmha_block_kernel<E, D, false>), grid, dim3(128), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fmha_block(const FmhaArgs& a, sparge_dtype dt, sparge_dtype o_dt, int d,
+                             hipStream_t st) {
+  const bool f32 = o_dt == SPARGE_F32;
+  if (dt == SPARGE_F16) return d == 128 ? launch_block_t<F16, 128>(a, f32, st) : launch_block_t<F16, 64>(a, f32, st);
+  return d == 128 ? launch_block_t<BF16, 128>(a, f32, st) : launch_block_t<BF16, 64>(a, f32, st);
+}
+
+template <class E, int D, int R>
+static hipError_t launch_tokens_r(const FmhaArgs& a, bool out_f32, hipStream_t st) {
+  const dim3 grid((unsigned)((int64_t)a.b * a.hkv * a.splits));
+  if (out_f32) hipLaunchKernelGGL((fmha_tokens_kernel<E, D, R, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((fmha_tokens_kernel<E, D, R, false>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <class E, int D>
+static hipError_t launch_tokens_d(const FmhaArgs& a, bool out_f32, int rows, hipStream_t st) {
+  switch (rows) {
+    case 1: return launch_tokens_r<E, D, 1>(a, out_f32, st);
+    case 2: return launch_tokens_r<E, D, 2>(a, out_f32, st);
+    case 3: case 4: return launch_tokens_r<E, D, 4>(a, out_f32, st);
+    default: return launch_tokens_r<E, D, 8>(a, out_f32, st);
+  }
+}
+
+hipError_t launch_fmha_tokens(const FmhaArgs& a, sparge_dtype dt, sparge_dtype o_dt, int d,
+                              int rows_per_group, hipStream_t st) {
+  const bool f32 = o_dt == SPARGE_F32;
+  if (dt == SPARGE_F16)
+    return d == 128 ? launch_tokens_d<F16, 128>(a, f32, rows_per_group, st)
+                    : launch_tokens_d<F16, 64>(a, f32, rows_per_group, st);
+  return d == 128 ? launch_tokens_d<BF16, 128>(a, f32, rows_per_group, st)
+                  : launch_tokens_d<BF16, 64>(a, f32, rows_per_group, st);
+}
+
+}  // namespace sparge

@@ -1,0 +1,83 @@
+// Internal kernel-argument structs and launchers of the gfx950 block-sparse
+// attention library.  Host entry points (abi.hip) validate arguments and call
+// these; each launcher enqueues its kernels on the given stream and returns the
+// launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sparge.h"
+
+namespace sparge {
+
+struct PoolArgs {
+  const void* q;
+  const void* k;
+  int64_t qs[3];
+  int64_t ks[3];
+  int b, h, nq, nk;
+  float* q_mean;     // [b, h, nq, d]
+  float* k_mean;     // [b, h, nk, d]
+  uint8_t* sim_q;    // [b, h, nq]
+  uint8_t* sim_k;    // [b, h, nk]
+  float thr[SPARGE_MAX_HEADS];
+};
+
+struct SelectArgs {
+  const float* q_mean;
+  const float* k_mean;
+  const uint8_t* sim_q;
+  const uint8_t* sim_k;
+  int b, h, nq, nk;
+  float scale;
+  int32_t* lut;      // [b, h, nq, nk]
+  int32_t* count;    // [b, h, nq]
+  uint8_t* bmap;     // [b, h, nq, nk] or null
+  float* prob;       // [b, h, nq, nk] or null
+  int nsel[SPARGE_MAX_HEADS];   // > 0: top-k count; <= 0: cdf mode
+  float cdf[SPARGE_MAX_HEADS];
+};
+
+struct FmhaArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t qs[3], ks[3], vs[3], os[3];
+  int b, hq, hkv, sq, sk;
+  int ratio;               // hq / hkv
+  const int32_t* lut;      // null => dense
+  const int32_t* cnt;      // null => up to the first -1
+  int lut_row_len;
+  int lut_heads;
+  int nqt;                 // rows per (b, lut head): q tiles, or query positions
+  int nkb;                 // K blocks (block mode)
+  float scale_log2;        // softmax scale * log2(e)
+  int splits;
+  int64_t o_split_stride;  // elements
+};
+
+struct CombineArgs {
+  const void* parts;
+  const float* lse_parts;
+  int n_parts;
+  int64_t rows;            // b * h * s
+  int64_t part_stride;     // elements
+  void* o;
+  float* lse_out;
+};
+
+hipError_t launch_pool_sim(const PoolArgs& a, sparge_dtype dt, int d, hipStream_t st);
+hipError_t launch_score_select(const SelectArgs& a, int d, hipStream_t st);
+hipError_t launch_fmha_block(const FmhaArgs& a, sparge_dtype dt, sparge_dtype o_dt, int d,
+                             hipStream_t st);
+hipError_t launch_fmha_tokens(const FmhaArgs& a, sparge_dtype dt, sparge_dtype o_dt, int d,
+                              int rows_per_group, hipStream_t st);
+hipError_t launch_combine(const CombineArgs& a, sparge_dtype part_dt, sparge_dtype out_dt,
+                          int d, hipStream_t st);
+hipError_t launch_validate_lut(const int32_t* lut, const int32_t* cnt, int64_t rows,
+                               int row_len, int n_blocks, int32_t* bad, hipStream_t st);
+
+}  // namespace sparge

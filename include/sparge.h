@@ -1,0 +1,209 @@
+/*
+ * sparge.h -- C ABI of the gfx950 (MI355X) block-sparse attention library.
+ *
+ * The library implements the forward pass of SpargeAttn-style block-sparse
+ * attention in two stages, as the "Sparge Attention (Composable Kernel)" page
+ * describes it ("Status vs Upstream"): a block map (per-block mean pool of Q
+ * and K, an intra-block cosine-similarity gate, a softmax over pooled QK
+ * scores, and top-k / cdfthreshd selection into a per-Q-tile LUT), then a
+ * sparse flash attention over the selected K/V blocks that exports the
+ * natural-log LSE (an empty row gives O = 0, LSE = -inf: aiter pull request
+ * 6841 page; "Updating Log -- Speculative Sparse Attention" page, Stage 3),
+ * plus the LSE combine that merges partial results (Updating Log page,
+ * Stage 1: FA(A u B) = Combine(FA(A), FA(B))).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is DEVICE memory owned by the caller.  The library
+ *   never allocates, frees or synchronises; it only enqueues kernels on the
+ *   given stream (a hipStream_t passed as void*; NULL = the null stream).
+ *   Outputs are valid once the stream has run the work.
+ * - Small per-head parameter arrays (topk, cdfthreshd, simthreshd1) are HOST
+ *   memory, read during the call only.
+ * - Tensors of shape [b, h, s, d] are addressed with element strides for the
+ *   b, h and s dimensions; the d dimension must be contiguous (stride 1) and
+ *   every row must start 16-byte aligned.
+ * - Arguments are checked on the host before anything is enqueued.  On any
+ *   error nothing is enqueued and the call returns a non-zero status;
+ *   sparge_last_error() then gives a message (per calling thread).
+ * - The device does not check LUT / index-list entries: an entry outside
+ *   [0, n_blocks) (or [0, s_k) for token lists), other than -1 padding, is
+ *   undefined behaviour.  sparge_validate_lut() checks a LUT on the device.
+ * - Supported: d in {64, 128}; fp16 or bf16 inputs; 64-token blocks (block
+ *   mode) or 1-token granularity (token-list mode, see sparse_fmha_fwd).
+ */
+#ifndef SPARGE_H
+#define SPARGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPARGE_OK = 0,
+  SPARGE_ERR_INVALID = 1,      /* null pointer, bad size, stride or parameter   */
+  SPARGE_ERR_UNSUPPORTED = 2,  /* valid but not built: head dim, block, causal  */
+  SPARGE_ERR_HIP = 3           /* a HIP runtime error at launch (see message)   */
+} sparge_status;
+
+typedef enum {
+  SPARGE_F16 = 0,
+  SPARGE_BF16 = 1,
+  SPARGE_F32 = 2
+} sparge_dtype;
+
+/* Largest head count accepted by sparge_build_block_map (per-head parameters
+ * travel in the kernel arguments). */
+#define SPARGE_MAX_HEADS 128
+/* Largest number of K blocks per row accepted by sparge_build_block_map
+ * (s_k <= 64 * 1024 tokens with 64-token blocks). */
+#define SPARGE_MAX_KBLOCKS 1024
+
+/* Library ABI version (this header: 1). */
+int sparge_abi_version(void);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* sparge_last_error(void);
+
+/*
+ * Stage 1: block map.  (CK page, "Status vs Upstream": mean-pool, cosine
+ * similarity, pooled QK, top-k / cdfthreshd selection, per-head knobs.)
+ *
+ * q [b, h, s_q, d], k [b, h, s_k, d] in `dt` (F16 or BF16), strides in
+ * elements for (b, h, s).  blk_q = blk_k = 64; s_q and s_k multiples of 64;
+ * nq = s_q / 64, nk = s_k / 64 <= SPARGE_MAX_KBLOCKS; h <= SPARGE_MAX_HEADS.
+ *
+ * For every 64-token block x_1..x_n of Q and of K:
+ *   mean  = (1/n) sum_i x_i                     (fp32)
+ *   sim   = |sum_i x_i/|x_i| |^2 / n^2           (mean pairwise cosine, i = j
+ *                                                 included; zero rows add 0)
+ *   flag  = sim > simthreshd1[head]
+ * Then per row (b, head, qb):
+ *   S[kb] = scale * <q_mean[qb], k_mean[kb]>, -inf where the K flag is 0;
+ *   P     = softmax_kb(S) in fp32 (a row of all -inf gives P = 0);
+ *   order kb by P descending, ties to the lower kb;
+ *   n     = clamp(floor(fp64(topk[head]) * nk), 1, nk) if topk[head] > 0,
+ *           else the fewest leading blocks whose fp64 running sum of P (added
+ *           one at a time in that order) reaches cdfthreshd[head] (nk if never);
+ *   selected = all kb if the Q flag is 0, else the first n of the order plus
+ *           every kb whose K flag is 0.
+ *
+ * Inputs:
+ *   topk        host float[h]; > 0 selects top-k mode for that head, must be <= 1.
+ *   cdfthreshd  host float[h] or NULL; used for heads with topk <= 0, must be
+ *               finite and in (0, 1].  NULL requires topk > 0 for every head.
+ *   simthreshd1 host float[h], finite.
+ *   softmax_scale  0 => 1/sqrt(d).
+ * Outputs (device, caller-owned; optional ones may be NULL):
+ *   lut        int32 [b, h, nq, nk]: selected kb ascending, then -1.
+ *   lut_count  int32 [b, h, nq]: number of selected blocks.
+ *   block_map  uint8 [b, h, nq, nk] or NULL: 1 = selected.
+ *   pooled_prob float [b, h, nq, nk] or NULL: P exactly as the selection saw it.
+ *   sim_q, sim_k uint8 [b, h, nq] / [b, h, nk] or NULL: gate flags.
+ *   q_mean, k_mean float [b, h, nq, d] / [b, h, nk, d] or NULL.
+ *   workspace  device scratch of at least sparge_build_block_map_workspace()
+ *              bytes, 256-byte aligned; contents on entry are ignored.
+ */
+sparge_status sparge_build_block_map(
+    const void* q, const void* k, sparge_dtype dt,
+    int b, int h, int s_q, int s_k, int d,
+    const int64_t q_strides[3], const int64_t k_strides[3],
+    int blk_q, int blk_k,
+    const float* topk, const float* cdfthreshd, const float* simthreshd1,
+    float softmax_scale,
+    int32_t* lut, int32_t* lut_count, uint8_t* block_map, float* pooled_prob,
+    uint8_t* sim_q, uint8_t* sim_k, float* q_mean, float* k_mean,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace sparge_build_block_map needs for these sizes
+ * (0 if the sizes are invalid). */
+size_t sparge_build_block_map_workspace(int b, int h, int s_q, int s_k, int d,
+                                        int blk_q, int blk_k);
+
+/*
+ * Stage 2: sparse flash attention forward.  (Updating Log page, Stage 3: the
+ * kernel walks the listed K/V blocks with an online softmax, an empty list
+ * writes O = 0 and LSE = -inf; aiter 6841 page: LSE export and GQA mapping,
+ * query head j reads KV head j / (h_q / h_kv).)
+ *
+ * q [b, h_q, s_q, d]; k, v [b, h_kv, s_k, d]; all in `dt` (F16 or BF16).
+ * For every query row i the kernel computes, over the keys J the LUT selects,
+ *   s_j = scale * <q_i, k_j>,  LSE_i = ln sum_j exp(s_j),
+ *   O_i = sum_j exp(s_j - LSE_i) v_j;   J empty => O_i = 0, LSE_i = -inf.
+ *
+ * Block mode (blk_q = blk_k = 64): s_q, s_k multiples of 64.  A LUT row
+ * belongs to (b, lut head, q tile of 64 rows) and lists K blocks (keys
+ * [64 kb, 64 kb + 64)):
+ *   lut        int32 [b, lut_heads, s_q / 64, lut_row_len], or NULL = dense
+ *              (every block, in order; the dense baseline);
+ *   lut_count  int32 [b, lut_heads, s_q / 64], or NULL = entries up to the
+ *              first -1 (or the whole row).
+ * Token-list mode (blk_q = blk_k = 1): a LUT row belongs to (b, lut head) and
+ *   lists token positions in [0, s_k); -1 entries are skipped wherever they
+ *   are; the same list serves every query position (decode: s_q = 1);
+ *   lut_count must be NULL; lut_heads must be h_kv (one list per KV head,
+ *   shared by its query heads); h_q / h_kv * s_q <= 8.
+ * In block mode lut_heads is h_q (one row per query head) or h_kv (a row
+ * shared by the query heads of one KV head).
+ *
+ * num_splits >= 1 divides every row's list into num_splits contiguous chunks
+ * of ceil(n / num_splits) entries; chunk c writes partial results to
+ * o + c * o_split_stride and lse + c * b * h_q * s_q (a chunk with no entry
+ * writes O = 0, LSE = -inf).  Merge them with attn_combine.
+ *
+ * Outputs: o [.., b, h_q, s_q, d] in o_dt (= dt, or F32 for partials), with
+ * o_strides for (b, h, s); lse float [.., b, h_q, s_q] contiguous, or NULL
+ * when num_splits = 1.
+ * softmax_scale 0 => 1/sqrt(d).
+ */
+sparge_status sparse_fmha_fwd(
+    const void* q, const void* k, const void* v, void* o, float* lse,
+    sparge_dtype dt, sparge_dtype o_dt,
+    int b, int h_q, int h_kv, int s_q, int s_k, int d,
+    const int64_t q_strides[3], const int64_t k_strides[3],
+    const int64_t v_strides[3], const int64_t o_strides[3],
+    int blk_q, int blk_k,
+    const int32_t* lut, const int32_t* lut_count, int lut_row_len, int lut_heads,
+    float softmax_scale, int num_splits, int64_t o_split_stride,
+    void* stream);
+
+/*
+ * LSE combine of n_parts partial results.  (Updating Log page, Stage 1:
+ * online-softmax merge with the running maximum; aiter 4919 page: partials
+ * whose LSE is -inf are masked before the exponential.)
+ *
+ * Per row r and part i:  m = max_i LSE_i;  w_i = exp(LSE_i - m), 0 where
+ * LSE_i = -inf;  O = sum_i w_i O_i / sum_i w_i;  LSE = m + ln sum_i w_i.
+ * Every part -inf => O = 0, LSE = -inf.
+ *
+ * o_parts   [n_parts][b, h, s, d] in part_dt (F32, F16 or BF16), each part
+ *           contiguous, part_stride elements apart (>= b*h*s*d).
+ * lse_parts float [n_parts][b, h, s] contiguous.
+ * o         [b, h, s, d] contiguous in out_dt (F32, F16 or BF16).
+ * lse_out   float [b, h, s] or NULL.
+ * 1 <= n_parts <= 256; d in {64, 128}.
+ */
+sparge_status attn_combine(
+    const void* o_parts, sparge_dtype part_dt, const float* lse_parts,
+    int n_parts, int b, int h, int s, int d, int64_t part_stride,
+    void* o, sparge_dtype out_dt, float* lse_out, void* stream);
+
+/*
+ * Debug check of a LUT on the device.  For `rows` rows of `row_len` entries
+ * (and per-row counts, or NULL = up to the first -1), counts the rows whose
+ * listed entries are not strictly ascending, fall outside [0, n_blocks), or
+ * whose count exceeds row_len, and whose tail after the count is not all -1.
+ * Writes that number of bad rows to bad_rows (device int32[1]).
+ */
+sparge_status sparge_validate_lut(const int32_t* lut, const int32_t* lut_count,
+                                  int64_t rows, int row_len, int n_blocks,
+                                  int32_t* bad_rows, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARGE_H */

@@ -1,0 +1,195 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch.
+
+Every rejection case below fails host validation, so no kernel is ever
+enqueued; the tests still refuse to run where a GPU is visible, so that a
+mistake in a case can never send a fake pointer to a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from block_sparse_attention_sparge_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparge.h")
+
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="host-only rejection tests (no device pointers)")
+
+FAKE = 0x10000          # 16-byte aligned address that validation must never hand to a kernel
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        from block_sparse_attention_sparge_amd import build
+        build.build(verbose=False)
+    return ops.load_library()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = header_functions()
+    assert set(names) == set(ops.EXPORTED_SYMBOLS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version(lib):
+    assert lib.sparge_abi_version() == 1
+
+
+def _s3(a, b, c):
+    return ops._I64x3(a, b, c)
+
+
+def _arr(vals):
+    return (ctypes.c_float * len(vals))(*vals)
+
+
+def _err(lib):
+    return lib.sparge_last_error().decode()
+
+
+def test_workspace_size(lib):
+    n = lib.sparge_build_block_map_workspace(2, 32, 16384, 16384, 128, 64, 64)
+    # q_mean + k_mean (fp32) + two flag arrays, each rounded to 256 bytes
+    assert n == 2 * (2 * 32 * 256 * 128 * 4) + 2 * ((2 * 32 * 256 + 255) // 256 * 256)
+    assert lib.sparge_build_block_map_workspace(1, 1, 100, 64, 64, 64, 64) == 0
+    assert lib.sparge_build_block_map_workspace(1, 1, 64, 64, 96, 64, 64) == 0
+
+
+def _bm(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, dt=ops.SPARGE_F16, b=1, h=2, s_q=512, s_k=512, d=64,
+                qs=_s3(65536, 32768, 64), ks=_s3(65536, 32768, 64), blk_q=64, blk_k=64,
+                topk=_arr([0.5, 0.5]), cdf=None, sim=_arr([0.001, 0.001]), scale=0.0,
+                lut=FAKE, cnt=FAKE, ws=FAKE, ws_bytes=1 << 20)
+    args.update(kw)
+    return lib.sparge_build_block_map(
+        args["q"], args["k"], args["dt"], args["b"], args["h"], args["s_q"], args["s_k"], args["d"],
+        args["qs"], args["ks"], args["blk_q"], args["blk_k"], args["topk"], args["cdf"], args["sim"],
+        args["scale"], args["lut"], args["cnt"], None, None, None, None, None, None,
+        args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ops.SPARGE_ERR_INVALID),
+    (dict(lut=None), ops.SPARGE_ERR_INVALID),
+    (dict(dt=ops.SPARGE_F32), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(d=96), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(s_q=500), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(s_k=100), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(blk_q=128), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(h=0), ops.SPARGE_ERR_INVALID),
+    (dict(h=200), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(s_k=64 * 1025), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(qs=_s3(65536, 32768, 60)), ops.SPARGE_ERR_INVALID),
+    (dict(topk=_arr([1.5, 0.5])), ops.SPARGE_ERR_INVALID),
+    (dict(topk=_arr([float("nan"), 0.5])), ops.SPARGE_ERR_INVALID),
+    (dict(topk=_arr([0.0, 0.5])), ops.SPARGE_ERR_INVALID),          # cdf mode without cdfthreshd
+    (dict(topk=_arr([0.0, 0.5]), cdf=_arr([1.5, 0.5])), ops.SPARGE_ERR_INVALID),
+    (dict(sim=_arr([float("inf"), 0.0])), ops.SPARGE_ERR_INVALID),
+    (dict(ws_bytes=16), ops.SPARGE_ERR_INVALID),
+    (dict(ws=FAKE + 16), ops.SPARGE_ERR_INVALID),
+    (dict(q=FAKE + 2), ops.SPARGE_ERR_INVALID),
+    (dict(scale=-1.0), ops.SPARGE_ERR_INVALID),
+])
+def test_block_map_rejections(lib, kw, status):
+    st = _bm(lib, **kw)
+    assert st == status, _err(lib)
+    assert _err(lib) != ""
+
+
+def _fmha(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dt=ops.SPARGE_BF16, odt=ops.SPARGE_BF16,
+             b=1, hq=8, hkv=2, sq=512, sk=512, d=128, qs=_s3(8 * 512 * 128, 512 * 128, 128),
+             ks=_s3(2 * 512 * 128, 512 * 128, 128), vs=_s3(2 * 512 * 128, 512 * 128, 128),
+             os=_s3(8 * 512 * 128, 512 * 128, 128), bq=64, bk=64, lut=FAKE, cnt=FAKE, L=8,
+             lh=8, scale=0.0, splits=1, sst=0)
+    a.update(kw)
+    return lib.sparse_fmha_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dt"], a["odt"], a["b"],
+                               a["hq"], a["hkv"], a["sq"], a["sk"], a["d"], a["qs"], a["ks"], a["vs"],
+                               a["os"], a["bq"], a["bk"], a["lut"], a["cnt"], a["L"], a["lh"],
+                               a["scale"], a["splits"], a["sst"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ops.SPARGE_ERR_INVALID),
+    (dict(o=None), ops.SPARGE_ERR_INVALID),
+    (dict(hkv=3), ops.SPARGE_ERR_INVALID),
+    (dict(d=80), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(dt=ops.SPARGE_F32), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(odt=ops.SPARGE_F16), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(sq=500), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(sk=520), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(bq=128, bk=128), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(bq=64, bk=1), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(lh=4), ops.SPARGE_ERR_INVALID),
+    (dict(L=0), ops.SPARGE_ERR_INVALID),
+    (dict(splits=0), ops.SPARGE_ERR_INVALID),
+    (dict(splits=2, lse=None), ops.SPARGE_ERR_INVALID),
+    (dict(splits=2, sst=12), ops.SPARGE_ERR_INVALID),
+    (dict(ks=_s3(2 * 512 * 128, 512 * 128, 130)), ops.SPARGE_ERR_INVALID),
+    (dict(vs=_s3(-8, 512 * 128, 128)), ops.SPARGE_ERR_INVALID),
+    (dict(k=FAKE + 8), ops.SPARGE_ERR_INVALID),
+    (dict(lut=None, cnt=FAKE), ops.SPARGE_ERR_INVALID),
+    (dict(scale=float("nan")), ops.SPARGE_ERR_INVALID),
+    # token-list mode
+    (dict(bq=1, bk=1, lut=None, cnt=None), ops.SPARGE_ERR_INVALID),
+    (dict(bq=1, bk=1, cnt=FAKE, lh=2), ops.SPARGE_ERR_INVALID),
+    (dict(bq=1, bk=1, cnt=None, lh=8), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(bq=1, bk=1, cnt=None, lh=2, sq=4), ops.SPARGE_ERR_UNSUPPORTED),   # 16 rows per KV head
+])
+def test_fmha_rejections(lib, kw, status):
+    st = _fmha(lib, **kw)
+    assert st == status, _err(lib)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(parts=None), ops.SPARGE_ERR_INVALID),
+    (dict(n=0), ops.SPARGE_ERR_INVALID),
+    (dict(n=300), ops.SPARGE_ERR_INVALID),
+    (dict(d=32), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(stride=100), ops.SPARGE_ERR_INVALID),
+    (dict(pdt=7), ops.SPARGE_ERR_INVALID),
+    (dict(o=FAKE + 4), ops.SPARGE_ERR_INVALID),
+])
+def test_combine_rejections(lib, kw, status):
+    a = dict(parts=FAKE, pdt=ops.SPARGE_F32, lse=FAKE, n=2, b=1, h=2, s=16, d=64,
+             stride=2 * 16 * 64, o=FAKE, odt=ops.SPARGE_F32, lse_out=FAKE)
+    a.update(kw)
+    st = lib.attn_combine(a["parts"], a["pdt"], a["lse"], a["n"], a["b"], a["h"], a["s"], a["d"],
+                          a["stride"], a["o"], a["odt"], a["lse_out"], None)
+    assert st == status, _err(lib)
+
+
+def test_validate_lut_rejections(lib):
+    assert lib.sparge_validate_lut(None, None, 4, 4, 4, FAKE, None) == ops.SPARGE_ERR_INVALID
+    assert lib.sparge_validate_lut(FAKE, None, 0, 4, 4, FAKE, None) == ops.SPARGE_ERR_INVALID
+
+
+def test_error_message_is_per_call(lib):
+    assert _bm(lib, d=96) == ops.SPARGE_ERR_UNSUPPORTED
+    assert "head dim" in _err(lib)
+
+
+def test_python_binding_rejects_cpu_tensors(lib):
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.float16)
+    with pytest.raises(ops.SpargeError):
+        ops.sparse_fmha_fwd(q, q, q)
+    with pytest.raises(ops.SpargeError):
+        ops.build_block_map(q, q, [0.5], [0.001])
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ops.SpargeError):
+        ops.load_library(str(tmp_path / "nope.so"))

@@ -1,0 +1,455 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars (fixed before any kernel existed):
+* LUT, count and bitmap bit-exact against the oracle's selection run on the
+  GPU's exported pooled probabilities and gate flags;
+* pooled means within 1e-3 relative (+1e-6 rms), pooled probabilities within
+  1e-3 relative (+1e-7);
+* attention output within atol 4e-2 / rtol 1e-2 (fp16 / bf16);
+* LSE within 2e-3 nats, and -inf exactly where the oracle has -inf.
+Inputs are seeded synthetic tensors drawn on the GPU and copied to the host
+for the oracle; no expected value comes from the HIP path.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_sparge_amd import ops, synth
+
+pytestmark = pytest.mark.gpu
+
+O_ATOL, O_RTOL, LSE_TOL = 4e-2, 1e-2, 2e-3
+
+
+def np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check_o(o_gpu, o_ref, atol=O_ATOL, rtol=O_RTOL, what="O"):
+    g = np64(o_gpu) if isinstance(o_gpu, torch.Tensor) else o_gpu
+    err = np.abs(g - o_ref)
+    bound = atol + rtol * np.abs(o_ref)
+    bad = err > bound
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} outside atol/rtol; max err {err.max():.3e}"
+    return float(err.max())
+
+
+def check_lse(l_gpu, l_ref, tol=LSE_TOL):
+    g = np64(l_gpu) if isinstance(l_gpu, torch.Tensor) else l_gpu
+    ninf_g, ninf_r = np.isneginf(g), np.isneginf(l_ref)
+    assert np.array_equal(ninf_g, ninf_r), f"-inf mismatch: {np.sum(ninf_g != ninf_r)} rows"
+    fin = ~ninf_r
+    if fin.any():
+        err = np.abs(g[fin] - l_ref[fin]).max()
+        assert err <= tol, f"LSE max err {err:.3e} nats"
+        return float(err)
+    return 0.0
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    ops.load_library()          # raises if the HIP library is missing
+    return torch.device("cuda:0")
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# combine
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("pdt", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n", [1, 2, 5])
+def test_combine_matches_oracle(dev, pdt, d, n):
+    b, h, s = 2, 3, 70
+    g = torch.Generator(device=dev).manual_seed(100 + n + d)
+    parts = torch.randn(n, b, h, s, d, generator=g, device=dev).to(pdt)
+    lse = torch.randn(n, b, h, s, generator=g, device=dev) * 3
+    lse[0, 0, 0, :10] = -math.inf                     # one part empty on some rows
+    lse[:, 1, 2, 5:9] = -math.inf                     # every part empty on some rows
+    out_dt = torch.float32 if pdt == torch.float32 else pdt
+    o, l = ops.attn_combine(parts, lse, out_dtype=out_dt)
+    _sync()
+    ro, rl = oracle.combine(list(np64(parts)), list(np64(lse)))
+    tol = 2e-6 if pdt == torch.float32 else 8e-3
+    check_o(o, ro, atol=tol, rtol=tol, what="combined O")
+    check_lse(l, rl, tol=1e-5)
+    assert (np64(o)[1, 2, 5:9] == 0).all()
+
+
+def test_combine_partials_with_stride_padding(dev):
+    n, b, h, s, d = 3, 1, 2, 33, 128
+    g = torch.Generator(device=dev).manual_seed(7)
+    buf = torch.randn(n, b * h * s * d + 64, generator=g, device=dev)
+    parts = buf[:, : b * h * s * d].view(n, b, h, s, d)
+    lse = torch.randn(n, b, h, s, generator=g, device=dev)
+    o, l = ops.attn_combine(parts, lse)
+    _sync()
+    ro, rl = oracle.combine(list(np64(parts)), list(np64(lse)))
+    check_o(o, ro, atol=2e-6, rtol=2e-6)
+    check_lse(l, rl, tol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# block map
+# ---------------------------------------------------------------------------
+
+def _block_map_case(dev, case, cdf=None, rel_pool=1e-3):
+    q, k = case.q, case.k
+    topk = case.topk if cdf is None else [0.0] * len(case.topk)
+    res = ops.build_block_map(q, k, topk, case.simthreshd1, cdfthreshd=cdf, return_debug=True)
+    _sync()
+    qn, kn = np64(q), np64(k)
+    ref = oracle.block_map(qn, kn, topk=topk, simthreshd1=case.simthreshd1, cdfthreshd=cdf)
+    # pooled means
+    for key in ("q_mean", "k_mean"):
+        g, r = np64(res[key]), ref[key]
+        rms = math.sqrt(float((r * r).mean()))
+        assert (np.abs(g - r) <= 1e-3 * np.abs(r) + 1e-6 * rms).all(), key
+    # gate flags, away from the threshold
+    for key, val in (("sim_q", "sim_q_val"), ("sim_k", "sim_k_val")):
+        g = np64(res[key]).astype(bool)
+        thr = np.array(case.simthreshd1)[None, :, None]
+        far = np.abs(ref[val] - thr) > 1e-5
+        assert np.array_equal(g[far], ref[key][far]), key
+    # pooled probabilities
+    gp = np64(res["prob"])
+    assert (np.abs(gp - ref["prob"]) <= 1e-3 * np.abs(ref["prob"]) + 1e-7).all(), "pooled prob"
+    # bit-exact selection on the GPU's own probabilities and flags
+    lut, cnt, bm = oracle.select_from_probs(gp, np64(res["sim_q"]).astype(bool),
+                                            np64(res["sim_k"]).astype(bool), topk, cdf)
+    assert np.array_equal(res["lut"].cpu().numpy(), lut), "LUT not bit-exact"
+    assert np.array_equal(res["count"].cpu().numpy(), cnt), "count not bit-exact"
+    assert np.array_equal(res["bitmap"].cpu().numpy(), bm), "bitmap not bit-exact"
+    # agreement with the oracle's independent selection: differences only at near-ties
+    own = ref["lut"]
+    rows_diff = np.argwhere((own != lut).any(axis=-1))
+    for ib, ih, qb in rows_diff:
+        p = ref["prob"][ib, ih, qb]
+        ps = np.sort(p)[::-1]
+        n = int(cnt[ib, ih, qb])
+        gap = min(abs(ps[n - 1] - ps[min(n, len(ps) - 1)]), abs(ps[max(n - 2, 0)] - ps[n - 1]))
+        assert gap <= 1e-4 * ps[0], f"row {(ib, ih, qb)} differs without a near-tie"
+    agree = 1.0 - len(rows_diff) / max(1, own.shape[0] * own.shape[1] * own.shape[2])
+    assert ops.validate_lut(res["lut"], res["count"], k.shape[2] // 64) == 0
+    return res, ref, agree
+
+
+def test_block_map_tiny(dev):
+    case = synth.tiny_case(dev)
+    res, ref, agree = _block_map_case(dev, case)
+    assert (res["count"].cpu().numpy() == 4).all()        # topk 0.5 of 8, gate never fires
+    assert agree == 1.0
+
+
+@pytest.mark.parametrize("topk", [0.4, 1.0])
+def test_block_map_mid(dev, topk):
+    case = synth.mid_case(dev, topk=topk)
+    res, ref, agree = _block_map_case(dev, case)
+    assert (res["count"].cpu().numpy() == (25 if topk == 0.4 else 64)).all()
+    assert agree >= 0.99
+
+
+def test_block_map_ragged_block_counts(dev):
+    # nk = 37 (not a power of two), s_q != s_k, d = 64, fp16, per-head topk.
+    b, h, sq, sk, d = 2, 3, 320, 37 * 64, 64
+    q = synth.centroid_noise(b, h, sq, d, 64, [1.0, 1.5, 2.0], 0.4, 3, 1, torch.float16, dev)
+    k = synth.centroid_noise(b, h, sk, d, 64, [1.0, 1.5, 2.0], 0.4, 3, 2, torch.float16, dev)
+    v = synth.normal((b, h, sk, d), 3, 3, torch.float16, dev)
+    case = synth.BlockSparseCase("ragged", q, k, v, [0.3, 0.05, 0.77], [0.001] * 3)
+    _block_map_case(dev, case)
+
+
+def test_block_map_cdf_mode(dev):
+    case = synth.mid_case(dev)
+    cdf = [0.3, 0.6, 0.9, 0.99, 1.0, 0.5, 0.75, 0.95]
+    res, ref, _ = _block_map_case(dev, case, cdf=cdf)
+    counts = res["count"].cpu().numpy()
+    assert counts[0, 4].max() == 64 or counts[0, 4].min() >= counts[0, 3].min()
+
+
+def test_block_map_gate_fires(dev):
+    # Q block 3 and K blocks 1, 5 of head 0 become +-v pairs (similarity 0).
+    case = synth.tiny_case(dev, seed=4)
+    q, k = case.q.clone(), case.k.clone()
+    vq = torch.randn(case.q.shape[-1], generator=torch.Generator(device=dev).manual_seed(9), device=dev)
+    pm = torch.cat([vq.expand(32, -1), -vq.expand(32, -1)]).to(q.dtype)
+    q[0, 0, 3 * 64:4 * 64] = pm
+    k[0, 0, 1 * 64:2 * 64] = pm
+    k[0, 0, 5 * 64:6 * 64] = pm.flip(0)
+    case = synth.BlockSparseCase("gate", q, k, case.v, [0.25, 0.25], [0.001, 0.001])
+    res, ref, agree = _block_map_case(dev, case)
+    sq = res["sim_q"].cpu().numpy()
+    sk = res["sim_k"].cpu().numpy()
+    assert sq[0, 0, 3] == 0 and sk[0, 0, 1] == 0 and sk[0, 0, 5] == 0
+    cnt = res["count"].cpu().numpy()
+    assert cnt[0, 0, 3] == 8                                # whole row
+    lut = res["lut"].cpu().numpy()
+    for qb in range(8):
+        if qb != 3:
+            row = set(lut[0, 0, qb, :cnt[0, 0, qb]].tolist())
+            assert {1, 5} <= row and cnt[0, 0, qb] == 4     # 2 chosen + 2 forced
+    assert agree == 1.0
+
+
+def test_block_map_per_head_topk_sweep(dev):
+    case = synth.headline_case(dev, topk=synth.mixed_topk(5), b=1, h=5, s=2048)
+    res, ref, agree = _block_map_case(dev, case)
+    counts = res["count"].cpu().numpy()[0]
+    expect = [oracle.topk_count(t, 32) for t in synth.mixed_topk(5)]
+    assert [int(c.max()) for c in counts] == expect
+
+
+@pytest.mark.parametrize("sk", [64, 64 * 1024])
+def test_block_map_extreme_block_counts(dev, sk):
+    b, h, sq, d = 1, 2, 256, 64
+    q = synth.centroid_noise(b, h, sq, d, 64, [1.0, 2.0], 0.3, 5, 1, torch.float16, dev)
+    k = synth.centroid_noise(b, h, sk, d, 64, [1.0, 2.0], 0.3, 5, 2, torch.float16, dev)
+    case = synth.BlockSparseCase("extreme", q, k, k, [0.1, 0.02], [0.001, 0.001])
+    _block_map_case(dev, case)
+
+
+# ---------------------------------------------------------------------------
+# sparse FMHA (block LUT)
+# ---------------------------------------------------------------------------
+
+def _fmha_vs_oracle(q, k, v, lut, cnt, o, lse, lut_per_kv=False):
+    ro, rl = oracle.block_sparse_attention(np64(q), np64(k), np64(v),
+                                           None if lut is None else lut.cpu().numpy(),
+                                           None if cnt is None else cnt.cpu().numpy(),
+                                           lut_per_kv_head=lut_per_kv)
+    e_o = check_o(o, ro)
+    e_l = check_lse(lse, rl)
+    return e_o, e_l
+
+
+def test_fmha_tiny_end_to_end(dev):
+    case = synth.tiny_case(dev)
+    bm = ops.build_block_map(case.q, case.k, case.topk, case.simthreshd1)
+    o, lse = ops.sparse_fmha_fwd(case.q, case.k, case.v, bm["lut"], bm["count"])
+    _sync()
+    _fmha_vs_oracle(case.q, case.k, case.v, bm["lut"], bm["count"], o, lse)
+
+
+@pytest.mark.parametrize("topk", [0.4, 1.0])
+def test_fmha_mid_end_to_end(dev, topk):
+    case = synth.mid_case(dev, topk=topk)
+    bm = ops.build_block_map(case.q, case.k, case.topk, case.simthreshd1)
+    o, lse = ops.sparse_fmha_fwd(case.q, case.k, case.v, bm["lut"], bm["count"])
+    _sync()
+    _fmha_vs_oracle(case.q, case.k, case.v, bm["lut"], bm["count"], o, lse)
+    if topk == 1.0:
+        ro, rl = oracle.dense_attention(np64(case.q), np64(case.k), np64(case.v))
+        check_o(o, ro)
+        check_lse(lse, rl)
+
+
+def test_dense_mode_bitexact_with_full_lut(dev):
+    case = synth.mid_case(dev)
+    b, h, s, d = case.q.shape
+    nq = nk = s // 64
+    full = torch.arange(nk, dtype=torch.int32, device=dev).expand(b, h, nq, nk).contiguous()
+    cnt = torch.full((b, h, nq), nk, dtype=torch.int32, device=dev)
+    o1, l1 = ops.sparse_fmha_fwd(case.q, case.k, case.v, full, cnt)
+    o2, l2 = ops.dense_fmha_fwd(case.q, case.k, case.v)
+    o3, l3 = ops.sparse_fmha_fwd(case.q, case.k, case.v, full, None)     # count from the -1 scan
+    _sync()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+def _random_lut(b, hl, nq, nk, row_len, seed, p_empty=0.15, dev="cpu"):
+    g = torch.Generator().manual_seed(seed)
+    lut = torch.full((b, hl, nq, row_len), -1, dtype=torch.int32)
+    cnt = torch.zeros((b, hl, nq), dtype=torch.int32)
+    for idx in np.ndindex(b, hl, nq):
+        if float(torch.rand(1, generator=g)) < p_empty:
+            continue
+        n = int(torch.randint(1, min(nk, row_len) + 1, (1,), generator=g))
+        sel = torch.sort(torch.randperm(nk, generator=g)[:n]).values
+        lut[idx][:n] = sel.to(torch.int32)
+        cnt[idx] = n
+    return lut.to(dev), cnt.to(dev)
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("per_kv", [False, True])
+def test_fmha_gqa_empty_rows_discontinuous_lut(dev, dtype, d, per_kv):
+    b, hq, hkv, sq, sk = 2, 8, 2, 256, 640
+    q = synth.normal((b, hq, sq, d), 11, 1, dtype, dev)
+    k = synth.normal((b, hkv, sk, d), 11, 2, dtype, dev)
+    v = synth.normal((b, hkv, sk, d), 11, 3, dtype, dev)
+    hl = hkv if per_kv else hq
+    lut, cnt = _random_lut(b, hl, sq // 64, sk // 64, sk // 64, seed=d + hl, dev=dev)
+    o, lse = ops.sparse_fmha_fwd(q, k, v, lut, cnt)
+    _sync()
+    _fmha_vs_oracle(q, k, v, lut, cnt, o, lse, lut_per_kv=per_kv)
+    # empty rows: exactly zero and -inf
+    cn = cnt.cpu().numpy()
+    on, ln = o.float().cpu().numpy(), lse.cpu().numpy()
+    ratio = hq // hkv
+    for ib, ih, qb in np.ndindex(b, hq, sq // 64):
+        row_cnt = cn[ib, ih // ratio if per_kv else ih, qb]
+        if row_cnt == 0:
+            assert (on[ib, ih, qb * 64:(qb + 1) * 64] == 0).all()
+            assert np.isneginf(ln[ib, ih, qb * 64:(qb + 1) * 64]).all()
+
+
+def test_fmha_strided_views_and_fp32_out(dev):
+    b, h, s, d = 1, 4, 256, 128
+    base = synth.normal((b, s, 3 * h, d), 12, 1, torch.bfloat16, dev)    # packed qkv-like layout
+    q = base[:, :, 0:h].permute(0, 2, 1, 3)
+    k = base[:, :, h:2 * h].permute(0, 2, 1, 3)
+    v = base[:, :, 2 * h:3 * h].permute(0, 2, 1, 3)
+    lut, cnt = _random_lut(b, h, s // 64, s // 64, s // 64, seed=3, p_empty=0.0, dev=dev)
+    o, lse = ops.sparse_fmha_fwd(q, k, v, lut, cnt, out_dtype=torch.float32)
+    _sync()
+    _fmha_vs_oracle(q, k, v, lut, cnt, o, lse)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 7])
+def test_fmha_splits_then_combine(dev, splits):
+    b, hq, hkv, sq, sk, d = 1, 4, 4, 128, 1024, 128
+    q = synth.normal((b, hq, sq, d), 13, 1, torch.float16, dev)
+    k = synth.normal((b, hkv, sk, d), 13, 2, torch.float16, dev)
+    v = synth.normal((b, hkv, sk, d), 13, 3, torch.float16, dev)
+    lut, cnt = _random_lut(b, hq, sq // 64, sk // 64, sk // 64, seed=splits, dev=dev)
+    op, lp = ops.sparse_fmha_fwd(q, k, v, lut, cnt, num_splits=splits)
+    o, lse = ops.attn_combine(op, lp, out_dtype=torch.float16)
+    _sync()
+    _fmha_vs_oracle(q, k, v, lut, cnt, o, lse)
+
+
+def test_fmha_long_rows(dev):
+    # 1024 K blocks per row: dense and a LUT of 700 blocks.
+    b, h, sq, sk, d = 1, 2, 128, 65536, 64
+    q = synth.normal((b, h, sq, d), 14, 1, torch.bfloat16, dev)
+    k = synth.normal((b, h, sk, d), 14, 2, torch.bfloat16, dev)
+    v = synth.normal((b, h, sk, d), 14, 3, torch.bfloat16, dev)
+    o, lse = ops.dense_fmha_fwd(q, k, v)
+    lut, cnt = _random_lut(b, h, sq // 64, sk // 64, sk // 64, seed=5, p_empty=0.0, dev=dev)
+    o2, l2 = ops.sparse_fmha_fwd(q, k, v, lut, cnt)
+    _sync()
+    _fmha_vs_oracle(q, k, v, None, None, o, lse)
+    _fmha_vs_oracle(q, k, v, lut, cnt, o2, l2)
+
+
+def test_determinism_relaunch(dev):
+    case = synth.mid_case(dev)
+    ref_bm = ops.build_block_map(case.q, case.k, case.topk, case.simthreshd1, return_debug=True)
+    ref_o, ref_l = ops.sparse_fmha_fwd(case.q, case.k, case.v, ref_bm["lut"], ref_bm["count"])
+    for _ in range(20):
+        bm = ops.build_block_map(case.q, case.k, case.topk, case.simthreshd1, return_debug=True)
+        o, lse = ops.sparse_fmha_fwd(case.q, case.k, case.v, bm["lut"], bm["count"])
+        assert torch.equal(bm["lut"], ref_bm["lut"]) and torch.equal(bm["prob"], ref_bm["prob"])
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_l)
+
+
+def test_validate_lut_detects_bad_rows(dev):
+    lut = torch.tensor([[0, 2, 5, -1], [3, 1, -1, -1], [0, 9, -1, -1], [1, -1, 2, -1]],
+                       dtype=torch.int32, device=dev)
+    assert ops.validate_lut(lut, None, 8) == 2          # row 1 descending, row 2 out of range
+    cnt = torch.tensor([3, 1, 1, 1], dtype=torch.int32, device=dev)
+    assert ops.validate_lut(lut, cnt, 8) == 2           # rows 1 and 3 have a non -1 tail
+
+
+# ---------------------------------------------------------------------------
+# two-pass combine workload: b1 h16 s_q 1024 s_k 32768 d128 bf16
+# ---------------------------------------------------------------------------
+
+def test_two_pass_combine_full_size(dev):
+    c = synth.combine_case(dev)
+    oa, la = ops.sparse_fmha_fwd(c.q, c.k, c.v, c.lut_a, c.count_a, out_dtype=torch.float32)
+    ob, lb = ops.sparse_fmha_fwd(c.q, c.k, c.v, c.lut_b, c.count_b, out_dtype=torch.float32)
+    o, lse = ops.attn_combine(torch.stack([oa, ob]), torch.stack([la, lb]), out_dtype=torch.bfloat16)
+    _sync()
+    cb = c.count_b.cpu().numpy()
+    assert (cb == 0).any() and np.isneginf(lb.cpu().numpy()[0][cb[0].repeat(64, axis=1) == 0]).all()
+    heads = [0, 7, 15]
+    qn, kn, vn = np64(c.q[:, heads]), np64(c.k[:, heads]), np64(c.v[:, heads])
+    la_np, lb_np = c.lut_a.cpu().numpy()[:, heads], c.lut_b.cpu().numpy()[:, heads]
+    ca_np, cb_np = c.count_a.cpu().numpy()[:, heads], cb[:, heads]
+    nk = c.k.shape[2] // 64
+    union = np.full(la_np.shape, -1, np.int32)
+    ucnt = np.zeros(ca_np.shape, np.int32)
+    for idx in np.ndindex(*ca_np.shape):
+        sel = sorted(set(la_np[idx][:ca_np[idx]]) | set(lb_np[idx][:cb_np[idx]]))
+        union[idx][:len(sel)] = sel
+        ucnt[idx] = len(sel)
+    assert union.shape[-1] == nk
+    ro, rl = oracle.block_sparse_attention(qn, kn, vn, union, ucnt)
+    check_o(o[:, heads], ro)
+    check_lse(lse[:, heads], rl)
+
+
+# ---------------------------------------------------------------------------
+# decode: token lists, grouped-query heads, split-K + combine
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,d", [(torch.float16, 64), (torch.bfloat16, 128)])
+@pytest.mark.parametrize("splits", [1, 4])
+def test_decode_ragged_lists(dev, dtype, d, splits):
+    c = synth.decode_case(dev, b=4, h_q=8, h_kv=2, s_k=5000, d=d, L=300, dtype=dtype, ragged=True,
+                          seed=splits)
+    lists = c.lists.clone()
+    lists[1, 1] = -1                                          # an empty list
+    if splits == 1:
+        o, lse = ops.sparse_fmha_fwd(c.q, c.k, c.v, lists, None, blk_q=1, blk_k=1)
+    else:
+        op, lp = ops.sparse_fmha_fwd(c.q, c.k, c.v, lists, None, blk_q=1, blk_k=1, num_splits=splits)
+        o, lse = ops.attn_combine(op, lp, out_dtype=dtype)
+    _sync()
+    ro, rl = oracle.token_list_attention(np64(c.q), np64(c.k), np64(c.v), lists.cpu().numpy())
+    check_o(o, ro)
+    check_lse(lse, rl)
+    assert (o[1, 4:8].float() == 0).all() and torch.isneginf(lse[1, 4:8]).all()
+
+
+def test_decode_full_size_sampled(dev):
+    c = synth.decode_case(dev)                 # b64 h_q32 h_kv8 s_k32768 d128 bf16, L 2048
+    op, lp = ops.sparse_fmha_fwd(c.q, c.k, c.v, c.lists, None, blk_q=1, blk_k=1, num_splits=8)
+    o, lse = ops.attn_combine(op, lp, out_dtype=torch.bfloat16)
+    _sync()
+    sample = [0, 9, 18, 27, 36, 45, 54, 63]
+    ro, rl = oracle.token_list_attention(np64(c.q[sample]), np64(c.k[sample]), np64(c.v[sample]),
+                                         c.lists[sample].cpu().numpy())
+    check_o(o[sample], ro)
+    check_lse(lse[sample], rl)
+
+
+# ---------------------------------------------------------------------------
+# headline workload: b2 h32 s16384 d128 fp16, sampled heads for attention
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("topk", [0.4, "mixed"])
+def test_headline_full_size(dev, topk):
+    tk = synth.mixed_topk(32) if topk == "mixed" else topk
+    case = synth.headline_case(dev, topk=tk)
+    res = ops.build_block_map(case.q, case.k, case.topk, case.simthreshd1, return_debug=True)
+    o, lse = ops.sparse_fmha_fwd(case.q, case.k, case.v, res["lut"], res["count"])
+    _sync()
+    # whole block map: bit-exact selection on the GPU's probabilities and flags
+    gp = np64(res["prob"])
+    lut, cnt, bm = oracle.select_from_probs(gp, np64(res["sim_q"]).astype(bool),
+                                            np64(res["sim_k"]).astype(bool), case.topk, None)
+    assert np.array_equal(res["lut"].cpu().numpy(), lut)
+    assert np.array_equal(res["count"].cpu().numpy(), cnt)
+    assert np.array_equal(res["bitmap"].cpu().numpy(), bm)
+    # sampled heads: pooled stage and attention against the oracle
+    heads = [0, 10, 21, 31]
+    qn, kn, vn = np64(case.q[:, heads]), np64(case.k[:, heads]), np64(case.v[:, heads])
+    ref = oracle.block_map(qn, kn, topk=[case.topk[h] for h in heads], simthreshd1=[0.001] * 4)
+    assert (np.abs(gp[:, heads] - ref["prob"]) <= 1e-3 * np.abs(ref["prob"]) + 1e-7).all()
+    ro, rl = oracle.block_sparse_attention(qn, kn, vn, res["lut"][:, heads].cpu().numpy(),
+                                           res["count"][:, heads].cpu().numpy())
+    check_o(o[:, heads], ro)
+    check_lse(lse[:, heads], rl)

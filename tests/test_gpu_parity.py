@@ -357,9 +357,17 @@ def test_determinism_relaunch(dev):
 def test_validate_lut_detects_bad_rows(dev):
     lut = torch.tensor([[0, 2, 5, -1], [3, 1, -1, -1], [0, 9, -1, -1], [1, -1, 2, -1]],
                        dtype=torch.int32, device=dev)
-    assert ops.validate_lut(lut, None, 8) == 2          # row 1 descending, row 2 out of range
+    # Without counts a row ends at its first -1: row 1 descends, row 2 holds 9 >= 8,
+    # row 3 has an entry after its first -1.
+    assert ops.validate_lut(lut, None, 8) == 3
+    good = lut[:1].contiguous()
+    assert ops.validate_lut(good, None, 8) == 0
+    # With counts 3, 1, 1, 1 rows 1..3 keep entries past their count.
     cnt = torch.tensor([3, 1, 1, 1], dtype=torch.int32, device=dev)
-    assert ops.validate_lut(lut, cnt, 8) == 2           # rows 1 and 3 have a non -1 tail
+    assert ops.validate_lut(lut, cnt, 8) == 3
+    cnt = torch.tensor([3, 1, 1, 1], dtype=torch.int32, device=dev)
+    assert ops.validate_lut(lut[:1].contiguous(), cnt[:1].contiguous(), 6) == 0
+    assert ops.validate_lut(lut[:1].contiguous(), cnt[:1].contiguous(), 5) == 1
 
 
 # ---------------------------------------------------------------------------

@@ -92,25 +92,42 @@ __device__ __forceinline__ void store4(void* base, int64_t off, float x0, float 
 // ---------------------------------------------------------------------------
 // block-LUT kernel
 // ---------------------------------------------------------------------------
+// One workgroup of 4 wavefronts per (Q-tile, head, batch, split).  Wave w owns
+// query rows 32*(w&1) .. +31 of the tile and keys 32*(w>>1) .. +31 of every
+// 64-key block, keeping its own running maximum, row sum and O^T; the two
+// key halves are merged in LDS at the end (the LSE combine of two partials).
+// K and V^T are double-buffered in LDS with one barrier per block; block i+1
+// is loaded into registers while block i is computed (so global latency
+// overlaps a whole block of compute) and written to LDS after it:
+//   * K is stored row-major with the 16-byte granules of row r XOR-swizzled
+//     by r, so the MFMA operand reads of 32 consecutive rows hit distinct banks;
+//   * V is written transposed (V^T) with the PV key permutation.
+// The running maximum is only moved when a row's new maximum exceeds it by
+// more than 2^8 (base-2 units), so most blocks skip rescaling O; the exported
+// LSE and O are exact for any reference maximum, and P stays below 2^8.
+constexpr float kRescaleSlack = 8.0f;
+
 template <class E, int D, bool OUT_F32>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void fmha_block_kernel(FmhaArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fmha_block_kernel(FmhaArgs a) {
   typedef typename E::T T;
-  constexpr int KP = D + 8;          // K tile pitch (elements)
-  constexpr int VP = 64 + 8;         // V^T tile pitch (elements)
-  constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
-  constexpr int RPP = 128 / CPR;     // K rows per staging pass
-  constexpr int NPASS = 64 / RPP;    // K staging passes
-  constexpr int NUV = D / 64;        // V units (4 keys x 8 d) per thread
-  constexpr int NKK = D / 16;        // k-steps of S^T
-  constexpr int NMD = D / 32;        // M-tiles of O^T
-  __shared__ __attribute__((aligned(16))) T sK[64 * KP];
-  __shared__ __attribute__((aligned(16))) T sV[D * VP];
+  constexpr int G16 = D / 8;                 // 16-byte granules per K/V row
+  constexpr int VP = 64 + 8;                 // V^T row pitch (elements)
+  constexpr int NKK = D / 16;                // k-steps of S^T
+  constexpr int NMD = D / 32;                // M-tiles of O^T
+  constexpr int KT = 64 * D;                 // elements per K buffer
+  constexpr int VT = D * VP;                 // elements per V^T buffer
+  constexpr int KLD = 64 * G16 / 256;        // direct K loads per thread per block
+  __shared__ __attribute__((aligned(16))) T sK[2 * KT];
+  __shared__ __attribute__((aligned(16))) T sV[2 * VT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hl = lane >> 5;
+  const int qh = wave & 1;                   // query half of the tile
+  const int kh = wave >> 1;                  // key half of every block
 
   const int64_t G = (int64_t)a.nqt * a.hq * a.b * a.splits;
   int64_t lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -137,15 +154,17 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int beg = split * chunk;
   const int nloc = max(0, min(n, beg + chunk) - beg);
 
-  const int q0 = qt * 64 + wave * 32;
+  const int q0 = qt * 64 + qh * 32;
   const int64_t orow = (int64_t)split * a.o_split_stride + bb * a.os[0] + hh * a.os[1] +
                        (int64_t)(q0 + l32) * a.os[2];
   float* lse_row = a.lse ? a.lse + (((int64_t)split * a.b + bb) * a.hq + hh) * a.sq : nullptr;
 
   if (nloc == 0) {
-    for (int d0 = hl * (D / 2); d0 < (hl + 1) * (D / 2); d0 += 4)
-      store4<E, OUT_F32>(a.o, orow + d0, 0.f, 0.f, 0.f, 0.f);
-    if (lse_row && hl == 0) lse_row[q0 + l32] = -INFINITY;
+    if (kh == 0) {
+      for (int d0 = hl * (D / 2); d0 < (hl + 1) * (D / 2); d0 += 4)
+        store4<E, OUT_F32>(a.o, orow + d0, 0.f, 0.f, 0.f, 0.f);
+      if (lse_row && hl == 0) lse_row[q0 + l32] = -INFINITY;
+    }
     return;
   }
 
@@ -159,131 +178,183 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const T* kbase = reinterpret_cast<const T*>(a.k) + bb * a.ks[0] + hk * a.ks[1];
   const T* vbase = reinterpret_cast<const T*>(a.v) + bb * a.vs[0] + hk * a.vs[1];
   const int64_t ks2 = a.ks[2], vs2 = a.vs[2];
-  const int kc = tid % CPR, kr = tid / CPR;
 
-  u32x4 kreg[NPASS];
-  u32x4 vreg[4 * NUV];
-  auto load_block = [&](int kb) {
-    const T* kp = kbase + (int64_t)kb * 64 * ks2 + kc * 8;
+  // K staging: thread t moves granules gi = t + 256 j of the tile; LDS granule
+  // (row r, slot sl) holds global granule sl ^ (r mod G16) of row r.
+  u32x4 kreg[KLD];
+  auto load_k = [&](int kb) {
+    const T* kp = kbase + (int64_t)kb * 64 * ks2;
 #pragma unroll
-    for (int p = 0; p < NPASS; ++p) kreg[p] = load16(kp + (int64_t)(kr + p * RPP) * ks2);
-    const T* vp = vbase + (int64_t)kb * 64 * vs2;
-#pragma unroll
-    for (int i = 0; i < NUV; ++i) {
-      const int u = tid + 128 * i;
-      const int c = u % CPR, g = u / CPR;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vreg[4 * i + j] = load16(vp + (int64_t)(4 * g + j) * vs2 + c * 8);
+    for (int j = 0; j < KLD; ++j) {
+      const int gi = tid + 256 * j;
+      const int r = gi / G16, sl = gi % G16;
+      kreg[j] = load16(kp + (int64_t)r * ks2 + (sl ^ (r % G16)) * 8);
     }
   };
-  auto store_block = [&]() {
+  auto store_k = [&](int buf) {
 #pragma unroll
-    for (int p = 0; p < NPASS; ++p)
-      *reinterpret_cast<u32x4*>(&sK[(kr + p * RPP) * KP + kc * 8]) = kreg[p];
+    for (int j = 0; j < KLD; ++j)
+      *reinterpret_cast<u32x4*>(&sK[buf * KT + (tid + 256 * j) * 8]) = kreg[j];
+  };
+  // V staging: thread (d chunk vc, key group vg) moves keys 4vg..4vg+3 x d 8vc..8vc+7.
+  // Each 16-lane group covers 8 key groups x 2 d chunks: its transposed 8-byte
+  // writes then land in 32 distinct banks (rows 8vc apart differ by 32 banks,
+  // the 8 key groups fill 16 banks), while each load still reads whole lines.
+  const int vg = (tid & 7) + 8 * ((tid >> (G16 == 16 ? 7 : 6)) & 1);
+  const int vc = ((tid >> 3) & 1) + 2 * ((tid >> 4) & (G16 / 2 - 1));
+  const bool v_active = tid < 16 * G16;
+  u32x4 vreg[4];
+  auto load_v = [&](int kb) {
+    if (v_active) {
+      const T* vp = vbase + (int64_t)(kb * 64 + 4 * vg) * vs2 + vc * 8;
 #pragma unroll
-    for (int i = 0; i < NUV; ++i) {
-      const int u = tid + 128 * i;
-      const int c = u % CPR, g = u / CPR;
-      const int pos = vt_pos(4 * g);
+      for (int j = 0; j < 4; ++j) vreg[j] = load16(vp + (int64_t)j * vs2);
+    }
+  };
+  auto store_v = [&](int buf) {
+    if (v_active) {
+      const int pos = vt_pos(4 * vg);
+      T* base = &sV[buf * VT];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t k0 = vreg[4 * i][w], k1 = vreg[4 * i + 1][w];
-        const uint32_t k2 = vreg[4 * i + 2][w], k3 = vreg[4 * i + 3][w];
+        const uint32_t k0 = vreg[0][w], k1 = vreg[1][w], k2 = vreg[2][w], k3 = vreg[3][w];
         const u32x2 ev = {(k0 & 0xFFFFu) | (k1 << 16), (k2 & 0xFFFFu) | (k3 << 16)};
         const u32x2 od = {(k0 >> 16) | (k1 & 0xFFFF0000u), (k2 >> 16) | (k3 & 0xFFFF0000u)};
-        *reinterpret_cast<u32x2*>(&sV[(c * 8 + 2 * w) * VP + pos]) = ev;
-        *reinterpret_cast<u32x2*>(&sV[(c * 8 + 2 * w + 1) * VP + pos]) = od;
+        *reinterpret_cast<u32x2*>(&base[(vc * 8 + 2 * w) * VP + pos]) = ev;
+        *reinterpret_cast<u32x2*>(&base[(vc * 8 + 2 * w + 1) * VP + pos]) = od;
       }
     }
   };
+  auto kb_of = [&](int i) { return list ? list[beg + i] : beg + i; };
 
   floatx16 acc_o[NMD];
 #pragma unroll
   for (int i = 0; i < NMD; ++i) acc_o[i] = floatx16{};
-  float m_run = -INFINITY;   // running row maximum, already times scale*log2(e)
-  float l_run = 0.f;         // this half-wave's share of the row sum
+  float m_run = -INFINITY;   // reference maximum, already times scale*log2(e)
+  float l_run = 0.f;         // this lane's share of the row sum
   const float c2 = a.scale_log2;
+  const int krow = 32 * kh + l32;                  // K row this lane feeds to S^T
+  const int kswz = krow % G16;
 
-  int kb_next = list ? list[beg] : beg;
-  load_block(kb_next);
+  // Prologue: block 0 staged in LDS, block 1 in flight in registers.
+  load_k(kb_of(0));
+  load_v(kb_of(0));
+  store_k(0);
+  store_v(0);
+  if (nloc > 1) {
+    load_k(kb_of(1));
+    load_v(kb_of(1));
+  }
+  __syncthreads();
+
 #pragma unroll 1
   for (int it = 0; it < nloc; ++it) {
-    if (it > 0) __syncthreads();
-    store_block();
-    __syncthreads();
-    if (it + 1 < nloc) {
-      kb_next = list ? list[beg + it + 1] : beg + it + 1;
-      load_block(kb_next);
+    const int cur = it & 1;
+    const T* kt = &sK[cur * KT];
+    const T* vt = &sV[cur * VT];
+
+    // S^T (32 keys x 32 queries) = K Q^T.
+    floatx16 s = floatx16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int g = (2 * kk + hl) ^ kswz;
+      const u32x4 af = *reinterpret_cast<const u32x4*>(&kt[(krow * G16 + g) * 8]);
+      s = mfma32<E>(af, qf[kk], s);
     }
 
-    // S^T = K Q^T : two 32-key M-tiles.
-    floatx16 s[2];
+    // Online softmax in base 2 over this lane's 16 scores.
+    float rmax = s[0];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      s[mt] = floatx16{};
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const u32x4 af = *reinterpret_cast<const u32x4*>(&sK[(32 * mt + l32) * KP + 16 * kk + 8 * hl]);
-        s[mt] = mfma32<E>(af, qf[kk], s[mt]);
-      }
-    }
-
-    // Online softmax in base 2; this lane holds 32 of the row's 64 scores.
-    float rmax = s[0][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) rmax = fmaxf(rmax, s[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[1][r]);
+    for (int r = 1; r < 16; ++r) rmax = fmaxf(rmax, s[r]);
     rmax = fmaxf(rmax, __shfl_xor(rmax, 32, kWave));
-    const float m_new = fmaxf(m_run, rmax * c2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    const float m_cand = rmax * c2;
+    const bool need = m_cand > m_run + kRescaleSlack;
+    if (__any(need)) {
+      const float m_new = need ? m_cand : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < NMD; ++i) acc_o[i] *= alpha;
+    }
     float psum = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[mt][r], c2, -m_new));
-        s[mt][r] = p;
-        psum += p;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -m_run));
+      s[r] = p;
+      psum += p;
     }
-    l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-    for (int i = 0; i < NMD; ++i) acc_o[i] *= alpha;
+    l_run += psum;
 
-    // P^T fragments: k-step ks uses registers 8(ks%2)..+7 of tile ks/2.
-    u32x4 pf[4];
+    // P^T fragments: k-step ks uses registers 8ks .. 8ks+7.
+    u32x4 pf[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        pf[ks][w] = E::pack2(s[ks >> 1][8 * (ks & 1) + 2 * w], s[ks >> 1][8 * (ks & 1) + 2 * w + 1]);
+      for (int w = 0; w < 4; ++w) pf[ks][w] = E::pack2(s[8 * ks + 2 * w], s[8 * ks + 2 * w + 1]);
     }
 
-    // O^T += V^T P^T.
+    // O^T += V^T P^T over this wave's 32 keys.
 #pragma unroll
-    for (int md = 0; md < NMD; ++md) {
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 af = *reinterpret_cast<const u32x4*>(&sV[(32 * md + l32) * VP + 16 * ks + 8 * hl]);
+      for (int md = 0; md < NMD; ++md) {
+        const u32x4 af = *reinterpret_cast<const u32x4*>(&vt[(32 * md + l32) * VP + 16 * (2 * kh + ks) + 8 * hl]);
         acc_o[md] = mfma32<E>(af, pf[ks], acc_o[md]);
       }
     }
+
+    // Stage block it+1 (loaded during this block's compute), hand the buffers
+    // over, then start loading block it+2.
+    if (it + 1 < nloc) {
+      store_k(cur ^ 1);
+      store_v(cur ^ 1);
+    }
+    __syncthreads();
+    if (it + 2 < nloc) {
+      const int kb2 = kb_of(it + 2);
+      load_k(kb2);
+      load_v(kb2);
+    }
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  // Merge the two key halves: waves kh = 1 publish (m, l, O^T); waves kh = 0 combine.
+  const float l_w = l_run + __shfl_xor(l_run, 32, kWave);
+  float* mrg = reinterpret_cast<float*>(sK) + qh * (NMD * 16 * 64);
+  float* ml = reinterpret_cast<float*>(sV) + qh * 64;
+  if (kh == 1) {
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mrg[(md * 16 + r) * 64 + lane] = acc_o[md][r];
+    if (hl == 0) {
+      ml[l32] = m_run;
+      ml[32 + l32] = l_w;
+    }
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  const float m1 = ml[l32], l1 = ml[32 + l32];
+  const float m = fmaxf(m_run, m1);
+  const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+  const float l_tot = l_w * a0 + l1 * a1;
+  const float inv = 1.0f / l_tot;
+  const float s0 = a0 * inv, s1 = a1 * inv;
 #pragma unroll
   for (int md = 0; md < NMD; ++md) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        x[i] = acc_o[md][r] * s0 + mrg[(md * 16 + r) * 64 + lane] * s1;
+      }
       const int d0 = 32 * md + 8 * g + 4 * hl;
-      store4<E, OUT_F32>(a.o, orow + d0, acc_o[md][4 * g] * inv, acc_o[md][4 * g + 1] * inv,
-                         acc_o[md][4 * g + 2] * inv, acc_o[md][4 * g + 3] * inv);
+      store4<E, OUT_F32>(a.o, orow + d0, x[0], x[1], x[2], x[3]);
     }
   }
-  if (lse_row && hl == 0) lse_row[q0 + l32] = (m_run + __log2f(l_tot)) * kLn2;
+  if (lse_row && hl == 0) lse_row[q0 + l32] = (m + __log2f(l_tot)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -490,8 +561,8 @@ template <class E, int D>
 static hipError_t launch_block_t(const FmhaArgs& a, bool out_f32, hipStream_t st) {
   const int64_t G = (int64_t)a.nqt * a.hq * a.b * a.splits;
   const dim3 grid((unsigned)(((G + 7) / 8) * 8));
-  if (out_f32) hipLaunchKernelGGL((fmha_block_kernel<E, D, true>), grid, dim3(128), 0, st, a);
-  else hipLaunchKernelGGL((fmha_block_kernel<E, D, false>), grid, dim3(128), 0, st, a);
+  if (out_f32) hipLaunchKernelGGL((fmha_block_kernel<E, D, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((fmha_block_kernel<E, D, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

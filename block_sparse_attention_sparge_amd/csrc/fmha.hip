@@ -96,34 +96,54 @@ __device__ __forceinline__ void store4(void* base, int64_t off, float x0, float 
 // query rows 32*(w&1) .. +31 of the tile and keys 32*(w>>1) .. +31 of every
 // 64-key block, keeping its own running maximum, row sum and O^T; the two
 // key halves are merged in LDS at the end (the LSE combine of two partials).
-// K and V^T are double-buffered in LDS with one barrier per block; block i+1
-// is loaded into registers while block i is computed (so global latency
-// overlaps a whole block of compute) and written to LDS after it:
+//
+// K and V blocks are double-buffered in LDS and arrive by direct global->LDS
+// loads (no registers on the way; on gfx950 this path moves gathered blocks
+// out of L2 much faster than loads into VGPRs).  The loads of block i+1 are
+// issued right after the barrier that retires block i-1, so they overlap the
+// compute of block i; one barrier per block.  These loads are issued from
+// inline assembly so the compiler does not guard every LDS read with a wait
+// for them; the kernel waits for them itself (vmcnt) before that barrier.
 //   * K is stored row-major with the 16-byte granules of row r XOR-swizzled
-//     by r, so the MFMA operand reads of 32 consecutive rows hit distinct banks;
-//   * V is written transposed (V^T) with the PV key permutation.
+//     by r mod 16, so S^T operand reads of 32 consecutive rows hit distinct
+//     banks.
+//   * V is stored row-major with granules XOR-swizzled by 2r, and the V^T
+//     operand of O^T += V^T P^T is read with the gfx950 transposing LDS read
+//     (ds_read_b64_tr_b16): within each 16-lane group, lane j receives element
+//     j%4 of the 4-element chunks addressed by lanes j/4 + 4t, t = 0..3.
 // The running maximum is only moved when a row's new maximum exceeds it by
 // more than 2^8 (base-2 units), so most blocks skip rescaling O; the exported
 // LSE and O are exact for any reference maximum, and P stays below 2^8.
 constexpr float kRescaleSlack = 8.0f;
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+#define SPARGE_LDS __attribute__((address_space(3)))
+
+// 16 bytes from global memory into LDS at (wave-uniform base) + 16 * lane.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_base), "v"(gsrc)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <class E, int D, bool OUT_F32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fmha_block_kernel(FmhaArgs a) {
   typedef typename E::T T;
   constexpr int G16 = D / 8;                 // 16-byte granules per K/V row
-  constexpr int VP = 64 + 8;                 // V^T row pitch (elements)
   constexpr int NKK = D / 16;                // k-steps of S^T
   constexpr int NMD = D / 32;                // M-tiles of O^T
-  constexpr int KT = 64 * D;                 // elements per K buffer
-  constexpr int VT = D * VP;                 // elements per V^T buffer
-  constexpr int KLD = 64 * G16 / 256;        // direct K loads per thread per block
-  __shared__ __attribute__((aligned(16))) T sK[2 * KT];
-  __shared__ __attribute__((aligned(16))) T sV[2 * VT];
+  constexpr int TILE = 64 * D;               // elements per K or V buffer
+  constexpr int NDMA = 64 * G16 / 256;       // direct loads per thread per tile
+  __shared__ __attribute__((aligned(16))) T sK[2 * TILE];
+  __shared__ __attribute__((aligned(16))) T sV[2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hl = lane >> 5;
   const int qh = wave & 1;                   // query half of the tile
@@ -150,6 +170,9 @@ void fmha_block_kernel(FmhaArgs a) {
   } else {
     n = a.nkb;
   }
+  // The row length is the same for every lane; saying so keeps the loop
+  // uniform and lets the LUT entries come through scalar loads.
+  n = __builtin_amdgcn_readfirstlane(n);
   const int chunk = (n + a.splits - 1) / a.splits;
   const int beg = split * chunk;
   const int nloc = max(0, min(n, beg + chunk) - beg);
@@ -178,51 +201,22 @@ void fmha_block_kernel(FmhaArgs a) {
   const T* kbase = reinterpret_cast<const T*>(a.k) + bb * a.ks[0] + hk * a.ks[1];
   const T* vbase = reinterpret_cast<const T*>(a.v) + bb * a.vs[0] + hk * a.vs[1];
   const int64_t ks2 = a.ks[2], vs2 = a.vs[2];
+  const uint32_t sk_lds = (uint32_t)(uintptr_t)((SPARGE_LDS void*)sK);
+  const uint32_t sv_lds = (uint32_t)(uintptr_t)((SPARGE_LDS void*)sV);
 
-  // K staging: thread t moves granules gi = t + 256 j of the tile; LDS granule
-  // (row r, slot sl) holds global granule sl ^ (r mod G16) of row r.
-  u32x4 kreg[KLD];
-  auto load_k = [&](int kb) {
+  // Block kb into buffer buf: instruction J of the tile fills LDS granules
+  // 64J .. 64J+63; granule (row r, slot sl) holds global granule sl ^ swz(r).
+  auto issue_block = [&](int kb, int buf) {
     const T* kp = kbase + (int64_t)kb * 64 * ks2;
+    const T* vp = vbase + (int64_t)kb * 64 * vs2;
 #pragma unroll
-    for (int j = 0; j < KLD; ++j) {
-      const int gi = tid + 256 * j;
+    for (int j = 0; j < NDMA; ++j) {
+      const int J = wave * NDMA + j;
+      const int gi = 64 * J + lane;
       const int r = gi / G16, sl = gi % G16;
-      kreg[j] = load16(kp + (int64_t)r * ks2 + (sl ^ (r % G16)) * 8);
-    }
-  };
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < KLD; ++j)
-      *reinterpret_cast<u32x4*>(&sK[buf * KT + (tid + 256 * j) * 8]) = kreg[j];
-  };
-  // V staging: thread (d chunk vc, key group vg) moves keys 4vg..4vg+3 x d 8vc..8vc+7.
-  // Each 16-lane group covers 8 key groups x 2 d chunks: its transposed 8-byte
-  // writes then land in 32 distinct banks (rows 8vc apart differ by 32 banks,
-  // the 8 key groups fill 16 banks), while each load still reads whole lines.
-  const int vg = (tid & 7) + 8 * ((tid >> (G16 == 16 ? 7 : 6)) & 1);
-  const int vc = ((tid >> 3) & 1) + 2 * ((tid >> 4) & (G16 / 2 - 1));
-  const bool v_active = tid < 16 * G16;
-  u32x4 vreg[4];
-  auto load_v = [&](int kb) {
-    if (v_active) {
-      const T* vp = vbase + (int64_t)(kb * 64 + 4 * vg) * vs2 + vc * 8;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vreg[j] = load16(vp + (int64_t)j * vs2);
-    }
-  };
-  auto store_v = [&](int buf) {
-    if (v_active) {
-      const int pos = vt_pos(4 * vg);
-      T* base = &sV[buf * VT];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t k0 = vreg[0][w], k1 = vreg[1][w], k2 = vreg[2][w], k3 = vreg[3][w];
-        const u32x2 ev = {(k0 & 0xFFFFu) | (k1 << 16), (k2 & 0xFFFFu) | (k3 << 16)};
-        const u32x2 od = {(k0 >> 16) | (k1 & 0xFFFF0000u), (k2 >> 16) | (k3 & 0xFFFF0000u)};
-        *reinterpret_cast<u32x2*>(&base[(vc * 8 + 2 * w) * VP + pos]) = ev;
-        *reinterpret_cast<u32x2*>(&base[(vc * 8 + 2 * w + 1) * VP + pos]) = od;
-      }
+      const uint32_t off = (uint32_t)((buf * TILE + J * 64 * 8) * sizeof(T));
+      dma16(kp + (int64_t)r * ks2 + (sl ^ (r % G16)) * 8, sk_lds + off);
+      dma16(vp + (int64_t)r * vs2 + (sl ^ ((2 * r) % G16)) * 8, sv_lds + off);
     }
   };
   auto kb_of = [&](int i) { return list ? list[beg + i] : beg + i; };
@@ -235,23 +229,25 @@ void fmha_block_kernel(FmhaArgs a) {
   const float c2 = a.scale_log2;
   const int krow = 32 * kh + l32;                  // K row this lane feeds to S^T
   const int kswz = krow % G16;
+  // V^T operand (transposing read): lane (s = lane%16, group g16 = lane/16)
+  // points at row 32kh + 16ks + 8c + 4(g16/2) + s/4, column
+  // 32md + 16(g16%2) + 4(s%4), for PV k-step ks and half c of the 8 keys.
+  const int vs16 = lane & 15, vgrp = lane >> 4;
+  const int vrow0 = 32 * kh + 4 * (vgrp >> 1) + (vs16 >> 2);
+  const int vcol0 = 16 * (vgrp & 1) + 4 * (vs16 & 3);
 
-  // Prologue: block 0 staged in LDS, block 1 in flight in registers.
-  load_k(kb_of(0));
-  load_v(kb_of(0));
-  store_k(0);
-  store_v(0);
-  if (nloc > 1) {
-    load_k(kb_of(1));
-    load_v(kb_of(1));
-  }
+  // Prologue: block 0 in LDS, block 1 in flight, LUT entry of block 2 read.
+  issue_block(kb_of(0), 0);
+  wait_dma();
   __syncthreads();
+  if (nloc > 1) issue_block(kb_of(1), 1);
+  int kb_ahead = nloc > 2 ? kb_of(2) : 0;
 
 #pragma unroll 1
   for (int it = 0; it < nloc; ++it) {
     const int cur = it & 1;
-    const T* kt = &sK[cur * KT];
-    const T* vt = &sV[cur * VT];
+    const T* kt = &sK[cur * TILE];
+    const SPARGE_LDS T* vt = (const SPARGE_LDS T*)&sV[cur * TILE];
 
     // S^T (32 keys x 32 queries) = K Q^T.
     floatx16 s = floatx16{};
@@ -299,22 +295,29 @@ void fmha_block_kernel(FmhaArgs a) {
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int md = 0; md < NMD; ++md) {
-        const u32x4 af = *reinterpret_cast<const u32x4*>(&vt[(32 * md + l32) * VP + 16 * (2 * kh + ks) + 8 * hl]);
+        u32x4 af;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int r = vrow0 + 16 * ks + 8 * c;
+          const int col = 32 * md + vcol0;
+          const int slot = (col >> 3) ^ ((2 * r) % G16);
+          const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (SPARGE_LDS short4v*)(vt + r * D + slot * 8 + (col & 7)));
+          const u32x2 w2 = __builtin_bit_cast(u32x2, x);
+          af[2 * c] = w2[0];
+          af[2 * c + 1] = w2[1];
+        }
         acc_o[md] = mfma32<E>(af, pf[ks], acc_o[md]);
       }
     }
 
-    // Stage block it+1 (loaded during this block's compute), hand the buffers
-    // over, then start loading block it+2.
-    if (it + 1 < nloc) {
-      store_k(cur ^ 1);
-      store_v(cur ^ 1);
-    }
+    // Block it+1 must have landed before the barrier hands the buffers over;
+    // then the buffer just consumed receives block it+2.
+    wait_dma();
     __syncthreads();
     if (it + 2 < nloc) {
-      const int kb2 = kb_of(it + 2);
-      load_k(kb2);
-      load_v(kb2);
+      issue_block(kb_ahead, cur);
+      if (it + 3 < nloc) kb_ahead = kb_of(it + 3);
     }
   }
 

@@ -29,6 +29,9 @@ if ROOT not in sys.path:
 
 PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+# rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the sparse FMHA (bytes per launch,
+# copy-calibrated); quoted only while it matches the current kernel source.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fmha_block_headline_traffic.md")
 B, H, S, D = 2, 32, 16384, 128
 
 
@@ -207,6 +210,8 @@ def main(argv=None) -> int:
 
     main_arm = arms[0.4]
     value = dense_flops / (main_arm["step_ms"] * 1e-3) / 1e12
+    from block_sparse_attention_sparge_amd import profile_summary
+    traffic = profile_summary.read_traffic(TRAFFIC_PROFILE, "topk 0.4")
     act = f_blk * main_arm["pairs"] / (main_arm["fmha_ms_mean"] * 1e-3) / 1e12
     res = {
         "metric": "sparse attn fwd ms + dense-equiv TFLOPS & speedup vs dense FMHA, s=16k topk 0.4/0.1",
@@ -225,7 +230,8 @@ def main(argv=None) -> int:
                                "block-centroid+noise Q/K", "global_batch": B, "seq_len": S,
                    "heads": H, "head_dim": D, "topk": 0.4, "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": round(act, 1), "peak": PEAK_FP16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(act / PEAK_FP16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(act / PEAK_FP16_TFLOPS, 4),
+                     "traffic": None if traffic is None else round(traffic),
                      "kernel": "fmha_block_kernel (sparse_fmha_fwd)",
                      "flops_per_launch": f_blk * main_arm["pairs"],
                      "avg_launch_ms": round(main_arm["fmha_ms_mean"], 4)},

@@ -1,0 +1,179 @@
+"""Summarise rocprofv3 CSV output of a bench.py run into short markdown files.
+
+Two reports:
+
+  trace    kernel statistics (rocprofv3 --kernel-trace --stats) plus the
+           per-arm durations of the sparse FMHA launches;
+  traffic  HBM bytes per sparse FMHA launch from two counter runs
+           (--pmc FETCH_SIZE, then --pmc WRITE_SIZE), each scaled by what the
+           same counter reads for a plain device-to-device copy of known size.
+
+bench.py times its arms in a fixed order (topk 0.4, topk 0.1, dense), each
+arm calling the FMHA 2 * (warmup + steps) times (FMHA alone, then block map +
+FMHA), and the dense arm 2 + max(5, steps // 2) times; dispatches are assigned
+to arms in that order.  The traffic report records the SHA-256 of the FMHA
+source so that bench.py stops quoting it once the kernel changes.
+
+Usage:
+  python -m block_sparse_attention_sparge_amd.profile_summary trace DIR \
+      --steps K --warmup W --command "..." > profiles/x.md
+  python -m block_sparse_attention_sparge_amd.profile_summary traffic \
+      --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \
+      --copy-bytes N --steps K --warmup W --command "..." > profiles/y.md
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+FMHA_SOURCE = os.path.join(PKG, "csrc", "fmha.hip")
+FMHA_KERNEL = "fmha_block_kernel"
+
+
+def source_sha256(path: str = FMHA_SOURCE) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _one(dirpath: str, pattern: str) -> str:
+    hits = sorted(glob.glob(os.path.join(dirpath, "**", pattern), recursive=True))
+    if not hits:
+        raise SystemExit(f"no {pattern} under {dirpath}")
+    return hits[0]
+
+
+def arm_slices(steps: int, warmup: int):
+    per = 2 * (warmup + steps)
+    dense = 2 + max(5, steps // 2)
+    return [("topk 0.4", 0, per), ("topk 0.1", per, 2 * per), ("dense", 2 * per, 2 * per + dense)]
+
+
+def _fmha_dispatches(rows, key="Dispatch_Id"):
+    sel = [r for r in rows if FMHA_KERNEL in r["Kernel_Name"]]
+    sel.sort(key=lambda r: int(r[key]))
+    return sel
+
+
+def trace_report(dirpath: str, steps: int, warmup: int, command: str) -> str:
+    stats = list(csv.DictReader(open(_one(dirpath, "*kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(_one(dirpath, "*kernel_trace.csv"))))
+    out = ["# Kernel trace summary (rocprofv3 --kernel-trace --stats)", "",
+           "Command:", "", "```", command, "```", "",
+           "| kernel | calls | average us | share % |", "|---|---|---|---|"]
+    for r in stats:
+        name = r["Name"].replace("|", "/")
+        if len(name) > 110:
+            name = name[:107] + "..."
+        out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    fm = _fmha_dispatches(trace)
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in fm]
+    out += ["", f"Sparse FMHA launches by bench arm (dispatch order; steps {steps}, warmup {warmup}):", "",
+            "| arm | launches | mean us | median us | min us |", "|---|---|---|---|---|"]
+    for name, a, b in arm_slices(steps, warmup):
+        d = dur[a:b]
+        if d:
+            out.append(f"| {name} | {len(d)} | {statistics.mean(d):.1f} | {statistics.median(d):.1f} | {min(d):.1f} |")
+    return "\n".join(out) + "\n"
+
+
+def _counter_means(dirpath: str, steps: int, warmup: int):
+    rows = list(csv.DictReader(open(_one(dirpath, "*counter_collection.csv"))))
+    fm = _fmha_dispatches(rows)
+    vals = {}
+    for r in fm:
+        vals.setdefault(int(r["Dispatch_Id"]), 0.0)
+        vals[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    ordered = [vals[k] for k in sorted(vals)]
+    res = {}
+    for name, a, b in arm_slices(steps, warmup):
+        v = ordered[a:b]
+        if v:
+            res[name] = sum(v) / len(v)
+    return res
+
+
+def _copy_kib(dirpath: str) -> float:
+    rows = list(csv.DictReader(open(_one(dirpath, "*counter_collection.csv"))))
+    per = {}
+    for r in rows:
+        per.setdefault(int(r["Dispatch_Id"]), 0.0)
+        per[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    vals = list(per.values())
+    return statistics.median(vals)
+
+
+def traffic_report(fetch: str, write: str, copy_fetch: str, copy_write: str, copy_bytes: int,
+                   steps: int, warmup: int, command: str) -> str:
+    fe = _counter_means(fetch, steps, warmup)
+    wr = _counter_means(write, steps, warmup)
+    cf, cw = _copy_kib(copy_fetch), _copy_kib(copy_write)
+    fetch_scale = copy_bytes / 1024.0 / cf
+    write_scale = copy_bytes / 1024.0 / cw
+    out = ["# HBM traffic of the sparse FMHA (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)", "",
+           "Commands:", "", "```", command, "```", "",
+           f"Copy calibration: a device-to-device copy of {copy_bytes} bytes reads FETCH_SIZE "
+           f"{cf:.0f} KiB and WRITE_SIZE {cw:.0f} KiB per dispatch, so the scale factors are "
+           f"{fetch_scale:.3f} (fetch) and {write_scale:.3f} (write).", "",
+           "| arm | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled bytes per launch |", "|---|---|---|---|"]
+    summary = {}
+    for arm in fe:
+        b = fe[arm] * fetch_scale * 1024 + wr.get(arm, 0.0) * write_scale * 1024
+        summary[arm] = b
+        out.append(f"| {arm} | {fe[arm]:.0f} | {wr.get(arm, 0.0):.0f} | {b:.4g} |")
+    rec = {"kernel": FMHA_KERNEL, "source_sha256": source_sha256(), "fetch_scale": fetch_scale,
+           "write_scale": write_scale, "bytes_per_launch": summary}
+    out += ["", "Machine-readable line read by bench.py:", "", "traffic_json: " + json.dumps(rec)]
+    return "\n".join(out) + "\n"
+
+
+def read_traffic(path: str, arm: str):
+    """Scaled HBM bytes per launch for `arm`, or None when the profile is missing
+    or was taken on a different FMHA source."""
+    try:
+        for line in open(path):
+            if line.startswith("traffic_json: "):
+                rec = json.loads(line[len("traffic_json: "):])
+                if rec.get("source_sha256") != source_sha256():
+                    return None
+                return rec["bytes_per_launch"].get(arm)
+    except OSError:
+        return None
+    return None
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("dir")
+    for p in (t,):
+        p.add_argument("--steps", type=int, required=True)
+        p.add_argument("--warmup", type=int, required=True)
+        p.add_argument("--command", required=True)
+    f = sub.add_parser("traffic")
+    f.add_argument("--fetch", required=True)
+    f.add_argument("--write", required=True)
+    f.add_argument("--copy-fetch", required=True)
+    f.add_argument("--copy-write", required=True)
+    f.add_argument("--copy-bytes", type=int, required=True)
+    f.add_argument("--steps", type=int, required=True)
+    f.add_argument("--warmup", type=int, required=True)
+    f.add_argument("--command", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "trace":
+        sys.stdout.write(trace_report(a.dir, a.steps, a.warmup, a.command))
+    else:
+        sys.stdout.write(traffic_report(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes,
+                                        a.steps, a.warmup, a.command))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -197,6 +197,12 @@ void fmha_block_kernel(FmhaArgs a) {
   u32x4 qf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) qf[kk] = load16(qp + 16 * kk);
+  // Consume the Q loads here.  The K/V loads below are invisible to the
+  // compiler's wait counting; if Q were still pending at the loop, the waits
+  // it places before the first S^T MFMAs would also wait for the K/V
+  // prefetches in flight (the hardware counter does not tell them apart).
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qf[kk]));
 
   const T* kbase = reinterpret_cast<const T*>(a.k) + bb * a.ks[0] + hk * a.ks[1];
   const T* vbase = reinterpret_cast<const T*>(a.v) + bb * a.vs[0] + hk * a.vs[1];

@@ -4,18 +4,26 @@
 // mean pool, cosine similarity, pooled QK, top-k / cdfthreshd selection into a
 // BlockMap LUT, with per-head topk / simthreshd1 / cdfthreshd.  The same page
 // lists sort-based top-k as the replacement for an O(nk^2) argmax that hurts
-// at long sequences; the selector here sorts each row with a bitonic network
-// held in the registers of one wavefront.
+// at long sequences.  Here the top-k count needs no full sort: the n-th
+// largest probability is found by bisection on its bits with wavefront
+// ballots (about 31 rounds of popcounts), and ties at it go to the lower
+// block index; the cdf rule needs the order itself and sorts each row with a
+// bitonic network held in the registers of one wavefront.
 //
 // Two kernels:
 //   pool_sim     one wavefront per 64-token block of Q or K: reads the block
 //                once (HBM bound), writes its fp32 mean and the gate flag
 //                (mean pairwise cosine of the block's tokens > simthreshd1).
 //   score_select one workgroup per 16 Q-tiles of one (b, h): pooled scores
-//                against every K block mean, fp32 softmax, a 64-bit-key bitonic
-//                sort per row (probability descending, block index ascending),
-//                top-k or cdf count, and an ascending LUT written by a prefix
-//                scan (no atomics, so the output is deterministic).
+//                against every K block mean with fp32 MFMA fed straight from
+//                memory, fp32 softmax, then the selection in the order
+//                (probability descending, block index ascending), the four
+//                rows of each wavefront interleaved step by step:
+//                top-k finds the n-th largest probability by bisection on its
+//                bits with wavefront ballots and takes ties at it by ascending
+//                index; cdf needs the order itself and sorts the row with a
+//                64-bit-key bitonic network.  The ascending LUT is written by
+//                a prefix scan (no atomics, so the output is deterministic).
 #include "common.h"
 #include "kernels.h"
 
@@ -155,12 +163,24 @@ __device__ __forceinline__ void bitonic_desc(uint64_t (&key)[KPL], int lane) {
   }
 }
 
+// Number of this wave's valid keys (bits of probabilities) that are >= t.
+template <int KPL>
+__device__ __forceinline__ int count_at_least(const uint32_t (&pb)[KPL], const bool (&valid)[KPL],
+                                              uint32_t t) {
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) c += __popcll(__ballot(valid[j] && pb[j] >= t));
+  return c;
+}
+
 template <int D, int KPL>
 __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
   constexpr int NKP = 64 * KPL;
-  __shared__ float s_qm[kSelRows][D];
-  __shared__ float s_score[kSelRows][NKP];
-  __shared__ uint8_t s_sel[4][NKP];
+  constexpr int SP = NKP + 4;            // padded pitch of a score row (floats)
+  constexpr int NG = D / 16;             // 16-wide slices of the head dimension
+  static_assert(kSelRows == 16, "one 16-row MFMA tile per group");
+  __shared__ __attribute__((aligned(16))) float s_score[kSelRows][SP];
+  __shared__ uint8_t s_sel[kSelRows][NKP];
   __shared__ float s_sorted[4][NKP];
 
   const int tid = threadIdx.x;
@@ -173,150 +193,253 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
   const int hh = (int)(bh % a.h);
   const int nk = a.nk;
 
-  // Pooled Q rows of this group into LDS.
-  const float* qm = a.q_mean + (bh * a.nq + qb0) * D;
-  for (int i = tid; i < kSelRows * D / 4; i += 256) {
-    const int r = (i * 4) / D;
-    floatx4 v = {0.f, 0.f, 0.f, 0.f};
-    if (r < rows) v = *reinterpret_cast<const floatx4*>(qm + i * 4);
-    *reinterpret_cast<floatx4*>(&s_qm[0][0] + i * 4) = v;
+  // Pooled scores with fp32 MFMA (16x16x4: exact products, fp32 sums).  The
+  // contraction over the head dimension may visit it in any order as long as
+  // both operands agree, so lane (m16, k4) feeds, at step t of slice g,
+  // element d = 16g + 4k4 + t: each operand is then one 16-byte load per
+  // slice, straight from memory into registers.  Wave w computes the columns
+  // 64c + 16w .. +15 of the 16 x nk score tile.
+  const int m16 = lane & 15, k4 = lane >> 4;
+  floatx4 qf[NG];
+  {
+    const float* qrow = a.q_mean + (bh * a.nq + qb0 + m16) * D + 4 * k4;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      qf[g] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (m16 < rows) qf[g] = *reinterpret_cast<const floatx4*>(qrow + 16 * g);
+    }
+  }
+  const float* km = a.k_mean + bh * nk * D;
+  const uint8_t* simk = a.sim_k + bh * nk;
+  auto load_k = [&](floatx4 (&kf)[NG], int kb) {
+    const float* krow = km + (int64_t)kb * D + 4 * k4;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      kf[g] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (kb < nk) kf[g] = *reinterpret_cast<const floatx4*>(krow + 16 * g);
+    }
+  };
+  floatx4 kf[NG], kn[NG];
+  load_k(kf, 16 * wave + m16);
+#pragma unroll 1
+  for (int c = 0; c < KPL; ++c) {
+    const int kb = 64 * c + 16 * wave + m16;
+    if (c + 1 < KPL) load_k(kn, kb + 64);
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[g][t], kf[g][t], acc, 0, 0, 0);
+    }
+    // C: lane holds column kb for rows 4*k4 .. 4*k4+3.
+    const bool live = kb < nk && simk[kb] != 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_score[4 * k4 + i][kb] = live ? acc[i] * a.scale : -INFINITY;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) kf[g] = kn[g];
   }
   __syncthreads();
 
-  // Pooled scores: one K block per thread, all 16 rows.
-  const float* km = a.k_mean + bh * nk * D;
-  const uint8_t* simk = a.sim_k + bh * nk;
-  for (int kb = tid; kb < NKP; kb += 256) {
-    float acc[kSelRows];
+  // Gate flags used by every row of the group, read once.
+  bool kgate[KPL];
 #pragma unroll
-    for (int r = 0; r < kSelRows; ++r) acc[r] = 0.f;
-    const bool live = kb < nk && simk[kb] != 0;
-    if (live) {
-      const float* kr = km + (int64_t)kb * D;
-      for (int d0 = 0; d0 < D; d0 += 4) {
-        const floatx4 kv = *reinterpret_cast<const floatx4*>(kr + d0);
-#pragma unroll
-        for (int r = 0; r < kSelRows; ++r) {
-          const floatx4 qv = *reinterpret_cast<const floatx4*>(&s_qm[r][d0]);
-          acc[r] = fmaf(qv[0], kv[0], acc[r]);
-          acc[r] = fmaf(qv[1], kv[1], acc[r]);
-          acc[r] = fmaf(qv[2], kv[2], acc[r]);
-          acc[r] = fmaf(qv[3], kv[3], acc[r]);
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kSelRows; ++r) s_score[r][kb] = live ? acc[r] * a.scale : -INFINITY;
+  for (int j = 0; j < KPL; ++j) {
+    const int e = lane * KPL + j;
+    kgate[j] = e < nk && simk[e] == 0;                 // K block forced on
   }
-  __syncthreads();
+  const bool qflag_lane = lane < rows && a.sim_q[bh * a.nq + qb0 + lane] != 0;
+  const uint64_t qflags = __ballot(qflag_lane);
 
   const int nsel_h = a.nsel[hh];
   const double cdf_h = (double)a.cdf[hh];
+  constexpr int RW = kSelRows / 4;       // rows per wave: 4i + wave, i < RW
+  bool valid[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) valid[j] = lane * KPL + j < nk;
+
+  // The RW rows of a wave go through every step side by side, so that their
+  // reduction and ballot chains overlap instead of running one after another.
+  // Softmax of each pooled row (fp32).
+  float p[RW][KPL];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const int r = 4 * i + wave;          // rows past the end hold finite scores of zero Q rows
+    const floatx4* src = reinterpret_cast<const floatx4*>(&s_score[r][lane * KPL]);
+#pragma unroll
+    for (int j4 = 0; j4 < KPL / 4 + (KPL < 4); ++j4) {
+      const floatx4 v = src[j4];
+#pragma unroll
+      for (int t = 0; t < 4 && 4 * j4 + t < KPL; ++t) p[i][4 * j4 + t] = valid[4 * j4 + t] ? v[t] : -INFINITY;
+    }
+  }
+  float mx[RW], sum[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    mx[i] = p[i][0];
+#pragma unroll
+    for (int j = 1; j < KPL; ++j) mx[i] = fmaxf(mx[i], p[i][j]);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1)
+#pragma unroll
+    for (int i = 0; i < RW; ++i) mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], m, kWave));
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    sum[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      p[i][j] = mx[i] == -INFINITY ? 0.f : expf(p[i][j] - mx[i]);
+      sum[i] += p[i][j];
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1)
+#pragma unroll
+    for (int i = 0; i < RW; ++i) sum[i] += __shfl_xor(sum[i], m, kWave);
+#pragma unroll
+  for (int i = 0; i < RW; ++i)
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) p[i][j] = sum[i] > 0.f ? p[i][j] / sum[i] : 0.f;
+
+  if (a.prob) {
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      if (4 * i + wave >= rows) continue;
+      const int64_t row = bh * a.nq + qb0 + 4 * i + wave;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j)
+        if (valid[j]) a.prob[row * nk + lane * KPL + j] = p[i][j];
+    }
+  }
+
+  // chosen[i][j]: element lane*KPL + j of row i is among the first n of the
+  // order (probability descending, block index ascending).  Probabilities are
+  // >= +0, so their bit patterns order like their values.
+  bool chosen[RW][KPL];
+  if (nsel_h > 0) {
+    // top-k: T = the n-th largest probability (bits), by bisection on
+    // count(>= lo) >= n > count(>= hi); 31 halvings close a range of 2^31.
+    uint32_t lo[RW], hi[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) { lo[i] = 0u; hi[i] = 0x7F800000u; }
 #pragma unroll 1
-  for (int it = 0; it < kSelRows / 4; ++it) {
-    const int r = it * 4 + wave;
-    const bool active = r < rows;
-    const int qb = qb0 + (active ? r : 0);
-    const int64_t row = bh * a.nq + qb;
-
-    // Softmax of the pooled row (fp32).
-    float sc[KPL];
-    float mx = -INFINITY;
+    for (int round = 0; round < 31; ++round) {
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-      const int e = lane * KPL + j;
-      sc[j] = e < nk ? s_score[active ? r : 0][e] : -INFINITY;
-      mx = fmaxf(mx, sc[j]);
+      for (int i = 0; i < RW; ++i) {
+        const uint32_t mid = lo[i] + ((hi[i] - lo[i]) >> 1);
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j)
+          c += __popcll(__ballot(valid[j] && __builtin_bit_cast(uint32_t, p[i][j]) >= mid));
+        if (c >= nsel_h) lo[i] = mid;
+        else hi[i] = mid;
+      }
     }
-    mx = wave_max(mx);
-    float p[KPL];
-    float sum = 0.f;
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-      p[j] = mx == -INFINITY ? 0.f : expf(sc[j] - mx);
-      sum += p[j];
+    for (int i = 0; i < RW; ++i) {
+      const uint32_t t = lo[i];
+      int above = 0, ties = 0;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        const uint32_t pb = __builtin_bit_cast(uint32_t, p[i][j]);
+        above += __popcll(__ballot(valid[j] && pb > t));      // strictly greater than T
+        ties += (valid[j] && pb == t) ? 1 : 0;
+      }
+      const int need = nsel_h - above;                           // ties at T to take
+      int tie_rank = wave_inclusive_scan(ties) - ties;           // ties before this lane
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        const uint32_t pb = __builtin_bit_cast(uint32_t, p[i][j]);
+        const bool tie = valid[j] && pb == t;
+        chosen[i][j] = valid[j] && (pb > t || (tie && tie_rank < need));
+        tie_rank += tie ? 1 : 0;
+      }
     }
-    sum = wave_sum(sum);
+  } else {
+    // cdf: per row, sort into the order, then a running fp64 sum one block
+    // at a time.  Keys: (probability bits, ~block index), descending;
+    // padding keys (0) sort last.  Rows go one at a time through LDS (each
+    // wave owns its rows of s_score and s_sel), which keeps every register
+    // array statically indexed.
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) p[j] = sum > 0.f ? p[j] / sum : 0.f;
-
-    if (active && a.prob) {
+    for (int i = 0; i < RW; ++i)
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) s_score[4 * i + wave][lane * KPL + j] = p[i][j];
+#pragma unroll 1
+    for (int i = 0; i < RW; ++i) {
+      const int r = 4 * i + wave;
+      uint64_t key[KPL];
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
         const int e = lane * KPL + j;
-        if (e < nk) a.prob[row * nk + e] = p[j];
+        key[j] = valid[j] ? (((uint64_t)__builtin_bit_cast(uint32_t, s_score[r][e]) << 32) |
+                             (uint64_t)(~(uint32_t)e))
+                          : 0ull;
       }
-    }
-
-    // Rank: 64-bit keys (probability bits, ~block index), sorted descending.
-    // Probabilities are >= +0, so their bit patterns order like their values;
-    // ~kb makes the lower block index win ties; padding keys (0) sort last.
-    uint64_t key[KPL];
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-      const int e = lane * KPL + j;
-      key[j] = e < nk ? (((uint64_t)__builtin_bit_cast(uint32_t, p[j]) << 32) |
-                         (uint64_t)(~(uint32_t)e))
-                      : 0ull;
-    }
-    bitonic_desc<KPL>(key, lane);
-
-    int n = nsel_h;
-    if (n <= 0) {
-      // cdf mode: running fp64 sum in sorted order, one block at a time.
+      bitonic_desc<KPL>(key, lane);
 #pragma unroll
       for (int j = 0; j < KPL; ++j)
         s_sorted[wave][lane * KPL + j] = __builtin_bit_cast(float, (uint32_t)(key[j] >> 32));
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) s_sel[r][lane * KPL + j] = 0;
       __builtin_amdgcn_s_waitcnt(0xc07f);
       __builtin_amdgcn_wave_barrier();
       int found = nk;
       if (lane == 0) {
         double c = 0.0;
-        for (int i = 0; i < nk; ++i) {
-          c += (double)s_sorted[wave][i];
-          if (c >= cdf_h) { found = i + 1; break; }
+        for (int q = 0; q < nk; ++q) {
+          c += (double)s_sorted[wave][q];
+          if (c >= cdf_h) { found = q + 1; break; }
         }
       }
-      n = __shfl(found, 0, kWave);
-    }
-
-    // Mark the first n sorted blocks, then OR in the gate.
+      const int n = __shfl(found, 0, kWave);
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) s_sel[wave][lane * KPL + j] = 0;
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
+      for (int j = 0; j < KPL; ++j)
+        if (lane * KPL + j < n) s_sel[r][~(uint32_t)key[j]] = 1;
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) chosen[i][j] = s_sel[4 * i + wave][lane * KPL + j] != 0;
+  }
+
+  // OR in the gate and write the ascending LUT by a prefix scan.
+  int cnt[RW], incl[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const bool simq = (qflags >> (4 * i + wave < rows ? 4 * i + wave : 0)) & 1ull;
+    cnt[i] = 0;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
-      const int pos = lane * KPL + j;
-      if (pos < n) s_sel[wave][~(uint32_t)key[j]] = 1;
+      chosen[i][j] = valid[j] && (!simq || chosen[i][j] || kgate[j]);
+      cnt[i] += chosen[i][j] ? 1 : 0;
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-
-    const bool simq = a.sim_q[row] != 0;
-    bool sel[KPL];
-    int cnt = 0;
+    incl[i] = cnt[i];
+  }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1)
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const int t = __shfl_up(incl[i], off, kWave);
+      if (lane >= off) incl[i] += t;
+    }
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    if (4 * i + wave >= rows) continue;
+    const int64_t row = bh * a.nq + qb0 + 4 * i + wave;
+    const int total = __shfl(incl[i], kWave - 1, kWave);
+    int32_t* lrow = a.lut + row * nk;
+    int pos = incl[i] - cnt[i];
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
       const int e = lane * KPL + j;
-      sel[j] = e < nk && (!simq || s_sel[wave][e] != 0 || simk[e] == 0);
-      cnt += sel[j] ? 1 : 0;
+      if (chosen[i][j]) lrow[pos++] = e;
+      if (valid[j] && e >= total) lrow[e] = -1;
+      if (valid[j] && a.bmap) a.bmap[row * nk + e] = chosen[i][j] ? 1 : 0;
     }
-    const int incl = wave_inclusive_scan(cnt);
-    const int total = __shfl(incl, kWave - 1, kWave);
-    if (active) {
-      int32_t* lrow = a.lut + row * nk;
-      int pos = incl - cnt;
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) {
-        const int e = lane * KPL + j;
-        if (sel[j]) lrow[pos++] = e;
-        if (e < nk && e >= total) lrow[e] = -1;
-        if (e < nk && a.bmap) a.bmap[row * nk + e] = sel[j] ? 1 : 0;
-      }
-      if (lane == 0) a.count[row] = total;
-    }
-    __builtin_amdgcn_wave_barrier();
+    if (lane == 0) a.count[row] = total;
   }
 }
 

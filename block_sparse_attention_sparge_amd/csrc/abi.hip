@@ -10,6 +10,8 @@
 
 #include <string>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -226,6 +228,10 @@ sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void*
       return fail(SPARGE_ERR_UNSUPPORTED, "ragged sequence (s_q=%d, s_k=%d) is not a multiple of 64", s_q, s_k);
     a.nqt = s_q / 64;
     a.nkb = s_k / 64;
+    // The kernel addresses a 64-row K or V block with 32-bit byte offsets.
+    const int64_t elem = 2, span = 64 * std::max(k_strides[2], v_strides[2]) * elem;
+    if (span >= (int64_t(1) << 31))
+      return fail(SPARGE_ERR_UNSUPPORTED, "a 64-row K/V block spans %lld bytes (limit 2^31)", (long long)span);
     if (!lut && lut_count) return fail(SPARGE_ERR_INVALID, "lut_count given without lut");
     return hip_status(launch_fmha_block(a, dt, o_dt, d, s), "sparse_fmha launch");
   }

@@ -17,6 +17,9 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -33,11 +36,14 @@ struct F16 {
   static __device__ __forceinline__ float hi(uint32_t w) {
     return (float)__builtin_bit_cast(half_t, (uint16_t)(w >> 16));
   }
-  // Pack two floats (round to nearest even) into one word, a in the low half.
+  // Pack two floats (round to nearest even) into one word, a in the low half
+  // (one v_cvt_pk_f16_f32).
   static __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    uint16_t ua = __builtin_bit_cast(uint16_t, (half_t)a);
-    uint16_t ub = __builtin_bit_cast(uint16_t, (half_t)b);
-    return (uint32_t)ua | ((uint32_t)ub << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v{a, b}), half2v));
+  }
+  // acc + lo(w) + hi(w) in fp32 (one v_dot2c_f32_f16 against (1, 1)).
+  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, w), half2v{(half_t)1.0f, (half_t)1.0f}, acc, false);
   }
 };
 
@@ -53,9 +59,11 @@ struct BF16 {
     return __builtin_bit_cast(float, w & 0xFFFF0000u);
   }
   static __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    uint16_t ua = __builtin_bit_cast(uint16_t, (bf16_t)a);
-    uint16_t ub = __builtin_bit_cast(uint16_t, (bf16_t)b);
-    return (uint32_t)ua | ((uint32_t)ub << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v{a, b}), bf16x2v));
+  }
+  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w), bf16x2v{(bf16_t)1.0f, (bf16_t)1.0f},
+                                           acc, false);
   }
 };
 

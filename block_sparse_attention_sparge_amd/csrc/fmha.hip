@@ -119,13 +119,32 @@ constexpr float kRescaleSlack = 8.0f;
 typedef short short4v __attribute__((ext_vector_type(4)));
 #define SPARGE_LDS __attribute__((address_space(3)))
 
-// 16 bytes from global memory into LDS at (wave-uniform base) + 16 * lane.
-__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+// 16 bytes from global memory at (wave-uniform base) + (per-lane 32-bit
+// offset) into LDS at (wave-uniform base) + 16 * lane.  The global base is a
+// scalar register pair, so moving to another block costs no vector ALU work.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t goff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(lds_base), "v"(gsrc)
+               : "s"(lds_base), "v"(goff), "s"(gbase)
                : "memory", "m0");
 }
+
+// max(x, x of lane l ^ 32).  v_permlane32_swap exchanges lanes 32..63 of its
+// first operand with lanes 0..31 of its second; with x in both, every lane
+// then holds its own value in one register and its partner's in the other.
+// Written in assembly because both outputs are needed (the s_nop covers the
+// VALU-write-to-permlane hazard).
+__device__ __forceinline__ float half_swap_max(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
+// Compile-time buffer index for the two-way unrolled block loop.
+template <int N>
+struct Buf {
+  static constexpr int value = N;
+};
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -204,28 +223,37 @@ void fmha_block_kernel(FmhaArgs a) {
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qf[kk]));
 
-  const T* kbase = reinterpret_cast<const T*>(a.k) + bb * a.ks[0] + hk * a.ks[1];
-  const T* vbase = reinterpret_cast<const T*>(a.v) + bb * a.vs[0] + hk * a.vs[1];
-  const int64_t ks2 = a.ks[2], vs2 = a.vs[2];
+  const char* kbase = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k) + bb * a.ks[0] + hk * a.ks[1]);
+  const char* vbase = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v) + bb * a.vs[0] + hk * a.vs[1]);
+  const int64_t kblk = 64 * a.ks[2] * (int64_t)sizeof(T), vblk = 64 * a.vs[2] * (int64_t)sizeof(T);
   const uint32_t sk_lds = (uint32_t)(uintptr_t)((SPARGE_LDS void*)sK);
   const uint32_t sv_lds = (uint32_t)(uintptr_t)((SPARGE_LDS void*)sV);
 
-  // Block kb into buffer buf: instruction J of the tile fills LDS granules
-  // 64J .. 64J+63; granule (row r, slot sl) holds global granule sl ^ swz(r).
+  // Direct-load instruction J of a tile fills LDS granules 64J .. 64J+63;
+  // granule (row r, slot sl) holds global granule sl ^ swz(r).  The byte
+  // offsets inside a block are the same for every block (the host keeps a
+  // block's span below 2^31 bytes).
+  uint32_t koff[NDMA], voff[NDMA];
+#pragma unroll
+  for (int j = 0; j < NDMA; ++j) {
+    const int gi = 64 * (wave * NDMA + j) + lane;
+    const int r = gi / G16, sl = gi % G16;
+    koff[j] = (uint32_t)((r * a.ks[2] + (sl ^ (r % G16)) * 8) * (int64_t)sizeof(T));
+    voff[j] = (uint32_t)((r * a.vs[2] + (sl ^ ((2 * r) % G16)) * 8) * (int64_t)sizeof(T));
+  }
   auto issue_block = [&](int kb, int buf) {
-    const T* kp = kbase + (int64_t)kb * 64 * ks2;
-    const T* vp = vbase + (int64_t)kb * 64 * vs2;
+    const char* kp = kbase + kb * kblk;
+    const char* vp = vbase + kb * vblk;
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
-      const int J = wave * NDMA + j;
-      const int gi = 64 * J + lane;
-      const int r = gi / G16, sl = gi % G16;
-      const uint32_t off = (uint32_t)((buf * TILE + J * 64 * 8) * sizeof(T));
-      dma16(kp + (int64_t)r * ks2 + (sl ^ (r % G16)) * 8, sk_lds + off);
-      dma16(vp + (int64_t)r * vs2 + (sl ^ ((2 * r) % G16)) * 8, sv_lds + off);
+      const uint32_t off = (uint32_t)((buf * TILE + (wave * NDMA + j) * 64 * 8) * sizeof(T));
+      dma16(kp, koff[j], sk_lds + off);
+      dma16(vp, voff[j], sv_lds + off);
     }
   };
-  auto kb_of = [&](int i) { return list ? list[beg + i] : beg + i; };
+  // LUT entries come through the scalar cache (the LUT is read-only here).
+  const __attribute__((address_space(4))) int32_t* clist = (const __attribute__((address_space(4))) int32_t*)list;
+  auto kb_of = [&](int i) { return list ? clist[beg + i] : beg + i; };
 
   floatx16 acc_o[NMD];
 #pragma unroll
@@ -249,26 +277,56 @@ void fmha_block_kernel(FmhaArgs a) {
   if (nloc > 1) issue_block(kb_of(1), 1);
   int kb_ahead = nloc > 2 ? kb_of(2) : 0;
 
-#pragma unroll 1
-  for (int it = 0; it < nloc; ++it) {
-    const int cur = it & 1;
+  // One 64-key block out of LDS buffer `cur` (a compile-time constant, so
+  // every LDS address is a fixed register plus an immediate offset).
+  auto step = [&](int it, auto cur_tag) {
+    constexpr int cur = decltype(cur_tag)::value;
     const T* kt = &sK[cur * TILE];
     const SPARGE_LDS T* vt = (const SPARGE_LDS T*)&sV[cur * TILE];
+
+    asm volatile("" ::"s"(kb_ahead));   // the LUT load of the previous step has landed
+    // LDS operands are requested early so that their latency overlaps the
+    // MFMAs: the 8 K reads and the first half of V^T before S^T, the second
+    // half of V^T right after it (16 reads in flight is as deep as the LDS
+    // wait counter can express).
+    u32x4 kf[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int g = (2 * kk + hl) ^ kswz;
+      kf[kk] = *reinterpret_cast<const u32x4*>(&kt[(krow * G16 + g) * 8]);
+    }
+    u32x4 vf[2][NMD];
+    auto read_vt = [&](int ks) {
+#pragma unroll
+      for (int md = 0; md < NMD; ++md) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int r = vrow0 + 16 * ks + 8 * c;
+          const int col = 32 * md + vcol0;
+          const int slot = (col >> 3) ^ ((2 * r) % G16);
+          const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (SPARGE_LDS short4v*)(vt + r * D + slot * 8 + (col & 7)));
+          const u32x2 w2 = __builtin_bit_cast(u32x2, x);
+          vf[ks][md][2 * c] = w2[0];
+          vf[ks][md][2 * c + 1] = w2[1];
+        }
+      }
+    };
+    read_vt(0);
+    __builtin_amdgcn_sched_barrier(0);
 
     // S^T (32 keys x 32 queries) = K Q^T.
     floatx16 s = floatx16{};
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const int g = (2 * kk + hl) ^ kswz;
-      const u32x4 af = *reinterpret_cast<const u32x4*>(&kt[(krow * G16 + g) * 8]);
-      s = mfma32<E>(af, qf[kk], s);
-    }
+    for (int kk = 0; kk < NKK; ++kk) s = mfma32<E>(kf[kk], qf[kk], s);
+    read_vt(1);
+    __builtin_amdgcn_sched_barrier(0);
 
     // Online softmax in base 2 over this lane's 16 scores.
     float rmax = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) rmax = fmaxf(rmax, s[r]);
-    rmax = fmaxf(rmax, __shfl_xor(rmax, 32, kWave));
+    rmax = half_swap_max(rmax);
     const float m_cand = rmax * c2;
     const bool need = m_cand > m_run + kRescaleSlack;
     if (__any(need)) {
@@ -279,52 +337,47 @@ void fmha_block_kernel(FmhaArgs a) {
 #pragma unroll
       for (int i = 0; i < NMD; ++i) acc_o[i] *= alpha;
     }
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -m_run));
-      s[r] = p;
-      psum += p;
-    }
-    l_run += psum;
-
-    // P^T fragments: k-step ks uses registers 8ks .. 8ks+7.
+    // P^T fragments (k-step ks uses registers 8ks .. 8ks+7), rounded to the
+    // input type; the row sum adds the rounded values, the ones PV uses.
     u32x4 pf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) pf[ks][w] = E::pack2(s[8 * ks + 2 * w], s[8 * ks + 2 * w + 1]);
+      for (int w = 0; w < 4; ++w) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w], c2, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w + 1], c2, -m_run));
+        pf[ks][w] = E::pack2(p0, p1);
+        l_run = E::sum2(pf[ks][w], l_run);
+      }
     }
 
     // O^T += V^T P^T over this wave's 32 keys.
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int md = 0; md < NMD; ++md) {
-        u32x4 af;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int r = vrow0 + 16 * ks + 8 * c;
-          const int col = 32 * md + vcol0;
-          const int slot = (col >> 3) ^ ((2 * r) % G16);
-          const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (SPARGE_LDS short4v*)(vt + r * D + slot * 8 + (col & 7)));
-          const u32x2 w2 = __builtin_bit_cast(u32x2, x);
-          af[2 * c] = w2[0];
-          af[2 * c + 1] = w2[1];
-        }
-        acc_o[md] = mfma32<E>(af, pf[ks], acc_o[md]);
-      }
+      for (int md = 0; md < NMD; ++md) acc_o[md] = mfma32<E>(vf[ks][md], pf[ks], acc_o[md]);
     }
+
+    // The LUT entry of block it+3 is requested only now, after this block's
+    // last LDS wait: scalar loads share the LDS wait counter but may return
+    // out of order, so one in flight would turn every partial LDS wait above
+    // into a full one.  The next step consumes it first thing.
+    __builtin_amdgcn_sched_barrier(0);
+    const int kb_next = it + 3 < nloc ? kb_of(it + 3) : 0;
 
     // Block it+1 must have landed before the barrier hands the buffers over;
     // then the buffer just consumed receives block it+2.
     wait_dma();
     __syncthreads();
-    if (it + 2 < nloc) {
-      issue_block(kb_ahead, cur);
-      if (it + 3 < nloc) kb_ahead = kb_of(it + 3);
-    }
+    if (it + 2 < nloc) issue_block(kb_ahead, cur);
+    kb_ahead = kb_next;
+  };
+
+#pragma unroll 1
+  for (int it = 0; it < nloc; it += 2) {
+    step(it, Buf<0>{});
+    if (it + 1 == nloc) break;
+    step(it + 1, Buf<1>{});
   }
 
   // Merge the two key halves: waves kh = 1 publish (m, l, O^T); waves kh = 0 combine.

@@ -143,6 +143,7 @@ def _fmha(lib, **kw):
     (dict(k=FAKE + 8), ops.SPARGE_ERR_INVALID),
     (dict(lut=None, cnt=FAKE), ops.SPARGE_ERR_INVALID),
     (dict(scale=float("nan")), ops.SPARGE_ERR_INVALID),
+    (dict(vs=_s3(2 * 512 * 128, 512 * 128, 1 << 24)), ops.SPARGE_ERR_UNSUPPORTED),   # 64 rows span 2^31 bytes
     # token-list mode
     (dict(bq=1, bk=1, lut=None, cnt=None), ops.SPARGE_ERR_INVALID),
     (dict(bq=1, bk=1, cnt=FAKE, lh=2), ops.SPARGE_ERR_INVALID),

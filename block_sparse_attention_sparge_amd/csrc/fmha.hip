@@ -6,22 +6,21 @@
 // over the keys of the listed blocks; O = sum_j softmax_j v_j and the
 // natural-log LSE; a list with no block writes O = 0 and LSE = -inf.
 //
-// Block kernel (blk_q = blk_k = 64), one workgroup of two wavefronts per
-// (Q-tile, head, batch, split).  Each wavefront owns 32 query rows and works
-// in the transposed orientation S^T = K Q^T, O^T += V^T P^T on the
-// 32x32x16 fp16/bf16 MFMA:
+// Block kernel (blk_q = blk_k = 64), one workgroup of four wavefronts per
+// (Q-tile, head, batch, split); each wavefront owns 32 query rows and 32 keys
+// of every block and works in the transposed orientation S^T = K Q^T,
+// O^T += V^T P^T on the 32x32x16 fp16/bf16 MFMA:
 //   * Q^T stays in registers as the B operand for the whole row;
-//   * the K block is staged row-major in LDS (A operand of S^T, 16-byte
-//     reads); the V block is staged transposed (V^T, A operand of O^T) with
-//     its key order permuted so that each lane's 8 keys are one 16-byte read;
+//   * K and V blocks arrive by direct global->LDS loads into double buffers;
+//     K is read row-major (A operand of S^T), V through the transposing LDS
+//     read (A operand of O^T);
 //   * the S^T accumulator already has the layout of the P^T B operand, so P
 //     goes from softmax to the PV MFMA without leaving registers, and every
 //     row reduction is in-lane plus one exchange with the partner half-wave;
 //   * the softmax runs in base 2 with the scale folded in once (aiter 4919
 //     page: one FMA per score, exp2), and the row sum is finished only at the
 //     end (one reciprocal per row);
-//   * the next block's K/V loads are issued into registers before the current
-//     block's MFMAs, so global latency overlaps compute;
+//   * the two key halves of a tile are merged at the end with the LSE rule;
 //   * workgroups are renumbered so that consecutive rows of one head land on
 //     one XCD and share its L2 (aiter 4919 page: workgroups round-robin over
 //     the 8 XCDs by linear id).
@@ -107,10 +106,13 @@ __device__ __forceinline__ void store4(void* base, int64_t off, float x0, float 
 //   * K is stored row-major with the 16-byte granules of row r XOR-swizzled
 //     by r mod 16, so S^T operand reads of 32 consecutive rows hit distinct
 //     banks.
-//   * V is stored row-major with granules XOR-swizzled by 2r, and the V^T
-//     operand of O^T += V^T P^T is read with the gfx950 transposing LDS read
-//     (ds_read_b64_tr_b16): within each 16-lane group, lane j receives element
-//     j%4 of the 4-element chunks addressed by lanes j/4 + 4t, t = 0..3.
+//   * V is stored row-major with granules XOR-swizzled by (G16/4) r (4r for
+//     d = 128, 2r for d = 64), and the V^T operand of O^T += V^T P^T is read
+//     with the gfx950 transposing LDS read (ds_read_b64_tr_b16): within each
+//     16-lane group, lane j receives element j%4 of the 4-element chunks
+//     addressed by lanes j/4 + 4t, t = 0..3.  These reads are served 32 lanes
+//     per clock; the swizzle puts the four rows one such half-wave touches on
+//     four different sets of banks.
 // The running maximum is only moved when a row's new maximum exceeds it by
 // more than 2^8 (base-2 units), so most blocks skip rescaling O; the exported
 // LSE and O are exact for any reference maximum, and P stays below 2^8.
@@ -157,6 +159,7 @@ void fmha_block_kernel(FmhaArgs a) {
   constexpr int NMD = D / 32;                // M-tiles of O^T
   constexpr int TILE = 64 * D;               // elements per K or V buffer
   constexpr int NDMA = 64 * G16 / 256;       // direct loads per thread per tile
+  constexpr int VSW = G16 / 4;               // V row r's granules are XOR-swizzled by VSW * r
   __shared__ __attribute__((aligned(16))) T sK[2 * TILE];
   __shared__ __attribute__((aligned(16))) T sV[2 * TILE];
 
@@ -239,7 +242,7 @@ void fmha_block_kernel(FmhaArgs a) {
     const int gi = 64 * (wave * NDMA + j) + lane;
     const int r = gi / G16, sl = gi % G16;
     koff[j] = (uint32_t)((r * a.ks[2] + (sl ^ (r % G16)) * 8) * (int64_t)sizeof(T));
-    voff[j] = (uint32_t)((r * a.vs[2] + (sl ^ ((2 * r) % G16)) * 8) * (int64_t)sizeof(T));
+    voff[j] = (uint32_t)((r * a.vs[2] + (sl ^ ((VSW * r) % G16)) * 8) * (int64_t)sizeof(T));
   }
   auto issue_block = [&](int kb, int buf) {
     const char* kp = kbase + kb * kblk;
@@ -303,7 +306,7 @@ void fmha_block_kernel(FmhaArgs a) {
         for (int c = 0; c < 2; ++c) {
           const int r = vrow0 + 16 * ks + 8 * c;
           const int col = 32 * md + vcol0;
-          const int slot = (col >> 3) ^ ((2 * r) % G16);
+          const int slot = (col >> 3) ^ ((VSW * r) % G16);
           const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (SPARGE_LDS short4v*)(vt + r * D + slot * 8 + (col & 7)));
           const u32x2 w2 = __builtin_bit_cast(u32x2, x);

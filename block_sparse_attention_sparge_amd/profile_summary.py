@@ -43,10 +43,11 @@ def source_sha256(path: str = FMHA_SOURCE) -> str:
 
 
 def _one(dirpath: str, pattern: str) -> str:
-    hits = sorted(glob.glob(os.path.join(dirpath, "**", pattern), recursive=True))
+    """The most recently written file matching `pattern` under `dirpath`."""
+    hits = glob.glob(os.path.join(dirpath, "**", pattern), recursive=True)
     if not hits:
         raise SystemExit(f"no {pattern} under {dirpath}")
-    return hits[0]
+    return max(hits, key=os.path.getmtime)
 
 
 def arm_slices(steps: int, warmup: int):

@@ -45,6 +45,10 @@ struct F16 {
   static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, w), half2v{(half_t)1.0f, (half_t)1.0f}, acc, false);
   }
+  // acc + lo(x) lo(y) + hi(x) hi(y), products exact, in fp32.
+  static __device__ __forceinline__ float dot2(uint32_t x, uint32_t y, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, x), __builtin_bit_cast(half2v, y), acc, false);
+  }
 };
 
 struct BF16 {
@@ -64,6 +68,9 @@ struct BF16 {
   static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w), bf16x2v{(bf16_t)1.0f, (bf16_t)1.0f},
                                            acc, false);
+  }
+  static __device__ __forceinline__ float dot2(uint32_t x, uint32_t y, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, x), __builtin_bit_cast(bf16x2v, y), acc, false);
   }
 };
 

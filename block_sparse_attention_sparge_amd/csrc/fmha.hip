@@ -432,8 +432,7 @@ __global__ __launch_bounds__(256) void fmha_tokens_kernel(FmhaArgs a) {
   constexpr int CPR = D / 8;         // 16-byte chunks per row
   constexpr int NS = 256 / CPR;      // key subsets (PV phase)
   constexpr int KPS = 64 / NS;       // keys per subset per chunk
-  __shared__ float s_q[R][D];
-  __shared__ int s_tok[64];
+  __shared__ uint32_t s_q[R][D / 2];   // query rows as packed input-type pairs
   __shared__ float s_p[R][64];
   __shared__ float s_alpha[R];
   __shared__ float s_ml[R][2];
@@ -461,16 +460,16 @@ __global__ __launch_bounds__(256) void fmha_tokens_kernel(FmhaArgs a) {
   // Query rows r = g * sq + sp for query head hk*ratio + g, position sp; the
   // template row count R may exceed the real one (rows), whose rows stay zero.
   const int rows = a.ratio * sq;
-  for (int i = tid; i < R * D; i += 256) {
-    const int r = i / D, d = i % D;
-    float x = 0.f;
+  for (int i = tid; i < R * D / 2; i += 256) {
+    const int r = i / (D / 2), d2 = i % (D / 2);
+    uint32_t x = 0u;
     if (r < rows) {
       const int g = r / sq, sp = r % sq;
       const T* qp = reinterpret_cast<const T*>(a.q) + bb * a.qs[0] + (int64_t)(hk * a.ratio + g) * a.qs[1] +
-                    (int64_t)sp * a.qs[2] + d;
-      x = E::to_f(*qp);
+                    (int64_t)sp * a.qs[2] + 2 * d2;
+      x = *reinterpret_cast<const uint32_t*>(qp);
     }
-    s_q[r][d] = x;
+    s_q[r][d2] = x;
   }
   float m_run[2], l_run[2];    // rows wave and wave + 4 (R <= 8)
 #pragma unroll
@@ -487,24 +486,38 @@ __global__ __launch_bounds__(256) void fmha_tokens_kernel(FmhaArgs a) {
   const int qj = tid >> 2, qq = tid & 3;        // QK phase: key slot, quarter
   const int pc = tid % CPR, ps = tid / CPR;     // PV phase: d chunk, key subset
 
-#pragma unroll 1
-  for (int pos0 = beg; pos0 < end; pos0 += 64) {
-    __syncthreads();
-    if (tid < 64) s_tok[tid] = pos0 + tid < end ? list[pos0 + tid] : -1;
-    __syncthreads();
-
-    // Issue the K and V gathers of this chunk together.
-    const int tk = s_tok[qj];
-    u32x4 kr[QW / 8];
+  // Pipeline over 64-token chunks: the token indices of chunk c+2 and the K/V
+  // rows of chunk c+1 are in flight while chunk c is scored and accumulated.
+  // Each thread reads only the list entries it gathers: key slot qj for K and
+  // key slots ps + NS*i for V.
+  auto tok = [&](int pos) { return pos < end ? list[pos] : -1; };
+  auto load_chunk = [&](int tk, const int (&tv)[KPS], u32x4 (&kr)[QW / 8], u32x4 (&vr)[KPS]) {
 #pragma unroll
     for (int i = 0; i < QW / 8; ++i)
       kr[i] = tk >= 0 ? load16(kbase + (int64_t)tk * a.ks[2] + qq * QW + 8 * i) : u32x4{0u, 0u, 0u, 0u};
-    u32x4 vr[KPS];
 #pragma unroll
-    for (int i = 0; i < KPS; ++i) {
-      const int tv = s_tok[ps + NS * i];
-      vr[i] = tv >= 0 ? load16(vbase + (int64_t)tv * a.vs[2] + pc * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < KPS; ++i)
+      vr[i] = tv[i] >= 0 ? load16(vbase + (int64_t)tv[i] * a.vs[2] + pc * 8) : u32x4{0u, 0u, 0u, 0u};
+  };
+  int tk_cur = tok(beg + qj), tv_cur[KPS];
+#pragma unroll
+  for (int i = 0; i < KPS; ++i) tv_cur[i] = tok(beg + ps + NS * i);
+  int tk_nxt = tok(beg + 64 + qj), tv_nxt[KPS];
+#pragma unroll
+  for (int i = 0; i < KPS; ++i) tv_nxt[i] = tok(beg + 64 + ps + NS * i);
+  u32x4 kr[QW / 8], vr[KPS];
+  load_chunk(tk_cur, tv_cur, kr, vr);
+  __syncthreads();                   // s_q is complete
+
+#pragma unroll 1
+  for (int pos0 = beg; pos0 < end; pos0 += 64) {
+    // Next chunk's rows and the chunk after's indices.
+    u32x4 kn[QW / 8], vn[KPS];
+    load_chunk(pos0 + 64 < end ? tk_nxt : -1, tv_nxt, kn, vn);
+    const int tk_far = tok(pos0 + 128 + qj);
+    int tv_far[KPS];
+#pragma unroll
+    for (int i = 0; i < KPS; ++i) tv_far[i] = tok(pos0 + 128 + ps + NS * i);
 
     // Scores: each thread dots a quarter of one key with every query row.
     float part[R];
@@ -514,10 +527,9 @@ __global__ __launch_bounds__(256) void fmha_tokens_kernel(FmhaArgs a) {
     for (int i = 0; i < QW / 8; ++i) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float x0 = E::lo(kr[i][w]), x1 = E::hi(kr[i][w]);
-        const int d = qq * QW + 8 * i + 2 * w;
+        const int d2 = (qq * QW + 8 * i + 2 * w) / 2;
 #pragma unroll
-        for (int r = 0; r < R; ++r) part[r] = fmaf(s_q[r][d + 1], x1, fmaf(s_q[r][d], x0, part[r]));
+        for (int r = 0; r < R; ++r) part[r] = E::dot2(s_q[r][d2], kr[i][w], part[r]);
       }
     }
 #pragma unroll
@@ -525,9 +537,10 @@ __global__ __launch_bounds__(256) void fmha_tokens_kernel(FmhaArgs a) {
       part[r] += __shfl_xor(part[r], 1, kWave);
       part[r] += __shfl_xor(part[r], 2, kWave);
     }
+    __syncthreads();                 // the previous chunk's PV has read s_p
     if (qq == 0) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) s_p[r][qj] = tk >= 0 ? part[r] * c2 : -INFINITY;
+      for (int r = 0; r < R; ++r) s_p[r][qj] = tk_cur >= 0 ? part[r] * c2 : -INFINITY;
     }
     __syncthreads();
 
@@ -578,6 +591,16 @@ __global__ __launch_bounds__(256) void fmha_tokens_kernel(FmhaArgs a) {
         for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(p, v[e], acc[r][e]);
       }
     }
+
+#pragma unroll
+    for (int i = 0; i < QW / 8; ++i) kr[i] = kn[i];
+#pragma unroll
+    for (int i = 0; i < KPS; ++i) {
+      vr[i] = vn[i];
+      tv_nxt[i] = tv_far[i];
+    }
+    tk_cur = tk_nxt;
+    tk_nxt = tk_far;
   }
 
   // Publish each row's (max, sum), then reduce the PV partials over key subsets.

@@ -75,9 +75,9 @@ __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
     float n2 = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) n2 = fmaf(x[i], x[i], n2);
-#pragma unroll
-    for (int m = 1; m < CH; m <<= 1) n2 += __shfl_xor(n2, m, kWave);
-    const float inv = n2 > 0.f ? 1.0f / sqrtf(n2) : 0.f;
+    if constexpr (CH == 16) n2 = row16_sum(n2);
+    else n2 = row8_sum(n2);
+    const float inv = n2 > 0.f ? __builtin_amdgcn_rsqf(n2) : 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       sx[i] += x[i];
@@ -96,8 +96,8 @@ __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
   float dot = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) dot = fmaf(sh[i], sh[i], dot);
-#pragma unroll
-  for (int m = 1; m < CH; m <<= 1) dot += __shfl_xor(dot, m, kWave);
+  if constexpr (CH == 16) dot = row16_sum(dot);
+  else dot = row8_sum(dot);
 
   float* mean = (is_k ? a.k_mean : a.q_mean) + (bh * nb + blk) * D;
   if (t0 == 0) {

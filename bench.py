@@ -57,6 +57,22 @@ def time_arm(fn, steps, warmup, torch):
     return wall, per
 
 
+def time_cold(fn, steps, torch, flush):
+    """Per-call HIP-event times of fn() with L2 and MALL flushed first: a
+    512 MiB write precedes every call, outside the timed events."""
+    per = []
+    for _ in range(steps):
+        flush.fill_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1))
+    return per
+
+
 def median(x):
     s = sorted(x)
     n = len(s)
@@ -136,11 +152,16 @@ def extras(ops, synth, torch, steps, warmup):
     def comb():
         ops.attn_combine(parts, lses, o=oc, lse=lc)
 
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     _, tp = time_arm(two_pass, steps, warmup, torch)
     _, cm = time_arm(comb, steps, warmup, torch)
+    tp_cold = time_cold(two_pass, steps, torch, flush)
+    cm_cold = time_cold(comb, steps, torch, flush)
     comb_bytes = parts.numel() * 4 + lses.numel() * 4 + oc.numel() * 2 + lc.numel() * 4
     out["two_pass_combine"] = dict(workload="b1 h16 s_q1024 s_k32768 d128 bf16", ms=median(tp),
-                                   combine_ms=median(cm), combine_gbs=comb_bytes / median(cm) / 1e6)
+                                   combine_ms=median(cm), combine_gbs=comb_bytes / median(cm) / 1e6,
+                                   cold_ms=median(tp_cold), cold_combine_ms=median(cm_cold),
+                                   cold_combine_gbs=comb_bytes / median(cm_cold) / 1e6)
     del c, oa, ob, parts, lses, oc, lc
     # Combine on headline-shaped fp32 partials: 2 x [2, 32, 16384, 128].
     parts = torch.randn(2, B, H, S, D, device=dev)
@@ -167,10 +188,14 @@ def extras(ops, synth, torch, steps, warmup):
         ops.attn_combine(op, lp, o=od, lse=ld)
 
     _, dm = time_arm(decode, steps, warmup, torch)
+    dm_cold = time_cold(decode, steps, torch, flush)
     gathered = 64 * 8 * 2048 * 128 * 2 * 2
     out["decode_gqa"] = dict(workload="b64 h_q32 h_kv8 s_k32768 d128 bf16, 2048 listed keys, 8 splits",
                              ms=median(dm), gathered_gbs=gathered / median(dm) / 1e6,
-                             frac_hbm=gathered / median(dm) / 1e6 / PEAK_HBM_GBS)
+                             frac_hbm=gathered / median(dm) / 1e6 / PEAK_HBM_GBS,
+                             cold_ms=median(dm_cold), cold_gathered_gbs=gathered / median(dm_cold) / 1e6,
+                             cold_frac_hbm=gathered / median(dm_cold) / 1e6 / PEAK_HBM_GBS)
+    del flush
     return out
 
 

@@ -187,8 +187,11 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
   const int groups = (a.nq + kSelRows - 1) / kSelRows;
-  const int64_t bh = blockIdx.x / groups;
-  const int qb0 = (int)(blockIdx.x % groups) * kSelRows;
+  // The groups of one (b, h) share its K means: keep them on one XCD's L2.
+  const int64_t lin = xcd_remap(blockIdx.x, gridDim.x);
+  if (lin >= (int64_t)a.b * a.h * groups) return;
+  const int64_t bh = lin / groups;
+  const int qb0 = (int)(lin % groups) * kSelRows;
   const int rows = min(kSelRows, a.nq - qb0);
   const int hh = (int)(bh % a.h);
   const int nk = a.nk;
@@ -462,7 +465,7 @@ hipError_t launch_pool_sim(const PoolArgs& a, sparge_dtype dt, int d, hipStream_
 template <int D>
 static hipError_t launch_select_d(const SelectArgs& a, hipStream_t st) {
   const int groups = (a.nq + kSelRows - 1) / kSelRows;
-  const dim3 grid((unsigned)((int64_t)a.b * a.h * groups));
+  const dim3 grid((unsigned)(((int64_t)a.b * a.h * groups + 7) / 8 * 8));
   const int nk = a.nk;
   if (nk <= 64) hipLaunchKernelGGL((score_select_kernel<D, 1>), grid, dim3(256), 0, st, a);
   else if (nk <= 128) hipLaunchKernelGGL((score_select_kernel<D, 2>), grid, dim3(256), 0, st, a);

@@ -86,6 +86,13 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin by linear id; give every
+// XCD a contiguous range of logical ids (grid is a multiple of 8).
+__device__ __forceinline__ int64_t xcd_remap(int64_t pid, int64_t grid) {
+  const int64_t per = grid >> 3;
+  return (pid & 7) * per + (pid >> 3);
+}
+
 // Sum over each group of 8 lanes (aligned), left in every lane of the group.
 __device__ __forceinline__ float row8_sum(float x) {
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));

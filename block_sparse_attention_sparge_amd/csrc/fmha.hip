@@ -38,13 +38,6 @@ namespace sparge {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Workgroups are dispatched to the 8 XCDs round-robin by linear id; give every
-// XCD a contiguous range of logical ids (grid is a multiple of 8).
-__device__ __forceinline__ int64_t xcd_remap(int64_t pid, int64_t grid) {
-  const int64_t per = grid >> 3;
-  return (pid & 7) * per + (pid >> 3);
-}
-
 // Index of the first negative entry of a LUT row (or its length), by one wave.
 __device__ __forceinline__ int first_negative(const int32_t* row, int len, int lane) {
   int first = len;

@@ -14,6 +14,9 @@ FMHA), and the dense arm 2 + max(5, steps // 2) times; dispatches are assigned
 to arms in that order.  The traffic report records the SHA-256 of the FMHA
 source so that bench.py stops quoting it once the kernel changes.
 
+A third report, bytes, gives copy-calibrated HBM bytes per dispatch for
+every kernel of the library in two counter runs, grouped by kernel and grid.
+
 Usage:
   python -m block_sparse_attention_sparge_amd.profile_summary trace DIR \
       --steps K --warmup W --command "..." > profiles/x.md
@@ -149,6 +152,37 @@ def read_traffic(path: str, arm: str):
     return None
 
 
+def _short(name: str) -> str:
+    """Kernel name without the namespace and argument list."""
+    base = name.split("(")[0]
+    return base.replace("void ", "").replace("sparge::", "")
+
+
+def bytes_report(fetch: str, write: str, copy_fetch: str, copy_write: str, copy_bytes: int,
+                 command: str) -> str:
+    """Copy-calibrated HBM bytes per dispatch for every kernel in the runs,
+    grouped by kernel and grid size."""
+    cf, cw = _copy_kib(copy_fetch), _copy_kib(copy_write)
+    fs, ws = copy_bytes / 1024.0 / cf, copy_bytes / 1024.0 / cw
+    groups = {}
+    for path, key in ((fetch, "fetch"), (write, "write")):
+        for r in csv.DictReader(open(_one(path, "*counter_collection.csv"))):
+            if "sparge::" not in r["Kernel_Name"]:
+                continue
+            g = groups.setdefault((_short(r["Kernel_Name"]), int(r["Grid_Size"])), {"fetch": [], "write": []})
+            g[key].append(float(r["Counter_Value"]))
+    out = ["# HBM bytes per dispatch of the block-map, combine and decode kernels", "",
+           "Commands:", "", "```", command, "```", "",
+           f"Copy calibration: a device-to-device copy of {copy_bytes} bytes reads FETCH_SIZE {cf:.0f} KiB and "
+           f"WRITE_SIZE {cw:.0f} KiB per dispatch, so the scale factors are {fs:.3f} (fetch) and {ws:.3f} (write).",
+           "", "| kernel | grid (threads) | dispatches | read MB | written MB |", "|---|---|---|---|---|"]
+    for (name, grid), g in sorted(groups.items()):
+        rd = statistics.median(g["fetch"]) * fs * 1024 / 1e6 if g["fetch"] else float("nan")
+        wr = statistics.median(g["write"]) * ws * 1024 / 1e6 if g["write"] else float("nan")
+        out.append(f"| `{name}` | {grid} | {max(len(g['fetch']), len(g['write']))} | {rd:.2f} | {wr:.2f} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -167,9 +201,15 @@ def main(argv=None) -> int:
     f.add_argument("--steps", type=int, required=True)
     f.add_argument("--warmup", type=int, required=True)
     f.add_argument("--command", required=True)
+    bt = sub.add_parser("bytes")
+    for opt in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--command"):
+        bt.add_argument(opt, required=True)
+    bt.add_argument("--copy-bytes", type=int, required=True)
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         sys.stdout.write(trace_report(a.dir, a.steps, a.warmup, a.command))
+    elif a.cmd == "bytes":
+        sys.stdout.write(bytes_report(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes, a.command))
     else:
         sys.stdout.write(traffic_report(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes,
                                         a.steps, a.warmup, a.command))

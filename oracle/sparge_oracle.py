@@ -88,17 +88,43 @@ def pool_and_gate(x: np.ndarray, blk: int, simthreshd1: float):
     return means, sims, flags
 
 
+def smooth_keys(k: np.ndarray) -> np.ndarray:
+    """K with its mean over the sequence removed: k - km, km = mean_s k.
+
+    CK page, "Status vs Upstream", not-yet-ported list: K smoothing, the
+    pre-pool step k -= km.  Reading R22: km is the plain mean over all s_k
+    positions of the (b, h) slice, and smoothing feeds only the block map (the
+    pooled means and the K similarity gate); attention keeps the original K,
+    so its LSE stays the exact log-sum-exp of the true scores.
+    """
+    k = np.asarray(k, np.float64)
+    return k - k.mean(axis=-2, keepdims=True)
+
+
+def causal_valid(nq: int, nk: int) -> np.ndarray:
+    """valid[qb, kb]: K block kb holds a key at or before some query of Q-tile qb.
+
+    CK page, not-yet-ported list: the is_causal mask in the pooled score.
+    Reading R23 (blk_q = blk_k, s_q = s_k): block kb is entirely in the future
+    of tile qb exactly when kb > qb.
+    """
+    return np.arange(nk)[None, :] <= np.arange(nq)[:, None]
+
+
 def pooled_scores(qbar: np.ndarray, kbar: np.ndarray, sim_k: np.ndarray,
-                  scale: float) -> np.ndarray:
+                  scale: float, causal: bool = False) -> np.ndarray:
     """S[qb, kb] = scale * <qbar[qb], kbar[kb]>, and -inf on non-similar K blocks.
 
     CK page, "Status vs Upstream": pooled QK.  Reading R4: the attention
     softmax scale (1/sqrt(d) by default).  Reading R5: a K block that fails the
     similarity gate is kept out of the pooled softmax (its column is -inf) and
-    is forced on later, in `select_row`.
+    is forced on later, in `select_row`.  With `causal`, blocks in the future
+    of the tile are -inf as well (reading R23).
     """
     s = float(scale) * (np.asarray(qbar, np.float64) @ np.asarray(kbar, np.float64).T)
     s[:, ~np.asarray(sim_k, bool)] = NEG_INF
+    if causal:
+        s[~causal_valid(s.shape[0], s.shape[1])] = NEG_INF
     return s
 
 
@@ -160,7 +186,8 @@ def cdf_count(prob_row: np.ndarray, order: np.ndarray, cdfthreshd: float) -> int
 
 
 def select_row(prob_row: np.ndarray, sim_q_flag: bool, sim_k: np.ndarray,
-               topk: float, cdfthreshd: Optional[float]) -> np.ndarray:
+               topk: float, cdfthreshd: Optional[float],
+               valid: Optional[np.ndarray] = None, attention_sink: bool = False) -> np.ndarray:
     """Selected K blocks of one Q-tile row, ascending.
 
     * If the Q block fails the similarity gate, every K block is selected
@@ -170,19 +197,34 @@ def select_row(prob_row: np.ndarray, sim_q_flag: bool, sim_k: np.ndarray,
       when both are set).
     * Then add every K block that failed the gate (reading R9: these are
       added after the count, so a row may hold more than n blocks).
+    * `valid` (causal mode, reading R23) limits every one of these steps to the
+      blocks at or before the tile: "every block" means every valid block, n is
+      clamped to the number of valid blocks, and forced blocks must be valid.
+      Invalid blocks have probability 0 and a larger index than any valid
+      block, so the first n of the order are valid.
+    * `attention_sink` (CK page, not-yet-ported list: column 0 forced on)
+      adds block 0 to every row.
     """
     nk = prob_row.shape[0]
+    if valid is None:
+        valid = np.ones(nk, dtype=bool)
+    valid = np.asarray(valid, bool)
+    n_valid = int(valid.sum())
     if not sim_q_flag:
-        return np.arange(nk, dtype=np.int64)
-    order = selection_order(prob_row)
-    if topk is not None and float(np.float32(topk)) > 0.0:
-        n = topk_count(topk, nk)
+        chosen = set(int(kb) for kb in np.nonzero(valid)[0])
     else:
-        if cdfthreshd is None:
-            raise ValueError("either topk > 0 or cdfthreshd must be given")
-        n = cdf_count(prob_row, order, cdfthreshd)
-    chosen = set(int(kb) for kb in order[:n])
-    chosen |= set(int(kb) for kb in np.nonzero(~np.asarray(sim_k, bool))[0])
+        order = selection_order(prob_row)
+        if topk is not None and float(np.float32(topk)) > 0.0:
+            n = topk_count(topk, nk)
+        else:
+            if cdfthreshd is None:
+                raise ValueError("either topk > 0 or cdfthreshd must be given")
+            n = cdf_count(prob_row, order, cdfthreshd)
+        n = min(n, n_valid)
+        chosen = set(int(kb) for kb in order[:n])
+        chosen |= set(int(kb) for kb in np.nonzero(~np.asarray(sim_k, bool) & valid)[0])
+    if attention_sink:
+        chosen.add(0)
     return np.array(sorted(chosen), dtype=np.int64)
 
 
@@ -202,7 +244,8 @@ def lut_from_selection(rows: Sequence[np.ndarray], nk: int):
 
 
 def select_from_probs(prob: np.ndarray, sim_q: np.ndarray, sim_k: np.ndarray,
-                      topk: Sequence[float], cdfthreshd: Optional[Sequence[float]]):
+                      topk: Sequence[float], cdfthreshd: Optional[Sequence[float]],
+                      causal: bool = False, attention_sink: bool = False):
     """Selection steps applied to given pooled probabilities and gate flags.
 
     prob [b, h, nq, nk]; sim_q [b, h, nq]; sim_k [b, h, nk]; topk / cdfthreshd
@@ -218,8 +261,10 @@ def select_from_probs(prob: np.ndarray, sim_q: np.ndarray, sim_k: np.ndarray,
     for ib in range(b):
         for ih in range(h):
             cdf = None if cdfthreshd is None else cdfthreshd[ih]
+            valid = causal_valid(nq, nk) if causal else np.ones((nq, nk), dtype=bool)
             rows = [select_row(prob[ib, ih, qb], bool(sim_q[ib, ih, qb]),
-                               sim_k[ib, ih], topk[ih], cdf) for qb in range(nq)]
+                               sim_k[ib, ih], topk[ih], cdf, valid[qb], attention_sink)
+                    for qb in range(nq)]
             l, c, m = lut_from_selection(rows, nk)
             lut[ib, ih], count[ib, ih], bitmap[ib, ih] = l, c, m
     return lut, count, bitmap
@@ -227,14 +272,23 @@ def select_from_probs(prob: np.ndarray, sim_q: np.ndarray, sim_k: np.ndarray,
 
 def block_map(q: np.ndarray, k: np.ndarray, topk: Sequence[float],
               simthreshd1: Sequence[float], cdfthreshd: Optional[Sequence[float]] = None,
-              blk_q: int = 64, blk_k: int = 64, scale: Optional[float] = None) -> dict:
+              blk_q: int = 64, blk_k: int = 64, scale: Optional[float] = None,
+              smooth_k: bool = False, causal: bool = False,
+              attention_sink: bool = False) -> dict:
     """Whole stage 1 for q [b, h, s_q, d] and k [b, h, s_k, d].
 
-    Returns a dict with q_mean, k_mean, sim_q_val, sim_k_val, sim_q, sim_k,
-    scores, prob, lut, count, bitmap.
+    `smooth_k` pools and gates K after `smooth_keys`; `causal` applies the
+    causal block mask (requires s_q = s_k and blk_q = blk_k); `attention_sink`
+    forces block 0 in every row.  Returns a dict with q_mean, k_mean (of the
+    smoothed K when smoothing), sim_q_val, sim_k_val, sim_q, sim_k, scores,
+    prob, lut, count, bitmap.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
+    if causal and (q.shape[2] != k.shape[2] or blk_q != blk_k):
+        raise ValueError("causal block map needs s_q = s_k and blk_q = blk_k")
+    if smooth_k:
+        k = smooth_keys(k)
     b, h, s_q, d = q.shape
     s_k = k.shape[2]
     if scale is None:
@@ -254,9 +308,10 @@ def block_map(q: np.ndarray, k: np.ndarray, topk: Sequence[float],
             k_mean[ib, ih], sim_k_val[ib, ih], sim_k[ib, ih] = pool_and_gate(
                 k[ib, ih], blk_k, simthreshd1[ih])
             scores[ib, ih] = pooled_scores(q_mean[ib, ih], k_mean[ib, ih],
-                                           sim_k[ib, ih], scale)
+                                           sim_k[ib, ih], scale, causal)
     prob = row_softmax(scores)
-    lut, count, bitmap = select_from_probs(prob, sim_q, sim_k, topk, cdfthreshd)
+    lut, count, bitmap = select_from_probs(prob, sim_q, sim_k, topk, cdfthreshd,
+                                           causal, attention_sink)
     return dict(q_mean=q_mean, k_mean=k_mean, sim_q_val=sim_q_val, sim_k_val=sim_k_val,
                sim_q=sim_q, sim_k=sim_k, scores=scores, prob=prob,
                lut=lut, count=count, bitmap=bitmap)
@@ -266,37 +321,47 @@ def block_map(q: np.ndarray, k: np.ndarray, topk: Sequence[float],
 # Stage 2: attention over the selected keys, and the LSE combine
 # ----------------------------------------------------------------------------
 
-def attend(qi: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float):
+def attend(qi: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float,
+           allowed: Optional[np.ndarray] = None):
     """Exact softmax attention of query rows qi [m, d] over keys/values [n, d].
 
     LSE is the natural log of sum_j exp(scale * q.k_j) (reading R11: the scale is
     inside the LSE).  With no keys, O = 0 and LSE = -inf (Updating Log page,
-    Stage 3; aiter 6841 page; reading R12).
+    Stage 3; aiter 6841 page; reading R12).  `allowed` [m, n] (causal mode)
+    removes key j from row i where it is False; a row left with no key gets
+    O = 0 and LSE = -inf.
     """
     qi = np.asarray(qi, np.float64)
     m_rows = qi.shape[0]
     if keys.shape[0] == 0:
         return np.zeros((m_rows, values.shape[1])), np.full(m_rows, NEG_INF)
     s = float(scale) * (qi @ np.asarray(keys, np.float64).T)
+    if allowed is not None:
+        s = np.where(np.asarray(allowed, bool), s, NEG_INF)
     m = s.max(axis=1, keepdims=True)
+    empty = m[:, 0] == NEG_INF                      # rows with no allowed key
+    m = np.where(empty[:, None], 0.0, m)
     e = np.exp(s - m)
     l = e.sum(axis=1, keepdims=True)
-    lse = (m + np.log(l))[:, 0]
-    o = (e @ np.asarray(values, np.float64)) / l
+    l_safe = np.where(empty[:, None], 1.0, l)
+    lse = np.where(empty, NEG_INF, (m + np.log(l_safe))[:, 0])
+    o = np.where(empty[:, None], 0.0, (e @ np.asarray(values, np.float64)) / l_safe)
     return o, lse
 
 
 def block_sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                            lut: Optional[np.ndarray], count: Optional[np.ndarray],
                            blk_q: int = 64, blk_k: int = 64,
-                           scale: Optional[float] = None, lut_per_kv_head: bool = False):
+                           scale: Optional[float] = None, lut_per_kv_head: bool = False,
+                           causal: bool = False):
     """Attention of every Q-tile over the K blocks its LUT row lists.
 
     q [b, h_q, s_q, d]; k, v [b, h_kv, s_k, d]; query head j reads KV head
     j // (h_q / h_kv) (aiter 6841 page, GQA mapping).  lut [b, h_lut, nq, L]
     with count [b, h_lut, nq]; h_lut = h_kv when `lut_per_kv_head`, else h_q.
-    lut = None means every block (dense).  Returns O [b, h_q, s_q, d], LSE
-    [b, h_q, s_q].
+    lut = None means every block (dense).  With `causal` (s_q = s_k, reading
+    R23) query position i attends only to listed keys j <= i.  Returns O
+    [b, h_q, s_q, d], LSE [b, h_q, s_q].
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -321,8 +386,12 @@ def block_sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                     blocks = np.asarray(lut[ib, hl, qb, :n], dtype=np.int64)
                 idx = (blocks[:, None] * blk_k + np.arange(blk_k)[None, :]).reshape(-1)
                 rows = slice(qb * blk_q, (qb + 1) * blk_q)
+                allowed = None
+                if causal:
+                    qpos = np.arange(qb * blk_q, (qb + 1) * blk_q)
+                    allowed = idx[None, :] <= qpos[:, None]
                 o[ib, ih, rows], lse[ib, ih, rows] = attend(
-                    q[ib, ih, rows], k[ib, hk, idx], v[ib, hk, idx], scale)
+                    q[ib, ih, rows], k[ib, hk, idx], v[ib, hk, idx], scale, allowed)
     return o, lse
 
 

@@ -33,6 +33,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # copy-calibrated); quoted only while it matches the current kernel source.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fmha_block_headline_traffic.md")
 B, H, S, D = 2, 32, 16384, 128
+F_BLK = 4 * 64 * 64 * D          # flop per (64-query tile, 64-key block) pair
 
 
 def log(msg):
@@ -196,6 +197,34 @@ def extras(ops, synth, torch, steps, warmup):
                              cold_ms=median(dm_cold), cold_gathered_gbs=gathered / median(dm_cold) / 1e6,
                              cold_frac_hbm=gathered / median(dm_cold) / 1e6 / PEAK_HBM_GBS)
     del flush
+    # Causal prefill at the headline shape (b2 h32 s16384 d128 fp16, topk 0.4):
+    # block map with K smoothing, the causal block mask and the attention sink,
+    # then the causal sparse FMHA; the causal dense FMHA is the baseline.
+    hc = synth.headline_case(dev, topk=0.4)
+    ws = {}
+
+    def causal_map():
+        return ops.build_block_map(hc.q, hc.k, hc.topk, hc.simthreshd1, out=ws, smooth_k=True,
+                                   causal=True, attention_sink=True)
+
+    bm = causal_map()
+    o = torch.empty_like(hc.q)
+    l = torch.empty((B, H, S), device=dev)
+    _, bmt = time_arm(causal_map, steps, warmup, torch)
+    _, ft = time_arm(lambda: ops.sparse_fmha_fwd(hc.q, hc.k, hc.v, bm["lut"], bm["count"], o=o, lse=l,
+                                                 causal=True), steps, warmup, torch)
+    _, dt = time_arm(lambda: ops.sparse_fmha_fwd(hc.q, hc.k, hc.v, None, None, o=o, lse=l, causal=True),
+                     max(3, steps // 4), 1, torch)
+    pairs = int(bm["count"].sum().item())
+    dense_pairs = B * H * (S // 64) * (S // 64 + 1) // 2
+    out["causal_headline"] = dict(
+        workload="b2 h32 s16384 d128 fp16, topk 0.4, smooth_k + causal + attention_sink",
+        block_map_ms=median(bmt), fmha_ms=median(ft), pairs=pairs,
+        fmha_tflops_computed=pairs * F_BLK / median(ft) / 1e9,
+        dense_causal_ms=median(dt), dense_causal_pairs=dense_pairs,
+        dense_causal_tflops_computed=dense_pairs * F_BLK / median(dt) / 1e9,
+        speedup_vs_dense_step=median(dt) / (median(bmt) + median(ft)))
+    del hc, bm, o, l, ws
     return out
 
 

@@ -61,17 +61,20 @@ sparge_status check_strides(const char* name, const int64_t* st) {
 bool is_half(sparge_dtype dt) { return dt == SPARGE_F16 || dt == SPARGE_BF16; }
 
 struct BlockMapLayout {
-  size_t q_mean, k_mean, sim_q, sim_k, total;
+  size_t q_mean, k_mean, sim_q, sim_k, km_part, total;
+  int km_chunks;
 };
 
 BlockMapLayout block_map_layout(int b, int h, int s_q, int s_k, int d) {
   const size_t nq = (size_t)s_q / 64, nk = (size_t)s_k / 64, bh = (size_t)b * h;
   BlockMapLayout l;
+  l.km_chunks = (s_k + sparge::kKmChunkRows - 1) / sparge::kKmChunkRows;
   size_t off = 0;
   l.q_mean = off; off = align256(off + bh * nq * d * sizeof(float));
   l.k_mean = off; off = align256(off + bh * nk * d * sizeof(float));
   l.sim_q = off;  off = align256(off + bh * nq);
   l.sim_k = off;  off = align256(off + bh * nk);
+  l.km_part = off; off = align256(off + bh * (size_t)l.km_chunks * d * sizeof(float));
   l.total = off;
   return l;
 }
@@ -80,7 +83,7 @@ BlockMapLayout block_map_layout(int b, int h, int s_q, int s_k, int d) {
 
 extern "C" {
 
-int sparge_abi_version(void) { return 1; }
+int sparge_abi_version(void) { return 2; }
 
 const char* sparge_last_error(void) { return g_error.c_str(); }
 
@@ -94,7 +97,7 @@ sparge_status sparge_build_block_map(
     const void* q, const void* k, sparge_dtype dt, int b, int h, int s_q, int s_k, int d,
     const int64_t q_strides[3], const int64_t k_strides[3], int blk_q, int blk_k,
     const float* topk, const float* cdfthreshd, const float* simthreshd1, float softmax_scale,
-    int32_t* lut, int32_t* lut_count, uint8_t* block_map, float* pooled_prob, uint8_t* sim_q,
+    unsigned flags, int32_t* lut, int32_t* lut_count, uint8_t* block_map, float* pooled_prob, uint8_t* sim_q,
     uint8_t* sim_k, float* q_mean, float* k_mean, void* workspace, size_t workspace_bytes,
     void* stream) {
   if (!q || !k) return fail(SPARGE_ERR_INVALID, "q and k must be non-null");
@@ -118,6 +121,11 @@ sparge_status sparge_build_block_map(
   if (!aligned16(q) || !aligned16(k)) return fail(SPARGE_ERR_INVALID, "q/k must be 16-byte aligned");
   if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale))
     return fail(SPARGE_ERR_INVALID, "softmax_scale must be finite and >= 0");
+  if (flags & ~(SPARGE_FLAG_SMOOTH_K | SPARGE_FLAG_CAUSAL | SPARGE_FLAG_ATTN_SINK))
+    return fail(SPARGE_ERR_INVALID, "unknown flag bits 0x%x", flags);
+  const bool causal = (flags & SPARGE_FLAG_CAUSAL) != 0;
+  if (causal && s_q != s_k)
+    return fail(SPARGE_ERR_UNSUPPORTED, "causal block map needs s_q = s_k (got %d, %d)", s_q, s_k);
   const BlockMapLayout lay = block_map_layout(b, h, s_q, s_k, d);
   if (!workspace || workspace_bytes < lay.total)
     return fail(SPARGE_ERR_INVALID, "workspace of %zu bytes needed (got %zu)", lay.total, workspace_bytes);
@@ -158,14 +166,25 @@ sparge_status sparge_build_block_map(
   pa.k_mean = k_mean ? k_mean : reinterpret_cast<float*>(ws + lay.k_mean);
   pa.sim_q = sim_q ? sim_q : reinterpret_cast<uint8_t*>(ws + lay.sim_q);
   pa.sim_k = sim_k ? sim_k : reinterpret_cast<uint8_t*>(ws + lay.sim_k);
+  const bool smooth = (flags & SPARGE_FLAG_SMOOTH_K) != 0;
+  pa.km_part = smooth ? reinterpret_cast<float*>(ws + lay.km_part) : nullptr;
+  pa.km_chunks = lay.km_chunks;
+  pa.km_scale = 1.0f / (float)s_k;
 
   sa.q_mean = pa.q_mean; sa.k_mean = pa.k_mean; sa.sim_q = pa.sim_q; sa.sim_k = pa.sim_k;
   sa.b = b; sa.h = h; sa.nq = nq; sa.nk = nk;
   sa.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
   sa.lut = lut; sa.count = lut_count; sa.bmap = block_map; sa.prob = pooled_prob;
+  sa.causal = causal ? 1 : 0;
+  sa.sink = (flags & SPARGE_FLAG_ATTN_SINK) ? 1 : 0;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = launch_pool_sim(pa, dt, d, s);
+  hipError_t e;
+  if (smooth) {
+    e = launch_key_mean(pa, dt, d, s);
+    if (e != hipSuccess) return hip_status(e, "key_mean launch");
+  }
+  e = launch_pool_sim(pa, dt, d, s);
   if (e != hipSuccess) return hip_status(e, "pool_sim launch");
   e = launch_score_select(sa, d, s);
   return hip_status(e, "score_select launch");
@@ -176,7 +195,7 @@ sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void*
                               int s_k, int d, const int64_t q_strides[3], const int64_t k_strides[3],
                               const int64_t v_strides[3], const int64_t o_strides[3], int blk_q,
                               int blk_k, const int32_t* lut, const int32_t* lut_count, int lut_row_len,
-                              int lut_heads, float softmax_scale, int num_splits,
+                              int lut_heads, float softmax_scale, unsigned flags, int num_splits,
                               int64_t o_split_stride, void* stream) {
   if (!q || !k || !v || !o) return fail(SPARGE_ERR_INVALID, "q, k, v and o must be non-null");
   if (!is_half(dt)) return fail(SPARGE_ERR_UNSUPPORTED, "input dtype must be F16 or BF16");
@@ -203,6 +222,12 @@ sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void*
   const bool block_mode = blk_q == 64 && blk_k == 64;
   if (!token_mode && !block_mode)
     return fail(SPARGE_ERR_UNSUPPORTED, "blocks (%d, %d) not built: use (64, 64) or (1, 1)", blk_q, blk_k);
+  if (flags & ~SPARGE_FLAG_CAUSAL)
+    return fail(SPARGE_ERR_INVALID, "sparse_fmha_fwd takes only SPARGE_FLAG_CAUSAL (flags 0x%x)", flags);
+  const bool causal = (flags & SPARGE_FLAG_CAUSAL) != 0;
+  if (causal && token_mode) return fail(SPARGE_ERR_INVALID, "causal masking applies to block mode only");
+  if (causal && s_q != s_k)
+    return fail(SPARGE_ERR_UNSUPPORTED, "causal attention needs s_q = s_k (got %d, %d)", s_q, s_k);
   if (lut) {
     if (lut_row_len <= 0) return fail(SPARGE_ERR_INVALID, "lut_row_len must be positive");
     if (lut_heads != h_q && lut_heads != h_kv)
@@ -221,6 +246,7 @@ sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void*
   a.scale_log2 = scale * 1.4426950408889634f;
   a.splits = num_splits;
   a.o_split_stride = num_splits > 1 ? o_split_stride : 0;
+  a.causal = causal ? 1 : 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   if (block_mode) {

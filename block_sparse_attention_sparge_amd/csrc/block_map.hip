@@ -30,9 +30,50 @@
 namespace sparge {
 
 // ---------------------------------------------------------------------------
+// key_mean: partial sums of K over the sequence (K smoothing)
+// ---------------------------------------------------------------------------
+// CK page, not-yet-ported list: K smoothing subtracts km = mean_s(k) before
+// pooling.  One workgroup sums kKmChunkRows consecutive K rows of one (b, h);
+// pool_sim adds the chunks in a fixed order, so km is deterministic.
+template <class E, int D>
+__global__ __launch_bounds__(256) void key_mean_kernel(PoolArgs a) {
+  constexpr int CH = D / 8;          // 16-byte chunks per row
+  constexpr int RPP = 256 / CH;      // rows per pass
+  __shared__ float s_part[RPP][D];
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.x / a.km_chunks;
+  const int chunk = (int)(blockIdx.x % a.km_chunks);
+  const int hh = (int)(bh % a.h), bb = (int)(bh / a.h);
+  const int r0 = chunk * kKmChunkRows;
+  const int rows = min(kKmChunkRows, a.nk * 64 - r0);
+  const int c = tid % CH, rsub = tid / CH;
+  const typename E::T* base = reinterpret_cast<const typename E::T*>(a.k) + bb * a.ks[0] + hh * a.ks[1] + c * 8;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll 8
+  for (int r = rsub; r < rows; r += RPP) {
+    const u32x4 w = load16(base + (int64_t)(r0 + r) * a.ks[2]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] += E::lo(w[j]);
+      acc[2 * j + 1] += E::hi(w[j]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s_part[rsub][c * 8 + i] = acc[i];
+  __syncthreads();
+  for (int dd = tid; dd < D; dd += 256) {
+    float sum = 0.f;
+    for (int j = 0; j < RPP; ++j) sum += s_part[j][dd];
+    a.km_part[(bh * a.km_chunks + chunk) * D + dd] = sum;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // pool_sim
 // ---------------------------------------------------------------------------
-template <class E, int D>
+template <class E, int D, bool SMOOTH>
 __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
   constexpr int CH = D / 8;          // 16-byte chunks per token
   constexpr int TPP = kWave / CH;    // tokens per pass of the wave
@@ -61,6 +102,20 @@ __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
 #pragma unroll
   for (int p = 0; p < NP; ++p) raw[p] = load16(p0 + (int64_t)(p * TPP) * st[2]);
 
+  // K smoothing: this lane's 8 entries of km (zero when not smoothing).
+  float kmv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kmv[i] = 0.f;
+  if (SMOOTH && is_k) {
+    const float* kp = a.km_part + bh * a.km_chunks * D + c * 8;
+    for (int ch = 0; ch < a.km_chunks; ++ch) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kmv[i] += kp[(int64_t)ch * D + i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kmv[i] *= a.km_scale;
+  }
+
   float sx[8], sh[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) { sx[i] = 0.f; sh[i] = 0.f; }
@@ -69,8 +124,8 @@ __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
     float x[8];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      x[2 * w] = E::lo(raw[p][w]);
-      x[2 * w + 1] = E::hi(raw[p][w]);
+      x[2 * w] = E::lo(raw[p][w]) - kmv[2 * w];
+      x[2 * w + 1] = E::hi(raw[p][w]) - kmv[2 * w + 1];
     }
     float n2 = 0.f;
 #pragma unroll
@@ -234,10 +289,14 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[g][t], kf[g][t], acc, 0, 0, 0);
     }
-    // C: lane holds column kb for rows 4*k4 .. 4*k4+3.
+    // C: lane holds column kb for rows 4*k4 .. 4*k4+3.  Causal: block kb is
+    // in the future of Q-tile qb0 + row when kb > qb0 + row.
     const bool live = kb < nk && simk[kb] != 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_score[4 * k4 + i][kb] = live ? acc[i] * a.scale : -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = live && (!a.causal || kb <= qb0 + 4 * k4 + i);
+      s_score[4 * k4 + i][kb] = ok ? acc[i] * a.scale : -INFINITY;
+    }
 #pragma unroll
     for (int g = 0; g < NG; ++g) kf[g] = kn[g];
   }
@@ -259,6 +318,12 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
   bool valid[KPL];
 #pragma unroll
   for (int j = 0; j < KPL; ++j) valid[j] = lane * KPL + j < nk;
+  // Blocks a row may select: all nk, or kb <= qb when causal.  Future blocks
+  // have probability 0 and a larger index than any allowed block, so the
+  // first `limit` of the order are allowed ones.
+  int limit[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) limit[i] = a.causal ? min(nk, qb0 + 4 * i + wave + 1) : nk;
 
   // The RW rows of a wave go through every step side by side, so that their
   // reduction and ballot chains overlap instead of running one after another.
@@ -334,7 +399,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
 #pragma unroll
         for (int j = 0; j < KPL; ++j)
           c += __popcll(__ballot(valid[j] && __builtin_bit_cast(uint32_t, p[i][j]) >= mid));
-        if (c >= nsel_h) lo[i] = mid;
+        if (c >= min(nsel_h, limit[i])) lo[i] = mid;
         else hi[i] = mid;
       }
     }
@@ -348,7 +413,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
         above += __popcll(__ballot(valid[j] && pb > t));      // strictly greater than T
         ties += (valid[j] && pb == t) ? 1 : 0;
       }
-      const int need = nsel_h - above;                           // ties at T to take
+      const int need = min(nsel_h, limit[i]) - above;            // ties at T to take
       int tie_rank = wave_inclusive_scan(ties) - ties;           // ties before this lane
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
@@ -395,7 +460,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
           if (c >= cdf_h) { found = q + 1; break; }
         }
       }
-      const int n = __shfl(found, 0, kWave);
+      const int n = min(__shfl(found, 0, kWave), a.causal ? min(nk, qb0 + r + 1) : nk);
 #pragma unroll
       for (int j = 0; j < KPL; ++j)
         if (lane * KPL + j < n) s_sel[r][~(uint32_t)key[j]] = 1;
@@ -408,7 +473,8 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
       for (int j = 0; j < KPL; ++j) chosen[i][j] = s_sel[4 * i + wave][lane * KPL + j] != 0;
   }
 
-  // OR in the gate and write the ascending LUT by a prefix scan.
+  // OR in the gate (within the allowed blocks) and the sink, then write the
+  // ascending LUT by a prefix scan.
   int cnt[RW], incl[RW];
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
@@ -416,7 +482,9 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
     cnt[i] = 0;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
-      chosen[i][j] = valid[j] && (!simq || chosen[i][j] || kgate[j]);
+      const int e = lane * KPL + j;
+      chosen[i][j] = (valid[j] && e < limit[i] && (!simq || chosen[i][j] || kgate[j])) ||
+                     (a.sink && e == 0);
       cnt[i] += chosen[i][j] ? 1 : 0;
     }
     incl[i] = cnt[i];
@@ -453,9 +521,26 @@ template <class E>
 static hipError_t launch_pool_t(const PoolArgs& a, int d, hipStream_t st) {
   const int64_t waves = (int64_t)a.b * a.h * (a.nq + a.nk);
   const dim3 grid((unsigned)((waves + 3) / 4));
-  if (d == 128) hipLaunchKernelGGL((pool_sim_kernel<E, 128>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((pool_sim_kernel<E, 64>), grid, dim3(256), 0, st, a);
+  if (a.km_part) {
+    if (d == 128) hipLaunchKernelGGL((pool_sim_kernel<E, 128, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((pool_sim_kernel<E, 64, true>), grid, dim3(256), 0, st, a);
+  } else {
+    if (d == 128) hipLaunchKernelGGL((pool_sim_kernel<E, 128, false>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((pool_sim_kernel<E, 64, false>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError();
+}
+
+template <class E>
+static hipError_t launch_key_mean_t(const PoolArgs& a, int d, hipStream_t st) {
+  const dim3 grid((unsigned)((int64_t)a.b * a.h * a.km_chunks));
+  if (d == 128) hipLaunchKernelGGL((key_mean_kernel<E, 128>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((key_mean_kernel<E, 64>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_key_mean(const PoolArgs& a, sparge_dtype dt, int d, hipStream_t st) {
+  return dt == SPARGE_F16 ? launch_key_mean_t<F16>(a, d, st) : launch_key_mean_t<BF16>(a, d, st);
 }
 
 hipError_t launch_pool_sim(const PoolArgs& a, sparge_dtype dt, int d, hipStream_t st) {

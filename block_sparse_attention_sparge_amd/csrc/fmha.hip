@@ -143,7 +143,7 @@ struct Buf {
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <class E, int D, bool OUT_F32>
+template <class E, int D, bool OUT_F32, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fmha_block_kernel(FmhaArgs a) {
   typedef typename E::T T;
@@ -183,7 +183,7 @@ void fmha_block_kernel(FmhaArgs a) {
     list = a.lut + row * a.lut_row_len;
     n = a.cnt ? a.cnt[row] : first_negative(list, a.lut_row_len, lane);
   } else {
-    n = a.nkb;
+    n = CAUSAL ? min(a.nkb, qt + 1) : a.nkb;   // dense causal: blocks 0..qt
   }
   // The row length is the same for every lane; saying so keeps the loop
   // uniform and lets the LUT entries come through scalar loads.
@@ -272,6 +272,10 @@ void fmha_block_kernel(FmhaArgs a) {
   __syncthreads();
   if (nloc > 1) issue_block(kb_of(1), 1);
   int kb_ahead = nloc > 2 ? kb_of(2) : 0;
+  // Causal masking needs the block index of the step: kb_cur (block it) and
+  // kb_nxt (block it+1) trail kb_ahead.
+  int kb_cur = CAUSAL ? kb_of(0) : 0;
+  int kb_nxt = CAUSAL && nloc > 1 ? kb_of(1) : 0;
 
   // One 64-key block out of LDS buffer `cur` (a compile-time constant, so
   // every LDS address is a fixed register plus an immediate offset).
@@ -318,6 +322,20 @@ void fmha_block_kernel(FmhaArgs a) {
     read_vt(1);
     __builtin_amdgcn_sched_barrier(0);
 
+    if constexpr (CAUSAL) {
+      // Key 64 kb + 32 kh + 8 (r/4) + 4 hl + r%4 of register r against query
+      // 64 qt + 32 qh + l32: keys past the query are removed.  Only the
+      // diagonal block and blocks past it (listed by hand) can hold any.
+      if (kb_cur >= qt) {
+        const int qpos = 64 * qt + 32 * qh + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 64 * kb_cur + 32 * kh + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (key > qpos) s[r] = -INFINITY;
+        }
+      }
+    }
+
     // Online softmax in base 2 over this lane's 16 scores.
     float rmax = s[0];
 #pragma unroll
@@ -335,13 +353,15 @@ void fmha_block_kernel(FmhaArgs a) {
     }
     // P^T fragments (k-step ks uses registers 8ks .. 8ks+7), rounded to the
     // input type; the row sum adds the rounded values, the ones PV uses.
+    // Causal rows may still have no key (m_run = -inf): their P is 0.
+    const float mref = CAUSAL && m_run == -INFINITY ? 0.f : m_run;
     u32x4 pf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w], c2, -m_run));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w + 1], c2, -m_run));
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w], c2, -mref));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w + 1], c2, -mref));
         pf[ks][w] = E::pack2(p0, p1);
         l_run = E::sum2(pf[ks][w], l_run);
       }
@@ -366,6 +386,10 @@ void fmha_block_kernel(FmhaArgs a) {
     wait_dma();
     __syncthreads();
     if (it + 2 < nloc) issue_block(kb_ahead, cur);
+    if constexpr (CAUSAL) {
+      kb_cur = kb_nxt;
+      kb_nxt = kb_ahead;
+    }
     kb_ahead = kb_next;
   };
 
@@ -393,10 +417,14 @@ void fmha_block_kernel(FmhaArgs a) {
   __syncthreads();
   if (kh == 1) return;
   const float m1 = ml[l32], l1 = ml[32 + l32];
-  const float m = fmaxf(m_run, m1);
+  float m = fmaxf(m_run, m1);
+  // Causal: a query row whose listed keys all lie past it has no key at all
+  // (both halves at -inf): O = 0, LSE = -inf.
+  const bool empty = CAUSAL && m == -INFINITY;
+  if (empty) m = 0.f;
   const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
   const float l_tot = l_w * a0 + l1 * a1;
-  const float inv = 1.0f / l_tot;
+  const float inv = empty ? 0.f : 1.0f / l_tot;
   const float s0 = a0 * inv, s1 = a1 * inv;
 #pragma unroll
   for (int md = 0; md < NMD; ++md) {
@@ -412,7 +440,7 @@ void fmha_block_kernel(FmhaArgs a) {
       store4<E, OUT_F32>(a.o, orow + d0, x[0], x[1], x[2], x[3]);
     }
   }
-  if (lse_row && hl == 0) lse_row[q0 + l32] = (m + __log2f(l_tot)) * kLn2;
+  if (lse_row && hl == 0) lse_row[q0 + l32] = empty ? -INFINITY : (m + __log2f(l_tot)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -642,8 +670,13 @@ template <class E, int D>
 static hipError_t launch_block_t(const FmhaArgs& a, bool out_f32, hipStream_t st) {
   const int64_t G = (int64_t)a.nqt * a.hq * a.b * a.splits;
   const dim3 grid((unsigned)(((G + 7) / 8) * 8));
-  if (out_f32) hipLaunchKernelGGL((fmha_block_kernel<E, D, true>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((fmha_block_kernel<E, D, false>), grid, dim3(256), 0, st, a);
+  if (a.causal) {
+    if (out_f32) hipLaunchKernelGGL((fmha_block_kernel<E, D, true, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((fmha_block_kernel<E, D, false, true>), grid, dim3(256), 0, st, a);
+  } else {
+    if (out_f32) hipLaunchKernelGGL((fmha_block_kernel<E, D, true, false>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((fmha_block_kernel<E, D, false, false>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -21,8 +21,16 @@ struct PoolArgs {
   float* k_mean;     // [b, h, nk, d]
   uint8_t* sim_q;    // [b, h, nq]
   uint8_t* sim_k;    // [b, h, nk]
+  // K smoothing: per-chunk sums of K over the sequence, [b, h, km_chunks, d];
+  // km = (sum over chunks) * km_scale.  Null when K is pooled as given.
+  float* km_part;
+  int km_chunks;
+  float km_scale;    // 1 / s_k
   float thr[SPARGE_MAX_HEADS];
 };
+
+// K rows summed per partial of the K sequence mean (16 blocks of 64).
+constexpr int kKmChunkRows = 1024;
 
 struct SelectArgs {
   const float* q_mean;
@@ -35,6 +43,8 @@ struct SelectArgs {
   int32_t* count;    // [b, h, nq]
   uint8_t* bmap;     // [b, h, nq, nk] or null
   float* prob;       // [b, h, nq, nk] or null
+  int causal;        // blocks kb > qb masked, counts clamped to qb + 1
+  int sink;          // block 0 forced on
   int nsel[SPARGE_MAX_HEADS];   // > 0: top-k count; <= 0: cdf mode
   float cdf[SPARGE_MAX_HEADS];
 };
@@ -57,6 +67,7 @@ struct FmhaArgs {
   float scale_log2;        // softmax scale * log2(e)
   int splits;
   int64_t o_split_stride;  // elements
+  int causal;              // block mode: key j > query i masked
 };
 
 struct CombineArgs {
@@ -69,6 +80,7 @@ struct CombineArgs {
   float* lse_out;
 };
 
+hipError_t launch_key_mean(const PoolArgs& a, sparge_dtype dt, int d, hipStream_t st);
 hipError_t launch_pool_sim(const PoolArgs& a, sparge_dtype dt, int d, hipStream_t st);
 hipError_t launch_score_select(const SelectArgs& a, int d, hipStream_t st);
 hipError_t launch_fmha_block(const FmhaArgs& a, sparge_dtype dt, sparge_dtype o_dt, int d,

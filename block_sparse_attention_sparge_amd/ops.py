@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(_PKG, "libsparge.so")
 
 SPARGE_OK, SPARGE_ERR_INVALID, SPARGE_ERR_UNSUPPORTED, SPARGE_ERR_HIP = 0, 1, 2, 3
 SPARGE_F16, SPARGE_BF16, SPARGE_F32 = 0, 1, 2
+SPARGE_FLAG_SMOOTH_K, SPARGE_FLAG_CAUSAL, SPARGE_FLAG_ATTN_SINK = 1, 2, 4
+ABI_VERSION = 2
 MAX_HEADS = 128
 MAX_KBLOCKS = 1024
 
@@ -47,6 +49,7 @@ _i = ctypes.c_int
 _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
 _f = ctypes.c_float
+_u = ctypes.c_uint
 _sz = ctypes.c_size_t
 _I64x3 = ctypes.c_int64 * 3
 
@@ -64,6 +67,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         lib = ctypes.CDLL(p)
         lib.sparge_abi_version.restype = _i
         lib.sparge_abi_version.argtypes = []
+        if lib.sparge_abi_version() != ABI_VERSION:
+            raise SpargeError(SPARGE_ERR_HIP, f"{p} has ABI version {lib.sparge_abi_version()}, this "
+                              f"binding needs {ABI_VERSION}: rebuild it")
         lib.sparge_last_error.restype = ctypes.c_char_p
         lib.sparge_last_error.argtypes = []
         lib.sparge_build_block_map_workspace.restype = _sz
@@ -71,11 +77,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         lib.sparge_build_block_map.restype = _i
         lib.sparge_build_block_map.argtypes = [
             _p, _p, _i, _i, _i, _i, _i, _i, _I64x3, _I64x3, _i, _i,
-            _p, _p, _p, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
+            _p, _p, _p, _f, _u, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
         lib.sparse_fmha_fwd.restype = _i
         lib.sparse_fmha_fwd.argtypes = [
             _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
-            _I64x3, _I64x3, _I64x3, _I64x3, _i, _i, _p, _p, _i, _i, _f, _i, _i64, _p]
+            _I64x3, _I64x3, _I64x3, _I64x3, _i, _i, _p, _p, _i, _i, _f, _u, _i, _i64, _p]
         lib.attn_combine.restype = _i
         lib.attn_combine.argtypes = [_p, _i, _p, _i, _i, _i, _i, _i, _i64, _p, _i, _p, _p]
         lib.sparge_validate_lut.restype = _i
@@ -142,6 +148,11 @@ def _f32_array(vals: Optional[Sequence[float]], n: int, name: str):
     return (ctypes.c_float * n)(*vals)
 
 
+def _flags(smooth_k: bool = False, causal: bool = False, attention_sink: bool = False) -> int:
+    return ((SPARGE_FLAG_SMOOTH_K if smooth_k else 0) | (SPARGE_FLAG_CAUSAL if causal else 0) |
+            (SPARGE_FLAG_ATTN_SINK if attention_sink else 0))
+
+
 def block_map_workspace_bytes(b: int, h: int, s_q: int, s_k: int, d: int, blk_q: int = 64,
                               blk_k: int = 64) -> int:
     return int(load_library().sparge_build_block_map_workspace(b, h, s_q, s_k, d, blk_q, blk_k))
@@ -150,13 +161,15 @@ def block_map_workspace_bytes(b: int, h: int, s_q: int, s_k: int, d: int, blk_q:
 def build_block_map(q: torch.Tensor, k: torch.Tensor, topk, simthreshd1, cdfthreshd=None,
                     softmax_scale: float = 0.0, blk_q: int = 64, blk_k: int = 64,
                     return_debug: bool = False, workspace: Optional[torch.Tensor] = None,
-                    out: Optional[dict] = None) -> dict:
+                    out: Optional[dict] = None, smooth_k: bool = False, causal: bool = False,
+                    attention_sink: bool = False) -> dict:
     """Stage 1 (sparge_build_block_map).  q [b, h, s_q, d], k [b, h, s_k, d].
 
     Returns a dict with 'lut' int32 [b, h, nq, nk], 'count' int32 [b, h, nq],
     and with return_debug also 'bitmap', 'prob', 'sim_q', 'sim_k', 'q_mean',
     'k_mean'.  `out` may hold preallocated tensors under the same keys (plus
-    'workspace').
+    'workspace').  smooth_k / causal / attention_sink set SPARGE_FLAG_SMOOTH_K /
+    SPARGE_FLAG_CAUSAL / SPARGE_FLAG_ATTN_SINK.
     """
     lib = load_library()
     dev = _on_gpu(q, k)
@@ -196,6 +209,7 @@ def build_block_map(q: torch.Tensor, k: torch.Tensor, topk, simthreshd1, cdfthre
         _ptr(q), _ptr(k), _dt(q.dtype), b, h, s_q, s_k, d, _strides(q), _strides(k), blk_q, blk_k,
         _f32_array(topk, h, "topk"), _f32_array(cdfthreshd, h, "cdfthreshd"),
         _f32_array(simthreshd1, h, "simthreshd1"), float(softmax_scale),
+        _flags(smooth_k=smooth_k, causal=causal, attention_sink=attention_sink),
         _ptr(lut), _ptr(count), _ptr(dbg.get("bitmap")), _ptr(dbg.get("prob")),
         _ptr(dbg.get("sim_q")), _ptr(dbg.get("sim_k")), _ptr(dbg.get("q_mean")),
         _ptr(dbg.get("k_mean")), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -211,14 +225,14 @@ def sparse_fmha_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                     blk_q: int = 64, blk_k: int = 64, softmax_scale: float = 0.0,
                     num_splits: int = 1, out_dtype: Optional[torch.dtype] = None,
                     o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                    return_lse: bool = True):
+                    return_lse: bool = True, causal: bool = False):
     """Stage 2 (sparse_fmha_fwd).  q [b, h_q, s_q, d]; k, v [b, h_kv, s_k, d].
 
     Block mode (64, 64): lut [b, h_lut, s_q/64, L] (+ count [b, h_lut, s_q/64]);
     lut None = dense.  Token mode (1, 1): lut [b, h_kv, L] token positions.
     With num_splits > 1 the outputs are partials o [S, b, h_q, s_q, d] and
-    lse [S, b, h_q, s_q] (fp32 unless out_dtype says otherwise).
-    Returns (o, lse).
+    lse [S, b, h_q, s_q] (fp32 unless out_dtype says otherwise).  causal sets
+    SPARGE_FLAG_CAUSAL (block mode, s_q = s_k).  Returns (o, lse).
     """
     lib = load_library()
     dev = _on_gpu(q, k, v, lut, count, o, lse)
@@ -252,7 +266,7 @@ def sparse_fmha_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dt(q.dtype), _dt(o.dtype),
         b, h_q, h_kv, s_q, s_k, d, _strides(q), _strides(k), _strides(v), _strides(o4),
         blk_q, blk_k, _ptr(lut), _ptr(count), lut_row_len, lut_heads, float(softmax_scale),
-        int(num_splits), int(split_stride), _stream(dev))
+        _flags(causal=causal), int(num_splits), int(split_stride), _stream(dev))
     _check(st)
     return o, lse
 

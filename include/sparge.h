@@ -62,7 +62,14 @@ typedef enum {
  * (s_k <= 64 * 1024 tokens with 64-token blocks). */
 #define SPARGE_MAX_KBLOCKS 1024
 
-/* Library ABI version (this header: 1). */
+/* Option bits for the `flags` arguments.  (CK page, "Status vs Upstream",
+ * not-yet-ported list: K smoothing before pooling, the is_causal mask in the
+ * pooled score, attention_sink with column 0 forced on.) */
+#define SPARGE_FLAG_SMOOTH_K 1u   /* block map: pool and gate k - mean_s(k)        */
+#define SPARGE_FLAG_CAUSAL 2u     /* block map and block-mode FMHA: causal masks   */
+#define SPARGE_FLAG_ATTN_SINK 4u  /* block map: K block 0 selected in every row    */
+
+/* Library ABI version (this header: 2). */
 int sparge_abi_version(void);
 
 /* Message for the last failed call on this thread ("" if none). */
@@ -91,12 +98,21 @@ const char* sparge_last_error(void);
  *   selected = all kb if the Q flag is 0, else the first n of the order plus
  *           every kb whose K flag is 0.
  *
+ * flags (SPARGE_FLAG_*; other bits are rejected):
+ *   SMOOTH_K   K is replaced by k - km before pooling and gating, km the fp32
+ *              mean over all s_k positions of the (b, h) slice; k_mean is then
+ *              the mean of the smoothed block.  Attention is unaffected.
+ *   CAUSAL     needs s_q = s_k.  S[kb] = -inf for kb > qb; n is clamped to
+ *              qb + 1; "all kb" and the forced blocks are limited to kb <= qb.
+ *   ATTN_SINK  kb = 0 is added to every row.
+ *
  * Inputs:
  *   topk        host float[h]; > 0 selects top-k mode for that head, must be <= 1.
  *   cdfthreshd  host float[h] or NULL; used for heads with topk <= 0, must be
  *               finite and in (0, 1].  NULL requires topk > 0 for every head.
  *   simthreshd1 host float[h], finite.
  *   softmax_scale  0 => 1/sqrt(d).
+ *   flags      SPARGE_FLAG_* bits (above).
  * Outputs (device, caller-owned; optional ones may be NULL):
  *   lut        int32 [b, h, nq, nk]: selected kb ascending, then -1.
  *   lut_count  int32 [b, h, nq]: number of selected blocks.
@@ -113,7 +129,7 @@ sparge_status sparge_build_block_map(
     const int64_t q_strides[3], const int64_t k_strides[3],
     int blk_q, int blk_k,
     const float* topk, const float* cdfthreshd, const float* simthreshd1,
-    float softmax_scale,
+    float softmax_scale, unsigned flags,
     int32_t* lut, int32_t* lut_count, uint8_t* block_map, float* pooled_prob,
     uint8_t* sim_q, uint8_t* sim_k, float* q_mean, float* k_mean,
     void* workspace, size_t workspace_bytes, void* stream);
@@ -160,6 +176,10 @@ size_t sparge_build_block_map_workspace(int b, int h, int s_q, int s_k, int d,
  * o_strides for (b, h, s); lse float [.., b, h_q, s_q] contiguous, or NULL
  * when num_splits = 1.
  * softmax_scale 0 => 1/sqrt(d).
+ * flags: 0 or SPARGE_FLAG_CAUSAL (block mode, s_q = s_k): query position i
+ * attends only to keys j <= i; listed blocks past the tile add nothing, and a
+ * row left with no key gives O = 0, LSE = -inf.  In dense mode (lut = NULL)
+ * the tile of rows [64 qt, 64 qt + 64) reads blocks 0..qt.
  */
 sparge_status sparse_fmha_fwd(
     const void* q, const void* k, const void* v, void* o, float* lse,
@@ -169,7 +189,7 @@ sparge_status sparse_fmha_fwd(
     const int64_t v_strides[3], const int64_t o_strides[3],
     int blk_q, int blk_k,
     const int32_t* lut, const int32_t* lut_count, int lut_row_len, int lut_heads,
-    float softmax_scale, int num_splits, int64_t o_split_stride,
+    float softmax_scale, unsigned flags, int num_splits, int64_t o_split_stride,
     void* stream);
 
 /*

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert lib.sparge_abi_version() == 1
+    assert lib.sparge_abi_version() == ops.ABI_VERSION == 2
 
 
 def _s3(a, b, c):
@@ -62,8 +62,10 @@ def _err(lib):
 
 def test_workspace_size(lib):
     n = lib.sparge_build_block_map_workspace(2, 32, 16384, 16384, 128, 64, 64)
-    # q_mean + k_mean (fp32) + two flag arrays, each rounded to 256 bytes
-    assert n == 2 * (2 * 32 * 256 * 128 * 4) + 2 * ((2 * 32 * 256 + 255) // 256 * 256)
+    # q_mean + k_mean (fp32) + two flag arrays + K-mean partials (16 chunks of
+    # 1024 rows per head, fp32), each rounded up to 256 bytes
+    assert n == (2 * (2 * 32 * 256 * 128 * 4) + 2 * ((2 * 32 * 256 + 255) // 256 * 256)
+                 + 2 * 32 * 16 * 128 * 4)
     assert lib.sparge_build_block_map_workspace(1, 1, 100, 64, 64, 64, 64) == 0
     assert lib.sparge_build_block_map_workspace(1, 1, 64, 64, 96, 64, 64) == 0
 
@@ -71,13 +73,13 @@ def test_workspace_size(lib):
 def _bm(lib, **kw):
     args = dict(q=FAKE, k=FAKE, dt=ops.SPARGE_F16, b=1, h=2, s_q=512, s_k=512, d=64,
                 qs=_s3(65536, 32768, 64), ks=_s3(65536, 32768, 64), blk_q=64, blk_k=64,
-                topk=_arr([0.5, 0.5]), cdf=None, sim=_arr([0.001, 0.001]), scale=0.0,
+                topk=_arr([0.5, 0.5]), cdf=None, sim=_arr([0.001, 0.001]), scale=0.0, flags=0,
                 lut=FAKE, cnt=FAKE, ws=FAKE, ws_bytes=1 << 20)
     args.update(kw)
     return lib.sparge_build_block_map(
         args["q"], args["k"], args["dt"], args["b"], args["h"], args["s_q"], args["s_k"], args["d"],
         args["qs"], args["ks"], args["blk_q"], args["blk_k"], args["topk"], args["cdf"], args["sim"],
-        args["scale"], args["lut"], args["cnt"], None, None, None, None, None, None,
+        args["scale"], args["flags"], args["lut"], args["cnt"], None, None, None, None, None, None,
         args["ws"], args["ws_bytes"], None)
 
 
@@ -102,6 +104,8 @@ def _bm(lib, **kw):
     (dict(ws=FAKE + 16), ops.SPARGE_ERR_INVALID),
     (dict(q=FAKE + 2), ops.SPARGE_ERR_INVALID),
     (dict(scale=-1.0), ops.SPARGE_ERR_INVALID),
+    (dict(flags=8), ops.SPARGE_ERR_INVALID),                         # unknown flag bit
+    (dict(flags=ops.SPARGE_FLAG_CAUSAL, s_k=1024), ops.SPARGE_ERR_UNSUPPORTED),   # causal, s_q != s_k
 ])
 def test_block_map_rejections(lib, kw, status):
     st = _bm(lib, **kw)
@@ -114,12 +118,12 @@ def _fmha(lib, **kw):
              b=1, hq=8, hkv=2, sq=512, sk=512, d=128, qs=_s3(8 * 512 * 128, 512 * 128, 128),
              ks=_s3(2 * 512 * 128, 512 * 128, 128), vs=_s3(2 * 512 * 128, 512 * 128, 128),
              os=_s3(8 * 512 * 128, 512 * 128, 128), bq=64, bk=64, lut=FAKE, cnt=FAKE, L=8,
-             lh=8, scale=0.0, splits=1, sst=0)
+             lh=8, scale=0.0, flags=0, splits=1, sst=0)
     a.update(kw)
     return lib.sparse_fmha_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dt"], a["odt"], a["b"],
                                a["hq"], a["hkv"], a["sq"], a["sk"], a["d"], a["qs"], a["ks"], a["vs"],
                                a["os"], a["bq"], a["bk"], a["lut"], a["cnt"], a["L"], a["lh"],
-                               a["scale"], a["splits"], a["sst"], None)
+                               a["scale"], a["flags"], a["splits"], a["sst"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -144,6 +148,9 @@ def _fmha(lib, **kw):
     (dict(lut=None, cnt=FAKE), ops.SPARGE_ERR_INVALID),
     (dict(scale=float("nan")), ops.SPARGE_ERR_INVALID),
     (dict(vs=_s3(2 * 512 * 128, 512 * 128, 1 << 24)), ops.SPARGE_ERR_UNSUPPORTED),   # 64 rows span 2^31 bytes
+    (dict(flags=ops.SPARGE_FLAG_SMOOTH_K), ops.SPARGE_ERR_INVALID),                  # block-map flag only
+    (dict(flags=ops.SPARGE_FLAG_CAUSAL, sk=1024), ops.SPARGE_ERR_UNSUPPORTED),       # causal, s_q != s_k
+    (dict(flags=ops.SPARGE_FLAG_CAUSAL, bq=1, bk=1, cnt=None, lh=2), ops.SPARGE_ERR_INVALID),   # token mode
     # token-list mode
     (dict(bq=1, bk=1, lut=None, cnt=None), ops.SPARGE_ERR_INVALID),
     (dict(bq=1, bk=1, cnt=FAKE, lh=2), ops.SPARGE_ERR_INVALID),

@@ -1,0 +1,212 @@
+"""GPU parity for K smoothing, the causal masks and the attention sink.
+
+These are the CK page's not-yet-ported items ("Sparge Attention (Composable
+Kernel)" page, "Status vs Upstream").  The bars are the ones of the other
+parity tests: the LUT bit-exact against the oracle's selection run on the
+GPU's own pooled probabilities and flags (with the same options), pooled means
+and probabilities within 1e-3 relative, attention within atol 4e-2 / rtol 1e-2
+and LSE within 2e-3 nats with -inf matching exactly.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_sparge_amd import ops, synth
+
+pytestmark = pytest.mark.gpu
+
+O_ATOL, O_RTOL, LSE_TOL = 4e-2, 1e-2, 2e-3
+
+
+def np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check_o(o_gpu, o_ref):
+    err = np.abs(np64(o_gpu) - o_ref)
+    bad = err > O_ATOL + O_RTOL * np.abs(o_ref)
+    assert not bad.any(), f"O: {bad.sum()} of {bad.size} outside atol/rtol; max err {err.max():.3e}"
+
+
+def check_lse(l_gpu, l_ref):
+    g = np64(l_gpu)
+    assert np.array_equal(np.isneginf(g), np.isneginf(l_ref)), "-inf rows differ"
+    fin = ~np.isneginf(l_ref)
+    if fin.any():
+        err = np.abs(g[fin] - l_ref[fin]).max()
+        assert err <= LSE_TOL, f"LSE max err {err:.3e} nats"
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    ops.load_library()
+    return torch.device("cuda:0")
+
+
+def _offset_keys(k, seed, scale=2.0):
+    """K plus one random offset vector per (b, h): the part smoothing removes."""
+    b, h, _, d = k.shape
+    g = torch.Generator(device=k.device).manual_seed(seed)
+    off = torch.randn(b, h, 1, d, generator=g, device=k.device) * scale
+    return (k.float() + off).to(k.dtype)
+
+
+def _block_map_with_options(dev, q, k, topk, simthreshd1, cdf=None, **opts):
+    res = ops.build_block_map(q, k, topk, simthreshd1, cdfthreshd=cdf, return_debug=True, **opts)
+    torch.cuda.synchronize()
+    ref = oracle.block_map(np64(q), np64(k), topk=topk, simthreshd1=simthreshd1, cdfthreshd=cdf, **opts)
+    for key in ("q_mean", "k_mean"):
+        g, r = np64(res[key]), ref[key]
+        rms = math.sqrt(float((r * r).mean()))
+        assert (np.abs(g - r) <= 1e-3 * np.abs(r) + 1e-6 * rms).all(), key
+    for key, val in (("sim_q", "sim_q_val"), ("sim_k", "sim_k_val")):
+        g = np64(res[key]).astype(bool)
+        thr = np.array(simthreshd1)[None, :, None]
+        far = np.abs(ref[val] - thr) > 1e-5
+        assert np.array_equal(g[far], ref[key][far]), key
+    gp = np64(res["prob"])
+    assert (np.abs(gp - ref["prob"]) <= 1e-3 * np.abs(ref["prob"]) + 1e-7).all(), "pooled prob"
+    lut, cnt, bm = oracle.select_from_probs(
+        gp, np64(res["sim_q"]).astype(bool), np64(res["sim_k"]).astype(bool), topk, cdf,
+        causal=opts.get("causal", False), attention_sink=opts.get("attention_sink", False))
+    assert np.array_equal(res["lut"].cpu().numpy(), lut), "LUT not bit-exact"
+    assert np.array_equal(res["count"].cpu().numpy(), cnt), "count not bit-exact"
+    assert np.array_equal(res["bitmap"].cpu().numpy(), bm), "bitmap not bit-exact"
+    assert ops.validate_lut(res["lut"], res["count"], k.shape[2] // 64) == 0
+    return res, ref
+
+
+@pytest.mark.parametrize("smooth_k", [False, True])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("attention_sink", [False, True])
+def test_block_map_options_tiny(dev, smooth_k, causal, attention_sink):
+    case = synth.tiny_case(dev, seed=7)
+    k = _offset_keys(case.k, 70)
+    res, ref = _block_map_with_options(dev, case.q, k, [0.5, 0.25], [0.001, 0.3],
+                                       smooth_k=smooth_k, causal=causal,
+                                       attention_sink=attention_sink)
+    lut, cnt = res["lut"].cpu().numpy(), res["count"].cpu().numpy()
+    for qb in range(lut.shape[2]):
+        sel = lut[:, :, qb]
+        if causal:
+            assert ((sel <= qb) | (sel == -1)).all()
+        if attention_sink:
+            assert (sel[..., 0] == 0).all() and (cnt[:, :, qb] >= 1).all()
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_block_map_smoothing_changes_the_k_gate(dev, dtype):
+    # A large common offset makes every raw K block look coherent (sim near
+    # 1); smoothing removes it, and the gate at 0.5 closes for noisy blocks.
+    b, h, s, d = 1, 2, 1024, 64
+    q = synth.centroid_noise(b, h, s, d, 64, [1.0, 1.0], 0.5, 11, 1, dtype, dev)
+    k = synth.centroid_noise(b, h, s, d, 64, [0.2, 0.2], 1.0, 11, 2, dtype, dev)
+    k = _offset_keys(k, 71, scale=4.0)
+    raw, _ = _block_map_with_options(dev, q, k, [0.25, 0.25], [0.5, 0.5])
+    sm, ref = _block_map_with_options(dev, q, k, [0.25, 0.25], [0.5, 0.5], smooth_k=True)
+    assert raw["sim_k"].cpu().numpy().all()
+    assert ref["sim_k"].sum() < ref["sim_k"].size // 2
+    # the smoothed K means average to zero over each (b, h)
+    assert np.abs(np64(sm["k_mean"]).mean(axis=2)).max() < 1e-3
+
+
+@pytest.mark.parametrize("topk", [0.4, 1.0])
+def test_block_map_causal_mid(dev, topk):
+    case = synth.mid_case(dev, topk=topk)
+    res, _ = _block_map_with_options(dev, case.q, case.k, case.topk, case.simthreshd1, causal=True)
+    cnt = res["count"].cpu().numpy()
+    nq = cnt.shape[2]
+    n = oracle.topk_count(topk, nq)
+    assert (cnt >= np.minimum(n, np.arange(nq) + 1)[None, None, :]).all()
+
+
+def test_block_map_causal_cdf_mode(dev):
+    case = synth.mid_case(dev)
+    cdf = [0.3, 0.6, 0.9, 0.99, 1.0, 0.5, 0.75, 0.95]
+    _block_map_with_options(dev, case.q, case.k, [0.0] * 8, case.simthreshd1, cdf=cdf,
+                            causal=True, attention_sink=True)
+
+
+# ---------------------------------------------------------------------------
+# causal attention
+# ---------------------------------------------------------------------------
+
+def _causal_vs_oracle(q, k, v, lut, cnt, o, lse, per_kv=False):
+    ro, rl = oracle.block_sparse_attention(np64(q), np64(k), np64(v),
+                                           None if lut is None else lut.cpu().numpy(),
+                                           None if cnt is None else cnt.cpu().numpy(),
+                                           lut_per_kv_head=per_kv, causal=True)
+    check_o(o, ro)
+    check_lse(lse, rl)
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.float16, 128), (torch.bfloat16, 64)])
+def test_causal_dense_mode(dev, dtype, d):
+    b, h, s = 2, 3, 640
+    g = torch.Generator(device=dev).manual_seed(80 + d)
+    q, k, v = (torch.randn(b, h, s, d, generator=g, device=dev).to(dtype) for _ in range(3))
+    o, lse = ops.sparse_fmha_fwd(q, k, v, None, None, causal=True)
+    torch.cuda.synchronize()
+    _causal_vs_oracle(q, k, v, None, None, o, lse)
+    ref = torch.nn.functional.scaled_dot_product_attention(q.float().cpu(), k.float().cpu(),
+                                                           v.float().cpu(), is_causal=True)
+    check_o(o, ref.double().numpy())
+
+
+@pytest.mark.parametrize("topk", [0.4, 1.0])
+def test_causal_end_to_end_mid(dev, topk):
+    case = synth.mid_case(dev, topk=topk)
+    bm = ops.build_block_map(case.q, case.k, case.topk, case.simthreshd1, causal=True,
+                             attention_sink=True)
+    o, lse = ops.sparse_fmha_fwd(case.q, case.k, case.v, bm["lut"], bm["count"], causal=True)
+    torch.cuda.synchronize()
+    _causal_vs_oracle(case.q, case.k, case.v, bm["lut"], bm["count"], o, lse)
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("per_kv", [False, True])
+def test_causal_lut_with_future_blocks_and_empty_rows(dev, dtype, per_kv):
+    # LUT rows may list blocks past their tile (they add nothing); a row whose
+    # only block lies in its future has no key: O = 0, LSE = -inf.
+    b, hq, hkv, s, d = 2, 4, 2, 512, 128
+    nq = s // 64
+    g = torch.Generator(device=dev).manual_seed(90)
+    q = torch.randn(b, hq, s, d, generator=g, device=dev).to(dtype)
+    k = torch.randn(b, hkv, s, d, generator=g, device=dev).to(dtype)
+    v = torch.randn(b, hkv, s, d, generator=g, device=dev).to(dtype)
+    hl = hkv if per_kv else hq
+    rng = np.random.default_rng(91)
+    lut = np.full((b, hl, nq, nq), -1, dtype=np.int32)
+    cnt = np.zeros((b, hl, nq), dtype=np.int32)
+    for ib in range(b):
+        for ih in range(hl):
+            for qb in range(nq):
+                if qb < nq - 1 and rng.random() < 0.2:
+                    sel = np.array([rng.integers(qb + 1, nq)])          # future only
+                else:
+                    m = int(rng.integers(1, nq + 1))
+                    sel = np.sort(rng.choice(nq, size=m, replace=False))
+                lut[ib, ih, qb, :len(sel)] = sel
+                cnt[ib, ih, qb] = len(sel)
+    lut_t = torch.from_numpy(lut).to(dev)
+    cnt_t = torch.from_numpy(cnt).to(dev)
+    o, lse = ops.sparse_fmha_fwd(q, k, v, lut_t, cnt_t, causal=True)
+    torch.cuda.synchronize()
+    _causal_vs_oracle(q, k, v, lut_t, cnt_t, o, lse, per_kv=per_kv)
+    assert np.isneginf(np64(lse)).any()
+
+
+@pytest.mark.parametrize("splits", [2, 3])
+def test_causal_splits_then_combine(dev, splits):
+    case = synth.mid_case(dev)
+    bm = ops.build_block_map(case.q, case.k, case.topk, case.simthreshd1, causal=True)
+    op, lp = ops.sparse_fmha_fwd(case.q, case.k, case.v, bm["lut"], bm["count"], causal=True,
+                                 num_splits=splits)
+    o, lse = ops.attn_combine(op, lp, out_dtype=case.q.dtype)
+    torch.cuda.synchronize()
+    _causal_vs_oracle(case.q, case.k, case.v, bm["lut"], bm["count"], o, lse)

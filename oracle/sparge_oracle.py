@@ -395,6 +395,123 @@ def block_sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     return o, lse
 
 
+def pv_skip_units(scores: np.ndarray, tau: float, q_unit: int, k_unit: int,
+                  num_splits: int = 1) -> np.ndarray:
+    """Which P.V products the pv_threshold rule drops, for one Q-tile.
+
+    CK page, "Status vs Upstream": pv_threshold is a per-Q-tile skip inside the
+    attention kernel, a pure speed measure.  The pages give no test; reading
+    R25 takes the plainest one that leaves the result an approximation of the
+    same attention:
+
+    * the listed blocks are visited in LUT order, as by an online softmax,
+      split into `num_splits` consecutive chunks of ceil(n / num_splits)
+      blocks, each chunk a pass of its own (its running maximum starts at
+      -inf);
+    * the keys of every block are cut into streams of `k_unit` keys (key j of a
+      block is in stream j // k_unit) and the query rows into groups of
+      `q_unit`; each (row group, stream) keeps its own running maximum per row,
+      M_i = max of the scores of row i over that stream's keys of the blocks
+      visited so far in the pass, this block included;
+    * the unit (row group, stream, block) is skipped when every row i of the
+      group has r_i < M_i - tau, r_i its maximum score over the unit's keys.
+
+    q_unit = k_unit = 64 is the whole Q-tile against the whole block.  A row
+    with no key in the unit has r_i = -inf; while M_i is still -inf nothing is
+    skipped.
+
+    scores [rows, n_blocks, blk_k] (scaled, -inf where masked).  Returns a bool
+    array [rows // q_unit, n_blocks, blk_k // k_unit], True = skipped.
+    """
+    rows, n, blk_k = scores.shape
+    n_groups, n_streams = rows // q_unit, blk_k // k_unit
+    skip = np.zeros((n_groups, n, n_streams), dtype=bool)
+    if n == 0:
+        return skip
+    chunk = -(-n // num_splits)
+    for u in range(n_groups):
+        for g in range(n_streams):
+            part = scores[u * q_unit:(u + 1) * q_unit, :, g * k_unit:(g + 1) * k_unit]
+            r = part.max(axis=2)                            # [q_unit, n]
+            for t in range(n):
+                if t % chunk == 0:
+                    run = np.full(q_unit, NEG_INF)          # a new pass starts
+                run = np.maximum(run, r[:, t])
+                skip[u, t, g] = bool(np.all(r[:, t] < run - tau))
+    return skip
+
+
+def block_sparse_attention_pv_skip(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                                   lut: Optional[np.ndarray], count: Optional[np.ndarray],
+                                   pv_threshold: float, q_unit: int = 64, k_unit: int = 64,
+                                   num_splits: int = 1, scale: Optional[float] = None,
+                                   lut_per_kv_head: bool = False, causal: bool = False,
+                                   return_skips: bool = False):
+    """block_sparse_attention with the pv_threshold skip (reading R25).
+
+    A skipped unit's keys still count in each row's softmax denominator and in
+    its LSE; only their P.V terms leave the numerator:
+        O_i = sum_{j kept} exp(s_ij - m_i) v_j / sum_{j all} exp(s_ij - m_i),
+        LSE_i = m_i + ln sum_{j all} exp(s_ij - m_i),
+    with m_i the maximum over all of row i's keys.  The LSE therefore equals the
+    exact one, and |O_i - O_exact,i| <= (skipped keys of row i) * exp(-tau) *
+    max |v|, since every skipped score lies more than tau below m_i.  The blocks
+    of 64 queries and 64 keys are the ones of block_sparse_attention.
+    With `return_skips`, also returns the number of skipped units and of all
+    units.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    b, h_q, s_q, d = q.shape
+    h_kv, s_k = k.shape[1], k.shape[2]
+    ratio = h_q // h_kv
+    blk = 64
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nq, nk = s_q // blk, s_k // blk
+    o = np.zeros((b, h_q, s_q, v.shape[3]))
+    lse = np.zeros((b, h_q, s_q))
+    n_skip = n_units = 0
+    for ib in range(b):
+        for ih in range(h_q):
+            hk = ih // ratio
+            hl = hk if lut_per_kv_head else ih
+            for qb in range(nq):
+                if lut is None:
+                    blocks = np.arange(nk)
+                else:
+                    blocks = np.asarray(lut[ib, hl, qb, :int(count[ib, hl, qb])], dtype=np.int64)
+                rows = slice(qb * blk, (qb + 1) * blk)
+                n = len(blocks)
+                if n == 0:
+                    o[ib, ih, rows], lse[ib, ih, rows] = 0.0, NEG_INF
+                    continue
+                idx = (blocks[:, None] * blk + np.arange(blk)[None, :]).reshape(-1)
+                s = scale * (q[ib, ih, rows] @ k[ib, hk, idx].T)          # [64, n * 64]
+                if causal:
+                    qpos = np.arange(qb * blk, (qb + 1) * blk)
+                    s = np.where(idx[None, :] <= qpos[:, None], s, NEG_INF)
+                skip = pv_skip_units(s.reshape(blk, n, blk), pv_threshold, q_unit, k_unit,
+                                     num_splits)
+                n_skip += int(skip.sum())
+                n_units += skip.size
+                # kept[i, t, j]: key j of block t stays in row i's numerator
+                kept = ~np.repeat(np.repeat(skip, q_unit, axis=0), k_unit, axis=2)
+                m = s.max(axis=1, keepdims=True)
+                empty = m[:, 0] == NEG_INF
+                m = np.where(empty[:, None], 0.0, m)
+                e = np.exp(s - m)
+                l = e.sum(axis=1, keepdims=True)
+                l_safe = np.where(empty[:, None], 1.0, l)
+                num = (e * kept.reshape(blk, n * blk)) @ v[ib, hk, idx]
+                o[ib, ih, rows] = np.where(empty[:, None], 0.0, num / l_safe)
+                lse[ib, ih, rows] = np.where(empty, NEG_INF, (m + np.log(l_safe))[:, 0])
+    if return_skips:
+        return o, lse, n_skip, n_units
+    return o, lse
+
+
 def token_list_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                          lists: np.ndarray, scale: Optional[float] = None):
     """Decode-style attention over per-(b, KV head) token index lists.

@@ -224,6 +224,18 @@ def extras(ops, synth, torch, steps, warmup):
         dense_causal_ms=median(dt), dense_causal_pairs=dense_pairs,
         dense_causal_tflops_computed=dense_pairs * F_BLK / median(dt) / 1e9,
         speedup_vs_dense_step=median(dt) / (median(bmt) + median(ft)))
+    # pv_threshold at the headline shape (plain block map, topk 0.4): the same
+    # FMHA with no skip and with thresholds of 4 and 8 nats.
+    bm = ops.build_block_map(hc.q, hc.k, hc.topk, hc.simthreshd1, out=ws)
+    pv = {}
+    for tau in (0.0, 4.0, 8.0):
+        _, t = time_arm(lambda: ops.sparse_fmha_fwd(hc.q, hc.k, hc.v, bm["lut"], bm["count"], o=o, lse=l,
+                                                    pv_threshold=tau), steps, warmup, torch)
+        pv[tau] = median(t)
+    out["pv_skip_headline"] = dict(
+        workload="b2 h32 s16384 d128 fp16, topk 0.4, pv_threshold 0 / 4 / 8",
+        fmha_ms_no_skip=pv[0.0], fmha_ms_tau4=pv[4.0], fmha_ms_tau8=pv[8.0],
+        speedup_tau4=pv[0.0] / pv[4.0], speedup_tau8=pv[0.0] / pv[8.0])
     del hc, bm, o, l, ws
     return out
 

@@ -83,7 +83,7 @@ BlockMapLayout block_map_layout(int b, int h, int s_q, int s_k, int d) {
 
 extern "C" {
 
-int sparge_abi_version(void) { return 2; }
+int sparge_abi_version(void) { return 3; }
 
 const char* sparge_last_error(void) { return g_error.c_str(); }
 
@@ -195,8 +195,8 @@ sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void*
                               int s_k, int d, const int64_t q_strides[3], const int64_t k_strides[3],
                               const int64_t v_strides[3], const int64_t o_strides[3], int blk_q,
                               int blk_k, const int32_t* lut, const int32_t* lut_count, int lut_row_len,
-                              int lut_heads, float softmax_scale, unsigned flags, int num_splits,
-                              int64_t o_split_stride, void* stream) {
+                              int lut_heads, float softmax_scale, unsigned flags, float pv_threshold,
+                              int num_splits, int64_t o_split_stride, void* stream) {
   if (!q || !k || !v || !o) return fail(SPARGE_ERR_INVALID, "q, k, v and o must be non-null");
   if (!is_half(dt)) return fail(SPARGE_ERR_UNSUPPORTED, "input dtype must be F16 or BF16");
   if (o_dt != dt && o_dt != SPARGE_F32)
@@ -225,6 +225,10 @@ sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void*
   if (flags & ~SPARGE_FLAG_CAUSAL)
     return fail(SPARGE_ERR_INVALID, "sparse_fmha_fwd takes only SPARGE_FLAG_CAUSAL (flags 0x%x)", flags);
   const bool causal = (flags & SPARGE_FLAG_CAUSAL) != 0;
+  if (!(pv_threshold >= 0.f) || !isfinite(pv_threshold))
+    return fail(SPARGE_ERR_INVALID, "pv_threshold must be finite and >= 0");
+  if (pv_threshold > 0.f && token_mode)
+    return fail(SPARGE_ERR_UNSUPPORTED, "pv_threshold applies to block mode only");
   if (causal && token_mode) return fail(SPARGE_ERR_INVALID, "causal masking applies to block mode only");
   if (causal && s_q != s_k)
     return fail(SPARGE_ERR_UNSUPPORTED, "causal attention needs s_q = s_k (got %d, %d)", s_q, s_k);
@@ -247,6 +251,7 @@ sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void*
   a.splits = num_splits;
   a.o_split_stride = num_splits > 1 ? o_split_stride : 0;
   a.causal = causal ? 1 : 0;
+  a.pv_tau2 = pv_threshold * 1.4426950408889634f;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   if (block_mode) {

@@ -27,6 +27,8 @@ constexpr int kWave = 64;
 struct F16 {
   typedef half_t T;
   typedef half8 V8;
+  // The attention row sum may add P after rounding to this type.
+  static constexpr bool kRowSumRounded = true;
   static __device__ __forceinline__ float to_f(T x) { return (float)x; }
   static __device__ __forceinline__ T from_f(float x) { return (T)x; }
   // Convert the low / high 16-bit lane of a packed word.
@@ -54,6 +56,7 @@ struct F16 {
 struct BF16 {
   typedef bf16_t T;
   typedef bf16x8 V8;
+  static constexpr bool kRowSumRounded = false;
   static __device__ __forceinline__ float to_f(T x) { return (float)x; }
   static __device__ __forceinline__ T from_f(float x) { return (T)x; }
   static __device__ __forceinline__ float lo(uint32_t w) {

@@ -21,6 +21,11 @@
 //     page: one FMA per score, exp2), and the row sum is finished only at the
 //     end (one reciprocal per row);
 //   * the two key halves of a tile are merged at the end with the LSE rule;
+//   * with a pv_threshold (CK page, "Status vs Upstream": a per-Q-tile skip
+//     in the attention kernel), a wavefront drops the PV product of a block
+//     when each of its 32 query rows scores, over the wavefront's 32 keys,
+//     more than the threshold below that row's running maximum over the keys
+//     of its half seen so far in the pass; those P still count in the row sum;
 //   * workgroups are renumbered so that consecutive rows of one head land on
 //     one XCD and share its L2 (aiter 4919 page: workgroups round-robin over
 //     the 8 XCDs by linear id).
@@ -143,7 +148,7 @@ struct Buf {
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <class E, int D, bool OUT_F32, bool CAUSAL>
+template <class E, int D, bool OUT_F32, bool CAUSAL, bool PVSKIP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fmha_block_kernel(FmhaArgs a) {
   typedef typename E::T T;
@@ -256,6 +261,7 @@ void fmha_block_kernel(FmhaArgs a) {
   for (int i = 0; i < NMD; ++i) acc_o[i] = floatx16{};
   float m_run = -INFINITY;   // reference maximum, already times scale*log2(e)
   float l_run = 0.f;         // this lane's share of the row sum
+  float m_top = -INFINITY;   // exact running maximum (pv_threshold test), same units
   const float c2 = a.scale_log2;
   const int krow = 32 * kh + l32;                  // K row this lane feeds to S^T
   const int kswz = krow % G16;
@@ -342,6 +348,7 @@ void fmha_block_kernel(FmhaArgs a) {
     for (int r = 1; r < 16; ++r) rmax = fmaxf(rmax, s[r]);
     rmax = half_swap_max(rmax);
     const float m_cand = rmax * c2;
+    if constexpr (PVSKIP) m_top = fmaxf(m_top, m_cand);
     const bool need = m_cand > m_run + kRescaleSlack;
     if (__any(need)) {
       const float m_new = need ? m_cand : m_run;
@@ -352,7 +359,10 @@ void fmha_block_kernel(FmhaArgs a) {
       for (int i = 0; i < NMD; ++i) acc_o[i] *= alpha;
     }
     // P^T fragments (k-step ks uses registers 8ks .. 8ks+7), rounded to the
-    // input type; the row sum adds the rounded values, the ones PV uses.
+    // input type.  With fp16 the row sum adds the rounded values, the ones PV
+    // uses (rounding moves a term by at most 2^-11 of itself).  bf16 rounds by
+    // up to 2^-8, which on a row dominated by one key would move the LSE by up
+    // to 4e-3 nats, so there the row sum adds the fp32 values.
     // Causal rows may still have no key (m_run = -inf): their P is 0.
     const float mref = CAUSAL && m_run == -INFINITY ? 0.f : m_run;
     u32x4 pf[2];
@@ -363,15 +373,21 @@ void fmha_block_kernel(FmhaArgs a) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w], c2, -mref));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w + 1], c2, -mref));
         pf[ks][w] = E::pack2(p0, p1);
-        l_run = E::sum2(pf[ks][w], l_run);
+        if constexpr (E::kRowSumRounded) l_run = E::sum2(pf[ks][w], l_run);
+        else l_run += p0 + p1;
       }
     }
 
-    // O^T += V^T P^T over this wave's 32 keys.
+    // O^T += V^T P^T over this wave's 32 keys, unless every query row of the
+    // wave lies more than the threshold below its running maximum.
+    bool pv = true;
+    if constexpr (PVSKIP) pv = __any(!(m_cand < m_top - a.pv_tau2));
+    if (pv) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int md = 0; md < NMD; ++md) acc_o[md] = mfma32<E>(vf[ks][md], pf[ks], acc_o[md]);
+        for (int md = 0; md < NMD; ++md) acc_o[md] = mfma32<E>(vf[ks][md], pf[ks], acc_o[md]);
+      }
     }
 
     // The LUT entry of block it+3 is requested only now, after this block's
@@ -666,17 +682,23 @@ __global__ __launch_bounds__(256) void fmha_tokens_kernel(FmhaArgs a) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+template <class E, int D, bool PVSKIP>
+static void launch_block_v(const FmhaArgs& a, bool out_f32, dim3 grid, hipStream_t st) {
+  if (a.causal) {
+    if (out_f32) hipLaunchKernelGGL((fmha_block_kernel<E, D, true, true, PVSKIP>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((fmha_block_kernel<E, D, false, true, PVSKIP>), grid, dim3(256), 0, st, a);
+  } else {
+    if (out_f32) hipLaunchKernelGGL((fmha_block_kernel<E, D, true, false, PVSKIP>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((fmha_block_kernel<E, D, false, false, PVSKIP>), grid, dim3(256), 0, st, a);
+  }
+}
+
 template <class E, int D>
 static hipError_t launch_block_t(const FmhaArgs& a, bool out_f32, hipStream_t st) {
   const int64_t G = (int64_t)a.nqt * a.hq * a.b * a.splits;
   const dim3 grid((unsigned)(((G + 7) / 8) * 8));
-  if (a.causal) {
-    if (out_f32) hipLaunchKernelGGL((fmha_block_kernel<E, D, true, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((fmha_block_kernel<E, D, false, true>), grid, dim3(256), 0, st, a);
-  } else {
-    if (out_f32) hipLaunchKernelGGL((fmha_block_kernel<E, D, true, false>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((fmha_block_kernel<E, D, false, false>), grid, dim3(256), 0, st, a);
-  }
+  if (a.pv_tau2 > 0.f) launch_block_v<E, D, true>(a, out_f32, grid, st);
+  else launch_block_v<E, D, false>(a, out_f32, grid, st);
   return hipGetLastError();
 }
 

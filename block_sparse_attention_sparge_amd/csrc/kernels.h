@@ -68,6 +68,7 @@ struct FmhaArgs {
   int splits;
   int64_t o_split_stride;  // elements
   int causal;              // block mode: key j > query i masked
+  float pv_tau2;           // block mode: pv_threshold * log2(e); 0 = no PV skip
 };
 
 struct CombineArgs {

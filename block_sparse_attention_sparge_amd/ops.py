@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libsparge.so")
 SPARGE_OK, SPARGE_ERR_INVALID, SPARGE_ERR_UNSUPPORTED, SPARGE_ERR_HIP = 0, 1, 2, 3
 SPARGE_F16, SPARGE_BF16, SPARGE_F32 = 0, 1, 2
 SPARGE_FLAG_SMOOTH_K, SPARGE_FLAG_CAUSAL, SPARGE_FLAG_ATTN_SINK = 1, 2, 4
-ABI_VERSION = 2
+ABI_VERSION = 3
 MAX_HEADS = 128
 MAX_KBLOCKS = 1024
 
@@ -81,7 +81,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         lib.sparse_fmha_fwd.restype = _i
         lib.sparse_fmha_fwd.argtypes = [
             _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
-            _I64x3, _I64x3, _I64x3, _I64x3, _i, _i, _p, _p, _i, _i, _f, _u, _i, _i64, _p]
+            _I64x3, _I64x3, _I64x3, _I64x3, _i, _i, _p, _p, _i, _i, _f, _u, _f, _i, _i64, _p]
         lib.attn_combine.restype = _i
         lib.attn_combine.argtypes = [_p, _i, _p, _i, _i, _i, _i, _i, _i64, _p, _i, _p, _p]
         lib.sparge_validate_lut.restype = _i
@@ -225,14 +225,16 @@ def sparse_fmha_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                     blk_q: int = 64, blk_k: int = 64, softmax_scale: float = 0.0,
                     num_splits: int = 1, out_dtype: Optional[torch.dtype] = None,
                     o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                    return_lse: bool = True, causal: bool = False):
+                    return_lse: bool = True, causal: bool = False, pv_threshold: float = 0.0):
     """Stage 2 (sparse_fmha_fwd).  q [b, h_q, s_q, d]; k, v [b, h_kv, s_k, d].
 
     Block mode (64, 64): lut [b, h_lut, s_q/64, L] (+ count [b, h_lut, s_q/64]);
     lut None = dense.  Token mode (1, 1): lut [b, h_kv, L] token positions.
     With num_splits > 1 the outputs are partials o [S, b, h_q, s_q, d] and
     lse [S, b, h_q, s_q] (fp32 unless out_dtype says otherwise).  causal sets
-    SPARGE_FLAG_CAUSAL (block mode, s_q = s_k).  Returns (o, lse).
+    SPARGE_FLAG_CAUSAL (block mode, s_q = s_k).  pv_threshold > 0 lets the
+    kernel skip the P.V product of 32x32 units scoring more than that far
+    below their running maximum (block mode).  Returns (o, lse).
     """
     lib = load_library()
     dev = _on_gpu(q, k, v, lut, count, o, lse)
@@ -266,7 +268,8 @@ def sparse_fmha_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dt(q.dtype), _dt(o.dtype),
         b, h_q, h_kv, s_q, s_k, d, _strides(q), _strides(k), _strides(v), _strides(o4),
         blk_q, blk_k, _ptr(lut), _ptr(count), lut_row_len, lut_heads, float(softmax_scale),
-        _flags(causal=causal), int(num_splits), int(split_stride), _stream(dev))
+        _flags(causal=causal), float(pv_threshold), int(num_splits), int(split_stride),
+        _stream(dev))
     _check(st)
     return o, lse
 

@@ -69,7 +69,7 @@ typedef enum {
 #define SPARGE_FLAG_CAUSAL 2u     /* block map and block-mode FMHA: causal masks   */
 #define SPARGE_FLAG_ATTN_SINK 4u  /* block map: K block 0 selected in every row    */
 
-/* Library ABI version (this header: 2). */
+/* Library ABI version (this header: 3). */
 int sparge_abi_version(void);
 
 /* Message for the last failed call on this thread ("" if none). */
@@ -180,6 +180,19 @@ size_t sparge_build_block_map_workspace(int b, int h, int s_q, int s_k, int d,
  * attends only to keys j <= i; listed blocks past the tile add nothing, and a
  * row left with no key gives O = 0, LSE = -inf.  In dense mode (lut = NULL)
  * the tile of rows [64 qt, 64 qt + 64) reads blocks 0..qt.
+ *
+ * pv_threshold (block mode; CK page, "Status vs Upstream": pv_threshold, a
+ * per-Q-tile skip in the attention kernel): 0 = off.  A value tau > 0 drops
+ * P.V products that cannot matter much.  Each chunk's blocks are visited in
+ * list order; a block pair is cut into four units of 32 query rows x 32 keys
+ * (keys 64 kb + [0, 32) and 64 kb + [32, 64)); for each unit and each of its
+ * rows i, M_i is the running maximum of s over that key half of the blocks
+ * visited so far in the chunk, this one included, and r_i the maximum of s
+ * over the unit's keys (-inf where masked).  The unit's P.V product is
+ * skipped when r_i < M_i - tau for all 32 rows.  Skipped keys still count in
+ * the softmax denominator and in LSE: LSE is the exact one, and O_i moves by
+ * at most (skipped keys of row i) * exp(-tau) * max |v|.  The decision is
+ * taken in fp32.  tau must be finite and >= 0; token-list mode takes 0 only.
  */
 sparge_status sparse_fmha_fwd(
     const void* q, const void* k, const void* v, void* o, float* lse,
@@ -189,8 +202,8 @@ sparge_status sparse_fmha_fwd(
     const int64_t v_strides[3], const int64_t o_strides[3],
     int blk_q, int blk_k,
     const int32_t* lut, const int32_t* lut_count, int lut_row_len, int lut_heads,
-    float softmax_scale, unsigned flags, int num_splits, int64_t o_split_stride,
-    void* stream);
+    float softmax_scale, unsigned flags, float pv_threshold,
+    int num_splits, int64_t o_split_stride, void* stream);
 
 /*
  * LSE combine of n_parts partial results.  (Updating Log page, Stage 1:

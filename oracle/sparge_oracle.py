@@ -396,7 +396,7 @@ def block_sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
 
 
 def pv_skip_units(scores: np.ndarray, tau: float, q_unit: int, k_unit: int,
-                  num_splits: int = 1) -> np.ndarray:
+                  num_splits: int = 1, return_margin: bool = False):
     """Which P.V products the pv_threshold rule drops, for one Q-tile.
 
     CK page, "Status vs Upstream": pv_threshold is a per-Q-tile skip inside the
@@ -421,13 +421,16 @@ def pv_skip_units(scores: np.ndarray, tau: float, q_unit: int, k_unit: int,
     skipped.
 
     scores [rows, n_blocks, blk_k] (scaled, -inf where masked).  Returns a bool
-    array [rows // q_unit, n_blocks, blk_k // k_unit], True = skipped.
+    array [rows // q_unit, n_blocks, blk_k // k_unit], True = skipped.  With
+    `return_margin`, also max_i (r_i - (M_i - tau)) per unit over the rows with
+    a key in the unit (-inf if none): how far the decision is from flipping.
     """
     rows, n, blk_k = scores.shape
     n_groups, n_streams = rows // q_unit, blk_k // k_unit
     skip = np.zeros((n_groups, n, n_streams), dtype=bool)
+    margin = np.full((n_groups, n, n_streams), NEG_INF)
     if n == 0:
-        return skip
+        return (skip, margin) if return_margin else skip
     chunk = -(-n // num_splits)
     for u in range(n_groups):
         for g in range(n_streams):
@@ -438,7 +441,10 @@ def pv_skip_units(scores: np.ndarray, tau: float, q_unit: int, k_unit: int,
                     run = np.full(q_unit, NEG_INF)          # a new pass starts
                 run = np.maximum(run, r[:, t])
                 skip[u, t, g] = bool(np.all(r[:, t] < run - tau))
-    return skip
+                live = r[:, t] > NEG_INF
+                if live.any():
+                    margin[u, t, g] = float(np.max(r[live, t] - (run[live] - tau)))
+    return (skip, margin) if return_margin else skip
 
 
 def block_sparse_attention_pv_skip(q: np.ndarray, k: np.ndarray, v: np.ndarray,
@@ -446,7 +452,7 @@ def block_sparse_attention_pv_skip(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                                    pv_threshold: float, q_unit: int = 64, k_unit: int = 64,
                                    num_splits: int = 1, scale: Optional[float] = None,
                                    lut_per_kv_head: bool = False, causal: bool = False,
-                                   return_skips: bool = False):
+                                   return_skips: bool = False, return_margins: bool = False):
     """block_sparse_attention with the pv_threshold skip (reading R25).
 
     A skipped unit's keys still count in each row's softmax denominator and in
@@ -458,7 +464,9 @@ def block_sparse_attention_pv_skip(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     max |v|, since every skipped score lies more than tau below m_i.  The blocks
     of 64 queries and 64 keys are the ones of block_sparse_attention.
     With `return_skips`, also returns the number of skipped units and of all
-    units.
+    units; with `return_margins`, then [b, h_q, nq, 64 // q_unit] the smallest
+    |margin| (pv_skip_units) of the row group's units: decisions closer than
+    rounding to the threshold may fall either way in another precision.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -473,6 +481,7 @@ def block_sparse_attention_pv_skip(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     o = np.zeros((b, h_q, s_q, v.shape[3]))
     lse = np.zeros((b, h_q, s_q))
     n_skip = n_units = 0
+    near = np.full((b, h_q, nq, blk // q_unit), math.inf)
     for ib in range(b):
         for ih in range(h_q):
             hk = ih // ratio
@@ -492,8 +501,9 @@ def block_sparse_attention_pv_skip(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                 if causal:
                     qpos = np.arange(qb * blk, (qb + 1) * blk)
                     s = np.where(idx[None, :] <= qpos[:, None], s, NEG_INF)
-                skip = pv_skip_units(s.reshape(blk, n, blk), pv_threshold, q_unit, k_unit,
-                                     num_splits)
+                skip, margin = pv_skip_units(s.reshape(blk, n, blk), pv_threshold, q_unit,
+                                             k_unit, num_splits, return_margin=True)
+                near[ib, ih, qb] = np.abs(margin).min(axis=(1, 2))
                 n_skip += int(skip.sum())
                 n_units += skip.size
                 # kept[i, t, j]: key j of block t stays in row i's numerator
@@ -507,9 +517,12 @@ def block_sparse_attention_pv_skip(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                 num = (e * kept.reshape(blk, n * blk)) @ v[ib, hk, idx]
                 o[ib, ih, rows] = np.where(empty[:, None], 0.0, num / l_safe)
                 lse[ib, ih, rows] = np.where(empty, NEG_INF, (m + np.log(l_safe))[:, 0])
+    out = (o, lse)
     if return_skips:
-        return o, lse, n_skip, n_units
-    return o, lse
+        out += (n_skip, n_units)
+    if return_margins:
+        out += (near,)
+    return out
 
 
 def token_list_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert lib.sparge_abi_version() == ops.ABI_VERSION == 2
+    assert lib.sparge_abi_version() == ops.ABI_VERSION == 3
 
 
 def _s3(a, b, c):
@@ -118,12 +118,12 @@ def _fmha(lib, **kw):
              b=1, hq=8, hkv=2, sq=512, sk=512, d=128, qs=_s3(8 * 512 * 128, 512 * 128, 128),
              ks=_s3(2 * 512 * 128, 512 * 128, 128), vs=_s3(2 * 512 * 128, 512 * 128, 128),
              os=_s3(8 * 512 * 128, 512 * 128, 128), bq=64, bk=64, lut=FAKE, cnt=FAKE, L=8,
-             lh=8, scale=0.0, flags=0, splits=1, sst=0)
+             lh=8, scale=0.0, flags=0, pv=0.0, splits=1, sst=0)
     a.update(kw)
     return lib.sparse_fmha_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dt"], a["odt"], a["b"],
                                a["hq"], a["hkv"], a["sq"], a["sk"], a["d"], a["qs"], a["ks"], a["vs"],
                                a["os"], a["bq"], a["bk"], a["lut"], a["cnt"], a["L"], a["lh"],
-                               a["scale"], a["flags"], a["splits"], a["sst"], None)
+                               a["scale"], a["flags"], a["pv"], a["splits"], a["sst"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -151,6 +151,10 @@ def _fmha(lib, **kw):
     (dict(flags=ops.SPARGE_FLAG_SMOOTH_K), ops.SPARGE_ERR_INVALID),                  # block-map flag only
     (dict(flags=ops.SPARGE_FLAG_CAUSAL, sk=1024), ops.SPARGE_ERR_UNSUPPORTED),       # causal, s_q != s_k
     (dict(flags=ops.SPARGE_FLAG_CAUSAL, bq=1, bk=1, cnt=None, lh=2), ops.SPARGE_ERR_INVALID),   # token mode
+    (dict(pv=-1.0), ops.SPARGE_ERR_INVALID),
+    (dict(pv=float("inf")), ops.SPARGE_ERR_INVALID),
+    (dict(pv=float("nan")), ops.SPARGE_ERR_INVALID),
+    (dict(pv=4.0, bq=1, bk=1, cnt=None, lh=2), ops.SPARGE_ERR_UNSUPPORTED),   # token mode
     # token-list mode
     (dict(bq=1, bk=1, lut=None, cnt=None), ops.SPARGE_ERR_INVALID),
     (dict(bq=1, bk=1, cnt=FAKE, lh=2), ops.SPARGE_ERR_INVALID),

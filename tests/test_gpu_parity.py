@@ -343,6 +343,20 @@ def test_fmha_long_rows(dev):
     _fmha_vs_oracle(q, k, v, lut, cnt, o2, l2)
 
 
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_fmha_lse_on_rows_dominated_by_one_key(dev, dtype):
+    # 4 N(0, 1) queries against N(0, 1) keys at d = 64: scores have a spread of
+    # 4, so most rows are carried by one or two keys.  Rounding P to bf16
+    # before the row sum would move such a row's LSE by up to 2^-8 (4e-3 nats).
+    b, h, s, d = 1, 2, 1024, 64
+    q = synth.normal((b, h, s, d), 15, 1, dtype, dev, scale=4.0)
+    k = synth.normal((b, h, s, d), 15, 2, dtype, dev)
+    v = synth.normal((b, h, s, d), 15, 3, dtype, dev)
+    o, lse = ops.dense_fmha_fwd(q, k, v)
+    _sync()
+    _fmha_vs_oracle(q, k, v, None, None, o, lse)
+
+
 def test_determinism_relaunch(dev):
     case = synth.mid_case(dev)
     ref_bm = ops.build_block_map(case.q, case.k, case.topk, case.simthreshd1, return_debug=True)

@@ -525,6 +525,62 @@ def block_sparse_attention_pv_skip(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     return out
 
 
+def quantize_block_int8(x_blk: np.ndarray):
+    """Symmetric int8 codes of one block of tokens, with one fp32 scale.
+
+    CK page, "Status vs Upstream", not-yet-ported list: Q/K int8 quantisation
+    fused into the pool kernel, feeding an int8 QK GEMM in the attention
+    kernel.  The pages give no formula.  Reading R27: the block is the
+    64-token pooling block; scale = absmax / 127 and
+    code = round-half-even(x * (127 / absmax)), clamped to [-127, 127], each
+    operation in fp32 (the codes are integers decided by floating point, so
+    the oracle takes the decision in the kernel's precision).  An all-zero
+    block has scale 0 and codes 0.  x_blk holds values exact in fp32 (the
+    fp16 / bf16 inputs).  Returns (int8 codes, np.float32 scale).
+    """
+    x = np.asarray(x_blk, np.float32)
+    amax = np.float32(np.abs(x).max()) if x.size else np.float32(0)
+    if amax == 0:
+        return np.zeros(x.shape, np.int8), np.float32(0)
+    inv = np.float32(127) / amax
+    codes = np.clip(np.rint(x * inv), -127, 127).astype(np.int8)
+    return codes, amax / np.float32(127)
+
+
+def quantize_int8(x: np.ndarray, blk: int = 64):
+    """quantize_block_int8 over every block of `blk` tokens of x [b, h, s, d].
+    Returns codes [b, h, s, d] int8 and scales [b, h, s // blk] fp32."""
+    b, h, s, d = x.shape
+    codes = np.zeros((b, h, s, d), np.int8)
+    scales = np.zeros((b, h, s // blk), np.float32)
+    for ib in range(b):
+        for ih in range(h):
+            for j in range(s // blk):
+                rows = slice(j * blk, (j + 1) * blk)
+                codes[ib, ih, rows], scales[ib, ih, j] = quantize_block_int8(x[ib, ih, rows])
+    return codes, scales
+
+
+def dequantize_int8(codes: np.ndarray, scales: np.ndarray, blk: int = 64) -> np.ndarray:
+    """codes * scale of their block, in fp64 (exact: an int8 times an fp32)."""
+    return codes.astype(np.float64) * np.repeat(scales.astype(np.float64), blk, axis=2)[..., None]
+
+
+def block_sparse_attention_qk_int8(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                                   lut: Optional[np.ndarray], count: Optional[np.ndarray],
+                                   scale: Optional[float] = None, lut_per_kv_head: bool = False,
+                                   causal: bool = False):
+    """block_sparse_attention with Q and K replaced by their int8 block codes
+    times their scales (reading R27): scores are scale * sq * sk * (cq . ck),
+    everything after them as in block_sparse_attention (V unquantised)."""
+    cq, sq = quantize_int8(q)
+    ck, sk = quantize_int8(k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[3])
+    return block_sparse_attention(dequantize_int8(cq, sq), dequantize_int8(ck, sk), v, lut, count,
+                                  scale=scale, lut_per_kv_head=lut_per_kv_head, causal=causal)
+
+
 def token_list_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                          lists: np.ndarray, scale: Optional[float] = None):
     """Decode-style attention over per-(b, KV head) token index lists.

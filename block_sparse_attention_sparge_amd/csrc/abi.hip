@@ -83,7 +83,7 @@ BlockMapLayout block_map_layout(int b, int h, int s_q, int s_k, int d) {
 
 extern "C" {
 
-int sparge_abi_version(void) { return 3; }
+int sparge_abi_version(void) { return 4; }
 
 const char* sparge_last_error(void) { return g_error.c_str(); }
 
@@ -98,8 +98,8 @@ sparge_status sparge_build_block_map(
     const int64_t q_strides[3], const int64_t k_strides[3], int blk_q, int blk_k,
     const float* topk, const float* cdfthreshd, const float* simthreshd1, float softmax_scale,
     unsigned flags, int32_t* lut, int32_t* lut_count, uint8_t* block_map, float* pooled_prob, uint8_t* sim_q,
-    uint8_t* sim_k, float* q_mean, float* k_mean, void* workspace, size_t workspace_bytes,
-    void* stream) {
+    uint8_t* sim_k, float* q_mean, float* k_mean, int8_t* q_i8, float* q_i8_scale, int8_t* k_i8,
+    float* k_i8_scale, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k) return fail(SPARGE_ERR_INVALID, "q and k must be non-null");
   if (!lut || !lut_count) return fail(SPARGE_ERR_INVALID, "lut and lut_count must be non-null");
   if (!topk || !simthreshd1) return fail(SPARGE_ERR_INVALID, "topk and simthreshd1 must be non-null");
@@ -132,6 +132,11 @@ sparge_status sparge_build_block_map(
   if (((uintptr_t)workspace & 255u) != 0) return fail(SPARGE_ERR_INVALID, "workspace must be 256-byte aligned");
   if ((q_mean && ((uintptr_t)q_mean & 15u)) || (k_mean && ((uintptr_t)k_mean & 15u)))
     return fail(SPARGE_ERR_INVALID, "q_mean/k_mean must be 16-byte aligned");
+  const int n_i8 = (q_i8 != nullptr) + (q_i8_scale != nullptr) + (k_i8 != nullptr) + (k_i8_scale != nullptr);
+  if (n_i8 != 0 && n_i8 != 4)
+    return fail(SPARGE_ERR_INVALID, "q_i8, q_i8_scale, k_i8 and k_i8_scale go together (all or none)");
+  if (n_i8 && (!aligned16(q_i8) || !aligned16(k_i8)))
+    return fail(SPARGE_ERR_INVALID, "q_i8/k_i8 must be 16-byte aligned");
 
   PoolArgs pa;
   SelectArgs sa;
@@ -170,6 +175,7 @@ sparge_status sparge_build_block_map(
   pa.km_part = smooth ? reinterpret_cast<float*>(ws + lay.km_part) : nullptr;
   pa.km_chunks = lay.km_chunks;
   pa.km_scale = 1.0f / (float)s_k;
+  pa.q_i8 = q_i8; pa.k_i8 = k_i8; pa.q_i8_scale = q_i8_scale; pa.k_i8_scale = k_i8_scale;
 
   sa.q_mean = pa.q_mean; sa.k_mean = pa.k_mean; sa.sim_q = pa.sim_q; sa.sim_k = pa.sim_k;
   sa.b = b; sa.h = h; sa.nq = nq; sa.nk = nk;
@@ -252,6 +258,7 @@ sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void*
   a.o_split_stride = num_splits > 1 ? o_split_stride : 0;
   a.causal = causal ? 1 : 0;
   a.pv_tau2 = pv_threshold * 1.4426950408889634f;
+  a.q_scale = nullptr; a.k_scale = nullptr;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   if (block_mode) {
@@ -277,6 +284,77 @@ sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void*
   a.nqt = s_q;
   a.nkb = s_k;
   return hip_status(launch_fmha_tokens(a, dt, o_dt, d, rows, s), "sparse_fmha token launch");
+}
+
+sparge_status sparse_fmha_fwd_qk_int8(const int8_t* q, const float* q_scale, const int8_t* k,
+                                      const float* k_scale, const void* v, void* o, float* lse,
+                                      sparge_dtype v_dt, sparge_dtype o_dt, int b, int h_q, int h_kv, int s_q,
+                                      int s_k, int d, const int64_t q_strides[3], const int64_t k_strides[3],
+                                      const int64_t v_strides[3], const int64_t o_strides[3], const int32_t* lut,
+                                      const int32_t* lut_count, int lut_row_len, int lut_heads,
+                                      float softmax_scale, unsigned flags, int num_splits,
+                                      int64_t o_split_stride, void* stream) {
+  if (!q || !k || !v || !o || !q_scale || !k_scale)
+    return fail(SPARGE_ERR_INVALID, "q, q_scale, k, k_scale, v and o must be non-null");
+  if (!is_half(v_dt)) return fail(SPARGE_ERR_UNSUPPORTED, "v dtype must be F16 or BF16");
+  if (o_dt != v_dt && o_dt != SPARGE_F32)
+    return fail(SPARGE_ERR_UNSUPPORTED, "output dtype must equal the v dtype or be F32");
+  if (b <= 0 || h_q <= 0 || h_kv <= 0 || s_q <= 0 || s_k <= 0 || d <= 0)
+    return fail(SPARGE_ERR_INVALID, "sizes must be positive");
+  if (h_q % h_kv != 0) return fail(SPARGE_ERR_INVALID, "h_q=%d is not a multiple of h_kv=%d", h_q, h_kv);
+  if (d != 64 && d != 128) return fail(SPARGE_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", d);
+  if (s_q % 64 || s_k % 64)
+    return fail(SPARGE_ERR_UNSUPPORTED, "ragged sequence (s_q=%d, s_k=%d) is not a multiple of 64", s_q, s_k);
+  sparge_status st;
+  if ((st = check_strides("q", q_strides)) != SPARGE_OK) return st;
+  if ((st = check_strides("k", k_strides)) != SPARGE_OK) return st;
+  if ((st = check_strides("v", v_strides)) != SPARGE_OK) return st;
+  if ((st = check_strides("o", o_strides)) != SPARGE_OK) return st;
+  if (q_strides[2] % 16 || k_strides[2] % 16)
+    return fail(SPARGE_ERR_INVALID, "int8 q/k row strides must be multiples of 16 bytes");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(SPARGE_ERR_INVALID, "q/k/v/o must be 16-byte aligned");
+  if (num_splits < 1 || num_splits > 1024) return fail(SPARGE_ERR_INVALID, "num_splits=%d out of [1, 1024]", num_splits);
+  if (num_splits > 1 && !lse) return fail(SPARGE_ERR_INVALID, "split partials need an lse output");
+  if (num_splits > 1 && (o_split_stride <= 0 || o_split_stride % 8))
+    return fail(SPARGE_ERR_INVALID, "o_split_stride must be a positive multiple of 8 elements");
+  if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale))
+    return fail(SPARGE_ERR_INVALID, "softmax_scale must be finite and >= 0");
+  if (flags & ~SPARGE_FLAG_CAUSAL)
+    return fail(SPARGE_ERR_INVALID, "sparse_fmha_fwd_qk_int8 takes only SPARGE_FLAG_CAUSAL (flags 0x%x)", flags);
+  const bool causal = (flags & SPARGE_FLAG_CAUSAL) != 0;
+  if (causal && s_q != s_k)
+    return fail(SPARGE_ERR_UNSUPPORTED, "causal attention needs s_q = s_k (got %d, %d)", s_q, s_k);
+  if (lut) {
+    if (lut_row_len <= 0) return fail(SPARGE_ERR_INVALID, "lut_row_len must be positive");
+    if (lut_heads != h_q && lut_heads != h_kv)
+      return fail(SPARGE_ERR_INVALID, "lut_heads=%d must be h_q=%d or h_kv=%d", lut_heads, h_q, h_kv);
+  } else if (lut_count) {
+    return fail(SPARGE_ERR_INVALID, "lut_count given without lut");
+  }
+  const int64_t span = std::max(64 * k_strides[2], 64 * v_strides[2] * 2);
+  if (span >= (int64_t(1) << 31))
+    return fail(SPARGE_ERR_UNSUPPORTED, "a 64-row K/V block spans %lld bytes (limit 2^31)", (long long)span);
+
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
+  FmhaArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = q_strides[i]; a.ks[i] = k_strides[i]; a.vs[i] = v_strides[i]; a.os[i] = o_strides[i];
+  }
+  a.b = b; a.hq = h_q; a.hkv = h_kv; a.sq = s_q; a.sk = s_k;
+  a.ratio = h_q / h_kv;
+  a.lut = lut; a.cnt = lut_count; a.lut_row_len = lut_row_len; a.lut_heads = lut_heads;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.splits = num_splits;
+  a.o_split_stride = num_splits > 1 ? o_split_stride : 0;
+  a.causal = causal ? 1 : 0;
+  a.pv_tau2 = 0.f;
+  a.q_scale = q_scale; a.k_scale = k_scale;
+  a.nqt = s_q / 64;
+  a.nkb = s_k / 64;
+  return hip_status(launch_fmha_qk8(a, v_dt, o_dt, d, reinterpret_cast<hipStream_t>(stream)),
+                    "sparse_fmha_qk_int8 launch");
 }
 
 sparge_status attn_combine(const void* o_parts, sparge_dtype part_dt, const float* lse_parts, int n_parts,

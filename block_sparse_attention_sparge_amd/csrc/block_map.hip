@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void key_mean_kernel(PoolArgs a) {
 // ---------------------------------------------------------------------------
 // pool_sim
 // ---------------------------------------------------------------------------
-template <class E, int D, bool SMOOTH>
+template <class E, int D, bool SMOOTH, bool QUANT>
 __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
   constexpr int CH = D / 8;          // 16-byte chunks per token
   constexpr int TPP = kWave / CH;    // tokens per pass of the wave
@@ -166,6 +166,47 @@ __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
     const float sim = dot * (1.0f / 4096.0f);
     uint8_t* flags = is_k ? a.sim_k : a.sim_q;
     flags[bh * nb + blk] = sim > a.thr[hh] ? 1 : 0;
+  }
+
+  if constexpr (QUANT) {
+    // int8 codes of the block as given (not smoothed): scale = absmax / 127,
+    // code = round-half-even(x * (127 / absmax)), both divisions correctly
+    // rounded in fp32; an all-zero block gets scale 0 and codes 0.
+    // Convert again below rather than keep the 8 NP floats of the statistics
+    // loop alive (the compiler would otherwise reuse them).
+#pragma unroll
+    for (int p = 0; p < NP; ++p) asm volatile("" : "+v"(raw[p]));
+    // The absolute maximum is taken on the 16-bit patterns: with the sign
+    // cleared they order like the values (inputs are finite).
+    uint32_t amax_bits = 0;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        amax_bits = max(amax_bits, max(raw[p][w] & 0x7FFFu, (raw[p][w] >> 16) & 0x7FFFu));
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, m, kWave));
+    const float amax = E::lo(amax_bits);
+    const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+    int8_t* codes = (is_k ? a.k_i8 : a.q_i8) + ((bh * nb + blk) * 64 + t0) * (int64_t)D + c * 8;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      uint32_t wd[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t wv = raw[p][2 * half + j / 2];
+          const float x = (j & 1) ? E::hi(wv) : E::lo(wv);
+          const float t = fminf(fmaxf(rintf(x * inv), -127.f), 127.f);
+          acc |= ((uint32_t)(int)t & 0xFFu) << (8 * j);
+        }
+        wd[half] = acc;
+      }
+      *reinterpret_cast<u32x2*>(codes + (int64_t)(p * TPP) * D) = u32x2{wd[0], wd[1]};
+    }
+    if (lane == 0) (is_k ? a.k_i8_scale : a.q_i8_scale)[bh * nb + blk] = amax / 127.0f;
   }
 }
 
@@ -517,17 +558,23 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+template <class E, bool QUANT>
+static void launch_pool_v(const PoolArgs& a, int d, dim3 grid, hipStream_t st) {
+  if (a.km_part) {
+    if (d == 128) hipLaunchKernelGGL((pool_sim_kernel<E, 128, true, QUANT>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((pool_sim_kernel<E, 64, true, QUANT>), grid, dim3(256), 0, st, a);
+  } else {
+    if (d == 128) hipLaunchKernelGGL((pool_sim_kernel<E, 128, false, QUANT>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((pool_sim_kernel<E, 64, false, QUANT>), grid, dim3(256), 0, st, a);
+  }
+}
+
 template <class E>
 static hipError_t launch_pool_t(const PoolArgs& a, int d, hipStream_t st) {
   const int64_t waves = (int64_t)a.b * a.h * (a.nq + a.nk);
   const dim3 grid((unsigned)((waves + 3) / 4));
-  if (a.km_part) {
-    if (d == 128) hipLaunchKernelGGL((pool_sim_kernel<E, 128, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((pool_sim_kernel<E, 64, true>), grid, dim3(256), 0, st, a);
-  } else {
-    if (d == 128) hipLaunchKernelGGL((pool_sim_kernel<E, 128, false>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((pool_sim_kernel<E, 64, false>), grid, dim3(256), 0, st, a);
-  }
+  if (a.q_i8) launch_pool_v<E, true>(a, d, grid, st);
+  else launch_pool_v<E, false>(a, d, grid, st);
   return hipGetLastError();
 }
 

@@ -35,56 +35,11 @@
 // head j reads KV head j / ratio) over an index list in which -1 entries are
 // skipped (aiter 4919 page).  Keys are gathered 64 at a time; scores and the
 // PV update run on the vector ALUs in fp32.
+#include "attn_common.h"
 #include "common.h"
 #include "kernels.h"
 
 namespace sparge {
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-// Index of the first negative entry of a LUT row (or its length), by one wave.
-__device__ __forceinline__ int first_negative(const int32_t* row, int len, int lane) {
-  int first = len;
-  for (int i = lane; i < len; i += kWave) {
-    if (row[i] < 0) { first = i; break; }
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) first = min(first, __shfl_xor(first, m, kWave));
-  return first;
-}
-
-// Position of key kappa (0..63) inside a V^T row: the 8 keys lane-half h uses
-// in PV k-step ks (keys 16ks + 8(e/4) + 4h + e%4, e = 0..7) become contiguous.
-__device__ __forceinline__ int vt_pos(int kappa) {
-  return 16 * (kappa >> 4) + 8 * ((kappa >> 2) & 1) + 4 * ((kappa >> 3) & 1) + (kappa & 3);
-}
-
-template <class E>
-__device__ __forceinline__ floatx16 mfma32(const u32x4& a, const u32x4& b, const floatx16& c);
-
-template <>
-__device__ __forceinline__ floatx16 mfma32<F16>(const u32x4& a, const u32x4& b, const floatx16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a),
-                                                __builtin_bit_cast(half8, b), c, 0, 0, 0);
-}
-
-template <>
-__device__ __forceinline__ floatx16 mfma32<BF16>(const u32x4& a, const u32x4& b, const floatx16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-template <class E, bool OUT_F32>
-__device__ __forceinline__ void store4(void* base, int64_t off, float x0, float x1, float x2, float x3) {
-  if constexpr (OUT_F32) {
-    floatx4 v = {x0, x1, x2, x3};
-    *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(base) + off) = v;
-  } else {
-    u32x2 v = {E::pack2(x0, x1), E::pack2(x2, x3)};
-    *reinterpret_cast<u32x2*>(reinterpret_cast<typename E::T*>(base) + off) = v;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // block-LUT kernel
@@ -114,40 +69,6 @@ __device__ __forceinline__ void store4(void* base, int64_t off, float x0, float 
 // The running maximum is only moved when a row's new maximum exceeds it by
 // more than 2^8 (base-2 units), so most blocks skip rescaling O; the exported
 // LSE and O are exact for any reference maximum, and P stays below 2^8.
-constexpr float kRescaleSlack = 8.0f;
-
-typedef short short4v __attribute__((ext_vector_type(4)));
-#define SPARGE_LDS __attribute__((address_space(3)))
-
-// 16 bytes from global memory at (wave-uniform base) + (per-lane 32-bit
-// offset) into LDS at (wave-uniform base) + 16 * lane.  The global base is a
-// scalar register pair, so moving to another block costs no vector ALU work.
-__device__ __forceinline__ void dma16(const void* gbase, uint32_t goff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds_base), "v"(goff), "s"(gbase)
-               : "memory", "m0");
-}
-
-// max(x, x of lane l ^ 32).  v_permlane32_swap exchanges lanes 32..63 of its
-// first operand with lanes 0..31 of its second; with x in both, every lane
-// then holds its own value in one register and its partner's in the other.
-// Written in assembly because both outputs are needed (the s_nop covers the
-// VALU-write-to-permlane hazard).
-__device__ __forceinline__ float half_swap_max(float x) {
-  float a = x, b = x;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-  return fmaxf(a, b);
-}
-
-// Compile-time buffer index for the two-way unrolled block loop.
-template <int N>
-struct Buf {
-  static constexpr int value = N;
-};
-
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 template <class E, int D, bool OUT_F32, bool CAUSAL, bool PVSKIP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fmha_block_kernel(FmhaArgs a) {

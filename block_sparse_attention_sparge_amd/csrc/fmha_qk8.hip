@@ -1,0 +1,353 @@
+// Stage 2 of SpargeAttn-style block-sparse attention with int8 Q and K on
+// gfx950 (CK page, "Status vs Upstream", not-yet-ported list: Q/K int8
+// quantisation in the pool kernel feeding an int8 QK product in the
+// attention kernel).
+//
+// The same walk as the fp16 / bf16 block kernel: one workgroup of four
+// wavefronts per (Q-tile, head, batch, split), wave (qh, kh) owning 32 query
+// rows and 32 keys of every listed 64-key block, K and V arriving by direct
+// global->LDS loads into double buffers, one barrier per block, the two key
+// halves merged by the LSE rule at the end.  What changes:
+//   * S^T = K Q^T runs on v_mfma_i32_32x32x32_i8 from the int8 codes: four
+//     MFMAs per block for d = 128 instead of eight, and the integer product is
+//     exact (|sum| <= 128 * 127^2 < 2^24, so its conversion to fp32 is exact
+//     too); the score is that integer times scale * q_scale * k_scale, one
+//     fp32 multiply folded into the base-2 softmax FMA;
+//   * a K block is 64 rows of d bytes in LDS, half the bytes of fp16, so the
+//     direct loads write half as much into LDS and the operand reads of K
+//     halve;
+//   * the K scale of every block comes through the scalar cache next to its
+//     LUT entry, requested after the block's last LDS wait like the entry.
+// V and P stay in fp16 / bf16 and the PV product is the one of the fp16 / bf16
+// kernel.
+#include "attn_common.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace sparge {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ i32x16 mfma_i8(const u32x4& a, const u32x4& b, const i32x16& c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c,
+                                               0, 0, 0);
+}
+
+// K rows are d bytes: GK 16-byte granules.  Row r's granule g sits in slot
+// g ^ ((r / (16 / GK)) % GK): the 16 rows that 16 consecutive lanes read for
+// one k-step then fall on 16 different 16-byte bank groups.
+template <int GK>
+__device__ __forceinline__ int k8_swz(int r) {
+  return (r / (16 / GK)) % GK;
+}
+
+template <class E, int D, bool OUT_F32, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fmha_qk8_kernel(FmhaArgs a) {
+  typedef typename E::T T;
+  constexpr int G16 = D / 8;                 // 16-byte granules per V row
+  constexpr int GK = D / 16;                 // 16-byte granules per int8 K row
+  constexpr int NKK = D / 32;                // k-steps of S^T (32 codes each)
+  constexpr int NMD = D / 32;                // M-tiles of O^T
+  constexpr int TILE = 64 * D;               // elements of a V buffer, bytes of a K buffer
+  constexpr int NDMA_V = 64 * G16 / 256;     // direct loads per thread per V tile
+  constexpr int NDMA_K = 64 * GK / 256;      // and per K tile
+  constexpr int VSW = G16 / 4;
+  __shared__ __attribute__((aligned(16))) int8_t sK[2 * TILE];
+  __shared__ __attribute__((aligned(16))) T sV[2 * TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+  const int qh = wave & 1;
+  const int kh = wave >> 1;
+
+  const int64_t G = (int64_t)a.nqt * a.hq * a.b * a.splits;
+  int64_t lin = xcd_remap(blockIdx.x, gridDim.x);
+  if (lin >= G) return;
+  const int qt = (int)(lin % a.nqt);
+  lin /= a.nqt;
+  const int hh = (int)(lin % a.hq);
+  lin /= a.hq;
+  const int bb = (int)(lin % a.b);
+  const int split = (int)(lin / a.b);
+  const int hk = hh / a.ratio;
+
+  int n;
+  const int32_t* list = nullptr;
+  if (a.lut) {
+    const int hlut = a.lut_heads == a.hq ? hh : hk;
+    const int64_t row = ((int64_t)bb * a.lut_heads + hlut) * a.nqt + qt;
+    list = a.lut + row * a.lut_row_len;
+    n = a.cnt ? a.cnt[row] : first_negative(list, a.lut_row_len, lane);
+  } else {
+    n = CAUSAL ? min(a.nkb, qt + 1) : a.nkb;
+  }
+  n = __builtin_amdgcn_readfirstlane(n);
+  const int chunk = (n + a.splits - 1) / a.splits;
+  const int beg = split * chunk;
+  const int nloc = max(0, min(n, beg + chunk) - beg);
+
+  const int q0 = qt * 64 + qh * 32;
+  const int64_t orow = (int64_t)split * a.o_split_stride + bb * a.os[0] + hh * a.os[1] +
+                       (int64_t)(q0 + l32) * a.os[2];
+  float* lse_row = a.lse ? a.lse + (((int64_t)split * a.b + bb) * a.hq + hh) * a.sq : nullptr;
+
+  if (nloc == 0) {
+    if (kh == 0) {
+      for (int d0 = hl * (D / 2); d0 < (hl + 1) * (D / 2); d0 += 4)
+        store4<E, OUT_F32>(a.o, orow + d0, 0.f, 0.f, 0.f, 0.f);
+      if (lse_row && hl == 0) lse_row[q0 + l32] = -INFINITY;
+    }
+    return;
+  }
+
+  // Q^T codes (B operand): lane (query l32, half hl) holds d = 32kk + 16hl .. +15.
+  const int8_t* qp = reinterpret_cast<const int8_t*>(a.q) + bb * a.qs[0] + hh * a.qs[1] +
+                     (int64_t)(q0 + l32) * a.qs[2] + 16 * hl;
+  u32x4 qf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) qf[kk] = load16(qp + 32 * kk);
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qf[kk]));
+
+  // Scales: the tile's Q scale and the softmax scale are folded once; the K
+  // scale of each block joins them per block.
+  const __attribute__((address_space(4))) float* ksc =
+      (const __attribute__((address_space(4))) float*)(a.k_scale + ((int64_t)bb * a.hkv + hk) * a.nkb);
+  const float c2q = a.scale_log2 * a.q_scale[((int64_t)bb * a.hq + hh) * a.nqt + qt];
+
+  const char* kbase = reinterpret_cast<const char*>(a.k) + bb * a.ks[0] + hk * a.ks[1];
+  const char* vbase = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v) + bb * a.vs[0] + hk * a.vs[1]);
+  const int64_t kblk = 64 * a.ks[2], vblk = 64 * a.vs[2] * (int64_t)sizeof(T);
+  const uint32_t sk_lds = (uint32_t)(uintptr_t)((SPARGE_LDS void*)sK);
+  const uint32_t sv_lds = (uint32_t)(uintptr_t)((SPARGE_LDS void*)sV);
+
+  uint32_t koff[NDMA_K], voff[NDMA_V];
+#pragma unroll
+  for (int j = 0; j < NDMA_K; ++j) {
+    const int gi = 64 * (wave * NDMA_K + j) + lane;
+    const int r = gi / GK, sl = gi % GK;
+    koff[j] = (uint32_t)(r * a.ks[2] + (sl ^ k8_swz<GK>(r)) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < NDMA_V; ++j) {
+    const int gi = 64 * (wave * NDMA_V + j) + lane;
+    const int r = gi / G16, sl = gi % G16;
+    voff[j] = (uint32_t)((r * a.vs[2] + (sl ^ ((VSW * r) % G16)) * 8) * (int64_t)sizeof(T));
+  }
+  auto issue_block = [&](int kb, int buf) {
+    const char* kp = kbase + kb * kblk;
+    const char* vp = vbase + kb * vblk;
+#pragma unroll
+    for (int j = 0; j < NDMA_K; ++j)
+      dma16(kp, koff[j], sk_lds + (uint32_t)(buf * TILE + (wave * NDMA_K + j) * 64 * 16));
+#pragma unroll
+    for (int j = 0; j < NDMA_V; ++j)
+      dma16(vp, voff[j], sv_lds + (uint32_t)((buf * TILE + (wave * NDMA_V + j) * 64 * 8) * sizeof(T)));
+  };
+  const __attribute__((address_space(4))) int32_t* clist = (const __attribute__((address_space(4))) int32_t*)list;
+  auto kb_of = [&](int i) { return list ? clist[beg + i] : beg + i; };
+
+  floatx16 acc_o[NMD];
+#pragma unroll
+  for (int i = 0; i < NMD; ++i) acc_o[i] = floatx16{};
+  float m_run = -INFINITY;   // reference maximum in base-2 units
+  float l_run = 0.f;
+  const int krow = 32 * kh + l32;
+  const int kswz = k8_swz<GK>(krow);
+  const int vs16 = lane & 15, vgrp = lane >> 4;
+  const int vrow0 = 32 * kh + 4 * (vgrp >> 1) + (vs16 >> 2);
+  const int vcol0 = 16 * (vgrp & 1) + 4 * (vs16 & 3);
+
+  issue_block(kb_of(0), 0);
+  wait_dma();
+  __syncthreads();
+  if (nloc > 1) issue_block(kb_of(1), 1);
+  int kb_ahead = nloc > 2 ? kb_of(2) : 0;
+  // K scales of blocks it (sk_cur) and it+1 (sk_nxt); block it+2's is
+  // requested at the end of step it.
+  float sk_cur = ksc[kb_of(0)];
+  float sk_nxt = nloc > 1 ? ksc[kb_of(1)] : 0.f;
+  int kb_cur = CAUSAL ? kb_of(0) : 0;
+  int kb_nxt = CAUSAL && nloc > 1 ? kb_of(1) : 0;
+
+  auto step = [&](int it, auto cur_tag) {
+    constexpr int cur = decltype(cur_tag)::value;
+    const int8_t* kt = &sK[cur * TILE];
+    const SPARGE_LDS T* vt = (const SPARGE_LDS T*)&sV[cur * TILE];
+
+    // The scalar loads of the previous step (and of the prologue) have landed.
+    asm volatile("" ::"s"(kb_ahead), "s"(sk_cur), "s"(sk_nxt));
+    u32x4 kf[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int g = (2 * kk + hl) ^ kswz;
+      kf[kk] = *reinterpret_cast<const u32x4*>(&kt[krow * D + g * 16]);
+    }
+    u32x4 vf[2][NMD];
+    auto read_vt = [&](int ks) {
+#pragma unroll
+      for (int md = 0; md < NMD; ++md) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int r = vrow0 + 16 * ks + 8 * c;
+          const int col = 32 * md + vcol0;
+          const int slot = (col >> 3) ^ ((VSW * r) % G16);
+          const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (SPARGE_LDS short4v*)(vt + r * D + slot * 8 + (col & 7)));
+          const u32x2 w2 = __builtin_bit_cast(u32x2, x);
+          vf[ks][md][2 * c] = w2[0];
+          vf[ks][md][2 * c + 1] = w2[1];
+        }
+      }
+    };
+    read_vt(0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // S^T (32 keys x 32 queries) = K Q^T on the codes, exact in int32.
+    i32x16 si = i32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) si = mfma_i8(kf[kk], qf[kk], si);
+    read_vt(1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    float s[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = (float)si[r];
+    if constexpr (CAUSAL) {
+      if (kb_cur >= qt) {
+        const int qpos = 64 * qt + 32 * qh + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 64 * kb_cur + 32 * kh + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (key > qpos) s[r] = -INFINITY;
+        }
+      }
+    }
+
+    const float c2 = c2q * sk_cur;   // this block's factor from code product to base-2 score
+    float rmax = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) rmax = fmaxf(rmax, s[r]);
+    rmax = half_swap_max(rmax);
+    const float m_cand = rmax * c2;
+    const bool need = m_cand > m_run + kRescaleSlack;
+    if (__any(need)) {
+      const float m_new = need ? m_cand : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < NMD; ++i) acc_o[i] *= alpha;
+    }
+    const float mref = CAUSAL && m_run == -INFINITY ? 0.f : m_run;
+    u32x4 pf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w], c2, -mref));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w + 1], c2, -mref));
+        pf[ks][w] = E::pack2(p0, p1);
+        if constexpr (E::kRowSumRounded) l_run = E::sum2(pf[ks][w], l_run);
+        else l_run += p0 + p1;
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int md = 0; md < NMD; ++md) acc_o[md] = mfma32<E>(vf[ks][md], pf[ks], acc_o[md]);
+    }
+
+    // After the last LDS wait: the LUT entry of block it+3 and the K scale of
+    // block it+2 (kb_ahead), both consumed first thing in the next step.
+    __builtin_amdgcn_sched_barrier(0);
+    const int kb_next = it + 3 < nloc ? kb_of(it + 3) : 0;
+    const float sk_next = it + 2 < nloc ? ksc[kb_ahead] : 0.f;
+
+    wait_dma();
+    __syncthreads();
+    if (it + 2 < nloc) issue_block(kb_ahead, cur);
+    if constexpr (CAUSAL) {
+      kb_cur = kb_nxt;
+      kb_nxt = kb_ahead;
+    }
+    sk_cur = sk_nxt;
+    sk_nxt = sk_next;
+    kb_ahead = kb_next;
+  };
+
+#pragma unroll 1
+  for (int it = 0; it < nloc; it += 2) {
+    step(it, Buf<0>{});
+    if (it + 1 == nloc) break;
+    step(it + 1, Buf<1>{});
+  }
+
+  // Merge the two key halves (as in the fp16 / bf16 kernel; the partial O^T
+  // goes to the V buffers, the larger ones here).
+  const float l_w = l_run + __shfl_xor(l_run, 32, kWave);
+  float* mrg = reinterpret_cast<float*>(sV) + qh * (NMD * 16 * 64);
+  float* ml = reinterpret_cast<float*>(sK) + qh * 64;
+  if (kh == 1) {
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mrg[(md * 16 + r) * 64 + lane] = acc_o[md][r];
+    if (hl == 0) {
+      ml[l32] = m_run;
+      ml[32 + l32] = l_w;
+    }
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  const float m1 = ml[l32], l1 = ml[32 + l32];
+  float m = fmaxf(m_run, m1);
+  const bool empty = CAUSAL && m == -INFINITY;
+  if (empty) m = 0.f;
+  const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+  const float l_tot = l_w * a0 + l1 * a1;
+  const float inv = empty ? 0.f : 1.0f / l_tot;
+  const float s0 = a0 * inv, s1 = a1 * inv;
+#pragma unroll
+  for (int md = 0; md < NMD; ++md) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        x[i] = acc_o[md][r] * s0 + mrg[(md * 16 + r) * 64 + lane] * s1;
+      }
+      const int d0 = 32 * md + 8 * g + 4 * hl;
+      store4<E, OUT_F32>(a.o, orow + d0, x[0], x[1], x[2], x[3]);
+    }
+  }
+  if (lse_row && hl == 0) lse_row[q0 + l32] = empty ? -INFINITY : (m + __log2f(l_tot)) * kLn2;
+}
+
+template <class E, int D>
+static hipError_t launch_qk8_t(const FmhaArgs& a, bool out_f32, hipStream_t st) {
+  const int64_t G = (int64_t)a.nqt * a.hq * a.b * a.splits;
+  const dim3 grid((unsigned)(((G + 7) / 8) * 8));
+  if (a.causal) {
+    if (out_f32) hipLaunchKernelGGL((fmha_qk8_kernel<E, D, true, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((fmha_qk8_kernel<E, D, false, true>), grid, dim3(256), 0, st, a);
+  } else {
+    if (out_f32) hipLaunchKernelGGL((fmha_qk8_kernel<E, D, true, false>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((fmha_qk8_kernel<E, D, false, false>), grid, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fmha_qk8(const FmhaArgs& a, sparge_dtype v_dt, sparge_dtype o_dt, int d, hipStream_t st) {
+  const bool f32 = o_dt == SPARGE_F32;
+  if (v_dt == SPARGE_F16) return d == 128 ? launch_qk8_t<F16, 128>(a, f32, st) : launch_qk8_t<F16, 64>(a, f32, st);
+  return d == 128 ? launch_qk8_t<BF16, 128>(a, f32, st) : launch_qk8_t<BF16, 64>(a, f32, st);
+}
+
+}  // namespace sparge

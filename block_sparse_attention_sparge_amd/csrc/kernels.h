@@ -26,6 +26,12 @@ struct PoolArgs {
   float* km_part;
   int km_chunks;
   float km_scale;    // 1 / s_k
+  // int8 codes of Q and K per 64-token block ([b, h, s, d] contiguous) and
+  // their scales ([b, h, nq], [b, h, nk]); null when not requested.
+  int8_t* q_i8;
+  int8_t* k_i8;
+  float* q_i8_scale;
+  float* k_i8_scale;
   float thr[SPARGE_MAX_HEADS];
 };
 
@@ -69,6 +75,9 @@ struct FmhaArgs {
   int64_t o_split_stride;  // elements
   int causal;              // block mode: key j > query i masked
   float pv_tau2;           // block mode: pv_threshold * log2(e); 0 = no PV skip
+  // int8-QK block kernel: q and k hold int8 codes; their per-block scales.
+  const float* q_scale;    // [b, hq, nqt]
+  const float* k_scale;    // [b, hkv, nkb]
 };
 
 struct CombineArgs {
@@ -86,6 +95,8 @@ hipError_t launch_pool_sim(const PoolArgs& a, sparge_dtype dt, int d, hipStream_
 hipError_t launch_score_select(const SelectArgs& a, int d, hipStream_t st);
 hipError_t launch_fmha_block(const FmhaArgs& a, sparge_dtype dt, sparge_dtype o_dt, int d,
                              hipStream_t st);
+hipError_t launch_fmha_qk8(const FmhaArgs& a, sparge_dtype v_dt, sparge_dtype o_dt, int d,
+                           hipStream_t st);
 hipError_t launch_fmha_tokens(const FmhaArgs& a, sparge_dtype dt, sparge_dtype o_dt, int d,
                               int rows_per_group, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, sparge_dtype part_dt, sparge_dtype out_dt,

@@ -23,13 +23,13 @@ LIB_PATH = os.path.join(_PKG, "libsparge.so")
 SPARGE_OK, SPARGE_ERR_INVALID, SPARGE_ERR_UNSUPPORTED, SPARGE_ERR_HIP = 0, 1, 2, 3
 SPARGE_F16, SPARGE_BF16, SPARGE_F32 = 0, 1, 2
 SPARGE_FLAG_SMOOTH_K, SPARGE_FLAG_CAUSAL, SPARGE_FLAG_ATTN_SINK = 1, 2, 4
-ABI_VERSION = 3
+ABI_VERSION = 4
 MAX_HEADS = 128
 MAX_KBLOCKS = 1024
 
 EXPORTED_SYMBOLS = (
     "sparge_abi_version", "sparge_last_error", "sparge_build_block_map",
-    "sparge_build_block_map_workspace", "sparse_fmha_fwd", "attn_combine",
+    "sparge_build_block_map_workspace", "sparse_fmha_fwd", "sparse_fmha_fwd_qk_int8", "attn_combine",
     "sparge_validate_lut",
 )
 
@@ -77,11 +77,15 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         lib.sparge_build_block_map.restype = _i
         lib.sparge_build_block_map.argtypes = [
             _p, _p, _i, _i, _i, _i, _i, _i, _I64x3, _I64x3, _i, _i,
-            _p, _p, _p, _f, _u, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
+            _p, _p, _p, _f, _u, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
         lib.sparse_fmha_fwd.restype = _i
         lib.sparse_fmha_fwd.argtypes = [
             _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
             _I64x3, _I64x3, _I64x3, _I64x3, _i, _i, _p, _p, _i, _i, _f, _u, _f, _i, _i64, _p]
+        lib.sparse_fmha_fwd_qk_int8.restype = _i
+        lib.sparse_fmha_fwd_qk_int8.argtypes = [
+            _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
+            _I64x3, _I64x3, _I64x3, _I64x3, _p, _p, _i, _i, _f, _u, _i, _i64, _p]
         lib.attn_combine.restype = _i
         lib.attn_combine.argtypes = [_p, _i, _p, _i, _i, _i, _i, _i, _i64, _p, _i, _p, _p]
         lib.sparge_validate_lut.restype = _i
@@ -162,14 +166,16 @@ def build_block_map(q: torch.Tensor, k: torch.Tensor, topk, simthreshd1, cdfthre
                     softmax_scale: float = 0.0, blk_q: int = 64, blk_k: int = 64,
                     return_debug: bool = False, workspace: Optional[torch.Tensor] = None,
                     out: Optional[dict] = None, smooth_k: bool = False, causal: bool = False,
-                    attention_sink: bool = False) -> dict:
+                    attention_sink: bool = False, quantize_int8: bool = False) -> dict:
     """Stage 1 (sparge_build_block_map).  q [b, h, s_q, d], k [b, h, s_k, d].
 
     Returns a dict with 'lut' int32 [b, h, nq, nk], 'count' int32 [b, h, nq],
     and with return_debug also 'bitmap', 'prob', 'sim_q', 'sim_k', 'q_mean',
     'k_mean'.  `out` may hold preallocated tensors under the same keys (plus
     'workspace').  smooth_k / causal / attention_sink set SPARGE_FLAG_SMOOTH_K /
-    SPARGE_FLAG_CAUSAL / SPARGE_FLAG_ATTN_SINK.
+    SPARGE_FLAG_CAUSAL / SPARGE_FLAG_ATTN_SINK.  quantize_int8 also returns the
+    per-block int8 codes 'q_i8' [b, h, s_q, d], 'k_i8' [b, h, s_k, d] and their
+    scales 'q_i8_scale' [b, h, nq], 'k_i8_scale' [b, h, nk].
     """
     lib = load_library()
     dev = _on_gpu(q, k)
@@ -199,6 +205,15 @@ def build_block_map(q: torch.Tensor, k: torch.Tensor, topk, simthreshd1, cdfthre
                    sim_k=get("sim_k", (b, h, nk), torch.uint8),
                    q_mean=get("q_mean", (b, h, nq, d), torch.float32),
                    k_mean=get("k_mean", (b, h, nk, d), torch.float32))
+    qz = {}
+    if quantize_int8:
+        qz = dict(q_i8=get("q_i8", (b, h, s_q, d), torch.int8),
+                  q_i8_scale=get("q_i8_scale", (b, h, nq), torch.float32),
+                  k_i8=get("k_i8", (b, h, s_k, d), torch.int8),
+                  k_i8_scale=get("k_i8_scale", (b, h, nk), torch.float32))
+        for key in ("q_i8", "k_i8"):
+            if not qz[key].is_contiguous():
+                raise SpargeError(SPARGE_ERR_INVALID, f"{key} must be contiguous")
     ws_bytes = lib.sparge_build_block_map_workspace(b, h, s_q, s_k, d, blk_q, blk_k)
     if workspace is None:
         workspace = out.get("workspace")
@@ -212,11 +227,13 @@ def build_block_map(q: torch.Tensor, k: torch.Tensor, topk, simthreshd1, cdfthre
         _flags(smooth_k=smooth_k, causal=causal, attention_sink=attention_sink),
         _ptr(lut), _ptr(count), _ptr(dbg.get("bitmap")), _ptr(dbg.get("prob")),
         _ptr(dbg.get("sim_q")), _ptr(dbg.get("sim_k")), _ptr(dbg.get("q_mean")),
-        _ptr(dbg.get("k_mean")), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(dev))
+        _ptr(dbg.get("k_mean")), _ptr(qz.get("q_i8")), _ptr(qz.get("q_i8_scale")),
+        _ptr(qz.get("k_i8")), _ptr(qz.get("k_i8_scale")), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(dev))
     _check(st)
     res = dict(lut=lut, count=count, workspace=workspace)
     res.update(dbg)
+    res.update(qz)
     return res
 
 
@@ -270,6 +287,57 @@ def sparse_fmha_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         blk_q, blk_k, _ptr(lut), _ptr(count), lut_row_len, lut_heads, float(softmax_scale),
         _flags(causal=causal), float(pv_threshold), int(num_splits), int(split_stride),
         _stream(dev))
+    _check(st)
+    return o, lse
+
+
+def sparse_fmha_fwd_qk_int8(q_i8: torch.Tensor, q_scale: torch.Tensor, k_i8: torch.Tensor,
+                            k_scale: torch.Tensor, v: torch.Tensor,
+                            lut: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None,
+                            softmax_scale: float = 0.0, num_splits: int = 1,
+                            out_dtype: Optional[torch.dtype] = None, o: Optional[torch.Tensor] = None,
+                            lse: Optional[torch.Tensor] = None, return_lse: bool = True,
+                            causal: bool = False):
+    """Stage 2 on int8 Q/K codes (sparse_fmha_fwd_qk_int8), block mode.
+
+    q_i8 [b, h_q, s_q, d] int8 with q_scale [b, h_q, s_q/64]; k_i8 [b, h_kv,
+    s_k, d] int8 with k_scale [b, h_kv, s_k/64] (as build_block_map(...,
+    quantize_int8=True) returns them); v [b, h_kv, s_k, d] fp16/bf16.  The LUT,
+    splits and outputs are as in sparse_fmha_fwd.  Returns (o, lse).
+    """
+    lib = load_library()
+    dev = _on_gpu(q_i8, q_scale, k_i8, k_scale, v, lut, count, o, lse)
+    b, h_q, s_q, d = q_i8.shape
+    h_kv, s_k = k_i8.shape[1], k_i8.shape[2]
+    if q_i8.dtype != torch.int8 or k_i8.dtype != torch.int8:
+        raise SpargeError(SPARGE_ERR_INVALID, "q_i8 and k_i8 must be int8")
+    for name, t, shape in (("q_scale", q_scale, (b, h_q, s_q // 64)), ("k_scale", k_scale, (b, h_kv, s_k // 64))):
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shape:
+            raise SpargeError(SPARGE_ERR_INVALID, f"{name} must be contiguous float32 {shape}")
+    if out_dtype is None:
+        out_dtype = v.dtype if num_splits == 1 else torch.float32
+    split_stride = 0
+    if o is None:
+        shape = (b, h_q, s_q, v.shape[3]) if num_splits == 1 else (num_splits, b, h_q, s_q, v.shape[3])
+        o = torch.empty(shape, dtype=out_dtype, device=dev)
+    o4 = o if o.dim() == 4 else o[0]
+    if num_splits > 1:
+        split_stride = o.stride(0)
+    if lse is None and (return_lse or num_splits > 1):
+        shape = (b, h_q, s_q) if num_splits == 1 else (num_splits, b, h_q, s_q)
+        lse = torch.empty(shape, dtype=torch.float32, device=dev)
+    lut_row_len, lut_heads = 0, h_q
+    if lut is not None:
+        if lut.dtype != torch.int32 or not lut.is_contiguous():
+            raise SpargeError(SPARGE_ERR_INVALID, "lut must be contiguous int32")
+        lut_row_len, lut_heads = lut.shape[-1], lut.shape[1]
+    if count is not None and (count.dtype != torch.int32 or not count.is_contiguous()):
+        raise SpargeError(SPARGE_ERR_INVALID, "count must be contiguous int32")
+    st = lib.sparse_fmha_fwd_qk_int8(
+        _ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale), _ptr(v), _ptr(o), _ptr(lse),
+        _dt(v.dtype), _dt(o.dtype), b, h_q, h_kv, s_q, s_k, d, _strides(q_i8), _strides(k_i8),
+        _strides(v), _strides(o4), _ptr(lut), _ptr(count), lut_row_len, lut_heads,
+        float(softmax_scale), _flags(causal=causal), int(num_splits), int(split_stride), _stream(dev))
     _check(st)
     return o, lse
 

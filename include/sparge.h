@@ -69,7 +69,7 @@ typedef enum {
 #define SPARGE_FLAG_CAUSAL 2u     /* block map and block-mode FMHA: causal masks   */
 #define SPARGE_FLAG_ATTN_SINK 4u  /* block map: K block 0 selected in every row    */
 
-/* Library ABI version (this header: 3). */
+/* Library ABI version (this header: 4). */
 int sparge_abi_version(void);
 
 /* Message for the last failed call on this thread ("" if none). */
@@ -120,6 +120,16 @@ const char* sparge_last_error(void);
  *   pooled_prob float [b, h, nq, nk] or NULL: P exactly as the selection saw it.
  *   sim_q, sim_k uint8 [b, h, nq] / [b, h, nk] or NULL: gate flags.
  *   q_mean, k_mean float [b, h, nq, d] / [b, h, nk, d] or NULL.
+ *   q_i8, k_i8 int8 [b, h, s_q, d] / [b, h, s_k, d] contiguous, 16-byte
+ *              aligned, with q_i8_scale, k_i8_scale float [b, h, nq] /
+ *              [b, h, nk]: all four or none.  (CK page, "Status vs Upstream",
+ *              not-yet-ported list: Q/K int8 quantisation fused into the pool
+ *              kernel, for an int8 QK product in the attention kernel.)  Per
+ *              64-token block of the inputs as given (K not smoothed):
+ *              scale = absmax / 127 and code = round-half-even(x * (127 /
+ *              absmax)) clamped to [-127, 127], in fp32 with correctly
+ *              rounded divisions; an all-zero block gets scale 0, codes 0.
+ *              Input to sparse_fmha_fwd_qk_int8.
  *   workspace  device scratch of at least sparge_build_block_map_workspace()
  *              bytes, 256-byte aligned; contents on entry are ignored.
  */
@@ -132,6 +142,7 @@ sparge_status sparge_build_block_map(
     float softmax_scale, unsigned flags,
     int32_t* lut, int32_t* lut_count, uint8_t* block_map, float* pooled_prob,
     uint8_t* sim_q, uint8_t* sim_k, float* q_mean, float* k_mean,
+    int8_t* q_i8, float* q_i8_scale, int8_t* k_i8, float* k_i8_scale,
     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace sparge_build_block_map needs for these sizes
@@ -204,6 +215,32 @@ sparge_status sparse_fmha_fwd(
     const int32_t* lut, const int32_t* lut_count, int lut_row_len, int lut_heads,
     float softmax_scale, unsigned flags, float pv_threshold,
     int num_splits, int64_t o_split_stride, void* stream);
+
+/*
+ * Stage 2 with int8 Q and K (CK page, "Status vs Upstream", not-yet-ported
+ * list: an int8 QK product in the attention kernel, fed by the pool kernel's
+ * quantisation).  Block mode only (64 x 64).  The same computation as
+ * sparse_fmha_fwd, with every score taken from the codes:
+ *   s_j = scale * q_scale[tile] * k_scale[block of j] * <q_code_i, k_code_j>
+ * (the integer product is exact; the scores are then fp32).  V, O, the LUT,
+ * num_splits, o_split_stride and flags (0 or SPARGE_FLAG_CAUSAL) are as in
+ * sparse_fmha_fwd; v_dt is F16 or BF16 and o_dt is v_dt or F32.
+ *   q        int8 [b, h_q, s_q, d], strides (elements) for (b, h, s);
+ *   q_scale  float [b, h_q, s_q / 64] contiguous;
+ *   k        int8 [b, h_kv, s_k, d], strides for (b, h, s);
+ *   k_scale  float [b, h_kv, s_k / 64] contiguous.
+ * d is 64 or 128; q, k, v, o 16-byte aligned; 64 rows of K or V must span
+ * less than 2^31 bytes.
+ */
+sparge_status sparse_fmha_fwd_qk_int8(
+    const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
+    const void* v, void* o, float* lse, sparge_dtype v_dt, sparge_dtype o_dt,
+    int b, int h_q, int h_kv, int s_q, int s_k, int d,
+    const int64_t q_strides[3], const int64_t k_strides[3],
+    const int64_t v_strides[3], const int64_t o_strides[3],
+    const int32_t* lut, const int32_t* lut_count, int lut_row_len, int lut_heads,
+    float softmax_scale, unsigned flags, int num_splits, int64_t o_split_stride,
+    void* stream);
 
 /*
  * LSE combine of n_parts partial results.  (Updating Log page, Stage 1:

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert lib.sparge_abi_version() == ops.ABI_VERSION == 3
+    assert lib.sparge_abi_version() == ops.ABI_VERSION == 4
 
 
 def _s3(a, b, c):
@@ -74,13 +74,13 @@ def _bm(lib, **kw):
     args = dict(q=FAKE, k=FAKE, dt=ops.SPARGE_F16, b=1, h=2, s_q=512, s_k=512, d=64,
                 qs=_s3(65536, 32768, 64), ks=_s3(65536, 32768, 64), blk_q=64, blk_k=64,
                 topk=_arr([0.5, 0.5]), cdf=None, sim=_arr([0.001, 0.001]), scale=0.0, flags=0,
-                lut=FAKE, cnt=FAKE, ws=FAKE, ws_bytes=1 << 20)
+                lut=FAKE, cnt=FAKE, q8=None, q8s=None, k8=None, k8s=None, ws=FAKE, ws_bytes=1 << 20)
     args.update(kw)
     return lib.sparge_build_block_map(
         args["q"], args["k"], args["dt"], args["b"], args["h"], args["s_q"], args["s_k"], args["d"],
         args["qs"], args["ks"], args["blk_q"], args["blk_k"], args["topk"], args["cdf"], args["sim"],
         args["scale"], args["flags"], args["lut"], args["cnt"], None, None, None, None, None, None,
-        args["ws"], args["ws_bytes"], None)
+        args["q8"], args["q8s"], args["k8"], args["k8s"], args["ws"], args["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -106,6 +106,9 @@ def _bm(lib, **kw):
     (dict(scale=-1.0), ops.SPARGE_ERR_INVALID),
     (dict(flags=8), ops.SPARGE_ERR_INVALID),                         # unknown flag bit
     (dict(flags=ops.SPARGE_FLAG_CAUSAL, s_k=1024), ops.SPARGE_ERR_UNSUPPORTED),   # causal, s_q != s_k
+    (dict(q8=FAKE), ops.SPARGE_ERR_INVALID),                                      # int8 outputs: all or none
+    (dict(q8=FAKE, q8s=FAKE, k8=FAKE), ops.SPARGE_ERR_INVALID),
+    (dict(q8=FAKE + 8, q8s=FAKE, k8=FAKE, k8s=FAKE), ops.SPARGE_ERR_INVALID),     # misaligned codes
 ])
 def test_block_map_rejections(lib, kw, status):
     st = _bm(lib, **kw)
@@ -163,6 +166,42 @@ def _fmha(lib, **kw):
 ])
 def test_fmha_rejections(lib, kw, status):
     st = _fmha(lib, **kw)
+    assert st == status, _err(lib)
+
+
+def _fmha8(lib, **kw):
+    a = dict(q=FAKE, qsc=FAKE, k=FAKE, ksc=FAKE, v=FAKE, o=FAKE, lse=FAKE, vdt=ops.SPARGE_BF16,
+             odt=ops.SPARGE_BF16, b=1, hq=8, hkv=2, sq=512, sk=512, d=128,
+             qs=_s3(8 * 512 * 128, 512 * 128, 128), ks=_s3(2 * 512 * 128, 512 * 128, 128),
+             vs=_s3(2 * 512 * 128, 512 * 128, 128), os=_s3(8 * 512 * 128, 512 * 128, 128),
+             lut=FAKE, cnt=FAKE, L=8, lh=8, scale=0.0, flags=0, splits=1, sst=0)
+    a.update(kw)
+    return lib.sparse_fmha_fwd_qk_int8(a["q"], a["qsc"], a["k"], a["ksc"], a["v"], a["o"], a["lse"],
+                                       a["vdt"], a["odt"], a["b"], a["hq"], a["hkv"], a["sq"], a["sk"],
+                                       a["d"], a["qs"], a["ks"], a["vs"], a["os"], a["lut"], a["cnt"],
+                                       a["L"], a["lh"], a["scale"], a["flags"], a["splits"], a["sst"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qsc=None), ops.SPARGE_ERR_INVALID),
+    (dict(ksc=None), ops.SPARGE_ERR_INVALID),
+    (dict(v=None), ops.SPARGE_ERR_INVALID),
+    (dict(vdt=ops.SPARGE_F32), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(odt=ops.SPARGE_F16), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(d=96), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(sk=520), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(hkv=3), ops.SPARGE_ERR_INVALID),
+    (dict(qs=_s3(8 * 512 * 128, 512 * 136, 136)), ops.SPARGE_ERR_INVALID),       # 136 B rows: not 16-aligned steps
+    (dict(k=FAKE + 4), ops.SPARGE_ERR_INVALID),
+    (dict(flags=ops.SPARGE_FLAG_ATTN_SINK), ops.SPARGE_ERR_INVALID),
+    (dict(flags=ops.SPARGE_FLAG_CAUSAL, sk=1024), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(splits=2, lse=None), ops.SPARGE_ERR_INVALID),
+    (dict(lut=None, cnt=FAKE), ops.SPARGE_ERR_INVALID),
+    (dict(lh=4), ops.SPARGE_ERR_INVALID),
+    (dict(vs=_s3(2 * 512 * 128, 512 * 128, 1 << 24)), ops.SPARGE_ERR_UNSUPPORTED),
+])
+def test_fmha_qk_int8_rejections(lib, kw, status):
+    st = _fmha8(lib, **kw)
     assert st == status, _err(lib)
 
 

@@ -52,8 +52,10 @@ namespace sparge {
 // K and V blocks are double-buffered in LDS and arrive by direct global->LDS
 // loads (no registers on the way; on gfx950 this path moves gathered blocks
 // out of L2 much faster than loads into VGPRs).  The loads of block i+1 are
-// issued right after the barrier that retires block i-1, so they overlap the
-// compute of block i; one barrier per block.  These loads are issued from
+// issued in the middle of block i, once its operand reads have been issued:
+// the buffer they fill was released by the barrier that ended block i-1, and
+// their LDS writes then meet the softmax and the PV MFMAs rather than the
+// burst of operand reads at the start of a block.  One barrier per block.  These loads are issued from
 // inline assembly so the compiler does not guard every LDS read with a wait
 // for them; the kernel waits for them itself (vmcnt) before that barrier.
 //   * K is stored row-major with the 16-byte granules of row r XOR-swizzled
@@ -193,16 +195,12 @@ void fmha_block_kernel(FmhaArgs a) {
   const int vrow0 = 32 * kh + 4 * (vgrp >> 1) + (vs16 >> 2);
   const int vcol0 = 16 * (vgrp & 1) + 4 * (vs16 & 3);
 
-  // Prologue: block 0 in LDS, block 1 in flight, LUT entry of block 2 read.
+  // Prologue: block 0 in LDS, LUT entry of block 1 read.
   issue_block(kb_of(0), 0);
   wait_dma();
   __syncthreads();
-  if (nloc > 1) issue_block(kb_of(1), 1);
-  int kb_ahead = nloc > 2 ? kb_of(2) : 0;
-  // Causal masking needs the block index of the step: kb_cur (block it) and
-  // kb_nxt (block it+1) trail kb_ahead.
+  int kb_ahead = nloc > 1 ? kb_of(1) : 0;
   int kb_cur = CAUSAL ? kb_of(0) : 0;
-  int kb_nxt = CAUSAL && nloc > 1 ? kb_of(1) : 0;
 
   // One 64-key block out of LDS buffer `cur` (a compile-time constant, so
   // every LDS address is a fixed register plus an immediate offset).
@@ -248,6 +246,8 @@ void fmha_block_kernel(FmhaArgs a) {
     for (int kk = 0; kk < NKK; ++kk) s = mfma32<E>(kf[kk], qf[kk], s);
     read_vt(1);
     __builtin_amdgcn_sched_barrier(0);
+    // The other buffer held block it-1, released by the last barrier.
+    if (it + 1 < nloc) issue_block(kb_ahead, 1 - cur);
 
     if constexpr (CAUSAL) {
       // Key 64 kb + 32 kh + 8 (r/4) + 4 hl + r%4 of register r against query
@@ -311,22 +311,17 @@ void fmha_block_kernel(FmhaArgs a) {
       }
     }
 
-    // The LUT entry of block it+3 is requested only now, after this block's
+    // The LUT entry of block it+2 is requested only now, after this block's
     // last LDS wait: scalar loads share the LDS wait counter but may return
     // out of order, so one in flight would turn every partial LDS wait above
     // into a full one.  The next step consumes it first thing.
     __builtin_amdgcn_sched_barrier(0);
-    const int kb_next = it + 3 < nloc ? kb_of(it + 3) : 0;
+    const int kb_next = it + 2 < nloc ? kb_of(it + 2) : 0;
 
-    // Block it+1 must have landed before the barrier hands the buffers over;
-    // then the buffer just consumed receives block it+2.
+    // Block it+1 must have landed before the barrier hands the buffers over.
     wait_dma();
     __syncthreads();
-    if (it + 2 < nloc) issue_block(kb_ahead, cur);
-    if constexpr (CAUSAL) {
-      kb_cur = kb_nxt;
-      kb_nxt = kb_ahead;
-    }
+    if constexpr (CAUSAL) kb_cur = kb_ahead;
     kb_ahead = kb_next;
   };
 

@@ -16,8 +16,8 @@
 //   * a K block is 64 rows of d bytes in LDS, half the bytes of fp16, so the
 //     direct loads write half as much into LDS and the operand reads of K
 //     halve;
-//   * the K scale of every block comes through the scalar cache next to its
-//     LUT entry, requested after the block's last LDS wait like the entry.
+//   * the K scale of every block comes through the scalar cache, requested
+//     one step ahead next to a LUT entry, after the block's last LDS wait.
 // V and P stay in fp16 / bf16 and the PV product is the one of the fp16 / bf16
 // kernel.
 #include "attn_common.h"
@@ -163,25 +163,23 @@ void fmha_qk8_kernel(FmhaArgs a) {
   const int vrow0 = 32 * kh + 4 * (vgrp >> 1) + (vs16 >> 2);
   const int vcol0 = 16 * (vgrp & 1) + 4 * (vs16 & 3);
 
+  // Block 0 in LDS; the LUT entry of block 1 and the K scale of block 0 read.
+  // Block it+1's K/V loads are issued in the middle of step it (as in the
+  // fp16 / bf16 kernel).
   issue_block(kb_of(0), 0);
   wait_dma();
   __syncthreads();
-  if (nloc > 1) issue_block(kb_of(1), 1);
-  int kb_ahead = nloc > 2 ? kb_of(2) : 0;
-  // K scales of blocks it (sk_cur) and it+1 (sk_nxt); block it+2's is
-  // requested at the end of step it.
+  int kb_ahead = nloc > 1 ? kb_of(1) : 0;
   float sk_cur = ksc[kb_of(0)];
-  float sk_nxt = nloc > 1 ? ksc[kb_of(1)] : 0.f;
   int kb_cur = CAUSAL ? kb_of(0) : 0;
-  int kb_nxt = CAUSAL && nloc > 1 ? kb_of(1) : 0;
 
   auto step = [&](int it, auto cur_tag) {
     constexpr int cur = decltype(cur_tag)::value;
     const int8_t* kt = &sK[cur * TILE];
     const SPARGE_LDS T* vt = (const SPARGE_LDS T*)&sV[cur * TILE];
 
-    // The scalar loads of the previous step (and of the prologue) have landed.
-    asm volatile("" ::"s"(kb_ahead), "s"(sk_cur), "s"(sk_nxt));
+    // The scalar loads of the previous step (or of the prologue) have landed.
+    asm volatile("" ::"s"(kb_ahead), "s"(sk_cur));
     u32x4 kf[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -214,6 +212,8 @@ void fmha_qk8_kernel(FmhaArgs a) {
     for (int kk = 0; kk < NKK; ++kk) si = mfma_i8(kf[kk], qf[kk], si);
     read_vt(1);
     __builtin_amdgcn_sched_barrier(0);
+    // The other buffer held block it-1, released by the last barrier.
+    if (it + 1 < nloc) issue_block(kb_ahead, 1 - cur);
 
     float s[16];
 #pragma unroll
@@ -263,21 +263,17 @@ void fmha_qk8_kernel(FmhaArgs a) {
       for (int md = 0; md < NMD; ++md) acc_o[md] = mfma32<E>(vf[ks][md], pf[ks], acc_o[md]);
     }
 
-    // After the last LDS wait: the LUT entry of block it+3 and the K scale of
-    // block it+2 (kb_ahead), both consumed first thing in the next step.
+    // After the last LDS wait: the LUT entry of block it+2 and the K scale of
+    // block it+1 (kb_ahead), both consumed first thing in the next step.
     __builtin_amdgcn_sched_barrier(0);
-    const int kb_next = it + 3 < nloc ? kb_of(it + 3) : 0;
-    const float sk_next = it + 2 < nloc ? ksc[kb_ahead] : 0.f;
+    const int kb_next = it + 2 < nloc ? kb_of(it + 2) : 0;
+    const float sk_next = it + 1 < nloc ? ksc[kb_ahead] : 0.f;
 
+    // Block it+1 must have landed before the barrier hands the buffers over.
     wait_dma();
     __syncthreads();
-    if (it + 2 < nloc) issue_block(kb_ahead, cur);
-    if constexpr (CAUSAL) {
-      kb_cur = kb_nxt;
-      kb_nxt = kb_ahead;
-    }
-    sk_cur = sk_nxt;
-    sk_nxt = sk_next;
+    if constexpr (CAUSAL) kb_cur = kb_ahead;
+    sk_cur = sk_next;
     kb_ahead = kb_next;
   };
 

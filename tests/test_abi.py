@@ -92,6 +92,9 @@ def _bm(lib, **kw):
     (dict(s_k=100), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(blk_q=128), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(h=0), ops.SPARGE_ERR_INVALID),
+    (dict(b=0), ops.SPARGE_ERR_INVALID),                             # empty batch
+    (dict(s_q=0), ops.SPARGE_ERR_INVALID),                           # empty sequence
+    (dict(s_k=0), ops.SPARGE_ERR_INVALID),
     (dict(h=200), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(s_k=64 * 1025), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(qs=_s3(65536, 32768, 60)), ops.SPARGE_ERR_INVALID),
@@ -142,6 +145,9 @@ def _fmha(lib, **kw):
     (dict(bq=64, bk=1), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(lh=4), ops.SPARGE_ERR_INVALID),
     (dict(L=0), ops.SPARGE_ERR_INVALID),
+    (dict(b=0), ops.SPARGE_ERR_INVALID),                             # empty inputs
+    (dict(sq=0), ops.SPARGE_ERR_INVALID),
+    (dict(sk=0), ops.SPARGE_ERR_INVALID),
     (dict(splits=0), ops.SPARGE_ERR_INVALID),
     (dict(splits=2, lse=None), ops.SPARGE_ERR_INVALID),
     (dict(splits=2, sst=12), ops.SPARGE_ERR_INVALID),
@@ -184,6 +190,8 @@ def _fmha8(lib, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(qsc=None), ops.SPARGE_ERR_INVALID),
+    (dict(b=0), ops.SPARGE_ERR_INVALID),
+    (dict(sq=0), ops.SPARGE_ERR_INVALID),
     (dict(ksc=None), ops.SPARGE_ERR_INVALID),
     (dict(v=None), ops.SPARGE_ERR_INVALID),
     (dict(vdt=ops.SPARGE_F32), ops.SPARGE_ERR_UNSUPPORTED),
@@ -208,6 +216,8 @@ def test_fmha_qk_int8_rejections(lib, kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(parts=None), ops.SPARGE_ERR_INVALID),
     (dict(n=0), ops.SPARGE_ERR_INVALID),
+    (dict(b=0), ops.SPARGE_ERR_INVALID),
+    (dict(s=0), ops.SPARGE_ERR_INVALID),
     (dict(n=300), ops.SPARGE_ERR_INVALID),
     (dict(d=32), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(stride=100), ops.SPARGE_ERR_INVALID),

@@ -436,6 +436,34 @@ def test_decode_ragged_lists(dev, dtype, d, splits):
     assert (o[1, 4:8].float() == 0).all() and torch.isneginf(lse[1, 4:8]).all()
 
 
+@pytest.mark.parametrize("h_q,h_kv,s_q", [
+    (4, 4, 1),     # 1 query row per KV head (plain multi-head)
+    (4, 2, 1),     # 2 rows
+    (6, 2, 1),     # 3 rows, served by the 4-row kernel with one idle row
+    (8, 1, 1),     # 8 rows
+    (4, 2, 2),     # 2 heads x 2 query positions
+    (2, 1, 3),     # 2 heads x 3 positions: 6 rows in the 8-row kernel
+])
+def test_decode_row_groups(dev, h_q, h_kv, s_q):
+    # Every row count the token-list kernel is built for (1, 2, 4, 8 rows per
+    # KV head, up to the 8 allowed), with idle template rows and several query
+    # positions sharing one list.
+    b, s_k, d, L = 3, 3000, 128, 200
+    q = synth.normal((b, h_q, s_q, d), 61, 1, torch.bfloat16, dev, scale=4.0)
+    k = synth.normal((b, h_kv, s_k, d), 61, 2, torch.bfloat16, dev)
+    v = synth.normal((b, h_kv, s_k, d), 61, 3, torch.bfloat16, dev)
+    lists = synth.token_lists(b, h_kv, L, s_k, 61, 4, True).to(dev)
+    op, lp = ops.sparse_fmha_fwd(q, k, v, lists, None, blk_q=1, blk_k=1, num_splits=2)
+    o, lse = ops.attn_combine(op, lp, out_dtype=torch.bfloat16)
+    o1, l1 = ops.sparse_fmha_fwd(q, k, v, lists, None, blk_q=1, blk_k=1)
+    _sync()
+    ro, rl = oracle.token_list_attention(np64(q), np64(k), np64(v), lists.cpu().numpy())
+    check_o(o, ro)
+    check_lse(lse, rl)
+    check_o(o1, ro)
+    check_lse(l1, rl)
+
+
 def test_decode_full_size_sampled(dev):
     c = synth.decode_case(dev)                 # b64 h_q32 h_kv8 s_k32768 d128 bf16, L 2048
     op, lp = ops.sparse_fmha_fwd(c.q, c.k, c.v, c.lists, None, blk_q=1, blk_k=1, num_splits=8)

@@ -184,3 +184,42 @@ def test_headline_sampled_heads(dev):
                        bm["count"][:, heads])
     check_o(o[:, heads], ro)
     check_lse(lse[:, heads], rl)
+
+
+def test_causal_end_to_end_with_smoothing_and_sink(dev):
+    # Causal block map (K smoothing, attention sink) with the int8 codes, then
+    # the causal int8-QK FMHA on its LUT.
+    case = synth.mid_case(dev)
+    bm = ops.build_block_map(case.q, case.k, case.topk, case.simthreshd1, smooth_k=True, causal=True,
+                             attention_sink=True, quantize_int8=True)
+    o, lse = ops.sparse_fmha_fwd_qk_int8(bm["q_i8"], bm["q_i8_scale"], bm["k_i8"], bm["k_i8_scale"],
+                                         case.v, bm["lut"], bm["count"], causal=True)
+    torch.cuda.synchronize()
+    _check_codes(bm, case.q, case.k)
+    ro, rl = _attn_ref(case.q, case.k, case.v, bm["lut"], bm["count"], causal=True)
+    check_o(o, ro)
+    check_lse(lse, rl)
+
+
+def test_strided_views(dev):
+    # Codes and V read through views with padded rows and a transposed
+    # (b, s, h, d) storage order; the output written into a padded view.
+    b, h, s, d = 2, 3, 512, 128
+    q = synth.normal((b, h, s, d), 71, 1, torch.float16, dev)
+    k = synth.normal((b, h, s, d), 71, 2, torch.float16, dev)
+    v = synth.normal((b, h, s, d), 71, 3, torch.float16, dev)
+    q8, qs = _codes_on_gpu(q, dev)
+    k8, ks = _codes_on_gpu(k, dev)
+    q8p = torch.zeros((b, h, s, d + 32), dtype=torch.int8, device=dev)[..., :d]
+    q8p.copy_(q8)
+    k8t = k8.transpose(1, 2).contiguous().transpose(1, 2)           # (b, s, h, d) storage
+    vt = v.transpose(1, 2).contiguous().transpose(1, 2)
+    o = torch.zeros((b, h, s, d + 64), dtype=torch.float16, device=dev)[..., :d]
+    nq = s // 64
+    lut = torch.arange(nq, dtype=torch.int32, device=dev).flip(0).sort().values.repeat(b, h, nq, 1).contiguous()
+    cnt = torch.full((b, h, nq), nq, dtype=torch.int32, device=dev)
+    _, lse = ops.sparse_fmha_fwd_qk_int8(q8p, qs, k8t, ks, vt, lut, cnt, o=o)
+    torch.cuda.synchronize()
+    ro, rl = _attn_ref(q, k, v, lut, cnt)
+    check_o(o, ro)
+    check_lse(lse, rl)

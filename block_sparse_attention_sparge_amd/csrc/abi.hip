@@ -361,7 +361,7 @@ sparge_status attn_combine(const void* o_parts, sparge_dtype part_dt, const floa
                            int b, int h, int s, int d, int64_t part_stride, void* o, sparge_dtype out_dt,
                            float* lse_out, void* stream) {
   if (!o_parts || !lse_parts || !o) return fail(SPARGE_ERR_INVALID, "o_parts, lse_parts and o must be non-null");
-  if (n_parts < 1 || n_parts > 256) return fail(SPARGE_ERR_INVALID, "n_parts=%d out of [1, 256]", n_parts);
+  if (n_parts < 1 || n_parts > 1024) return fail(SPARGE_ERR_INVALID, "n_parts=%d out of [1, 1024]", n_parts);
   if (b <= 0 || h <= 0 || s <= 0 || d <= 0) return fail(SPARGE_ERR_INVALID, "sizes must be positive");
   if (d != 64 && d != 128) return fail(SPARGE_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", d);
   if (part_dt != SPARGE_F32 && !is_half(part_dt)) return fail(SPARGE_ERR_INVALID, "bad part dtype");

@@ -256,7 +256,7 @@ sparge_status sparse_fmha_fwd_qk_int8(
  * lse_parts float [n_parts][b, h, s] contiguous.
  * o         [b, h, s, d] contiguous in out_dt (F32, F16 or BF16).
  * lse_out   float [b, h, s] or NULL.
- * 1 <= n_parts <= 256; d in {64, 128}.
+ * 1 <= n_parts <= 1024 (the most splits sparse_fmha_fwd makes); d in {64, 128}.
  */
 sparge_status attn_combine(
     const void* o_parts, sparge_dtype part_dt, const float* lse_parts,

@@ -218,7 +218,7 @@ def test_fmha_qk_int8_rejections(lib, kw, status):
     (dict(n=0), ops.SPARGE_ERR_INVALID),
     (dict(b=0), ops.SPARGE_ERR_INVALID),
     (dict(s=0), ops.SPARGE_ERR_INVALID),
-    (dict(n=300), ops.SPARGE_ERR_INVALID),
+    (dict(n=1025), ops.SPARGE_ERR_INVALID),
     (dict(d=32), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(stride=100), ops.SPARGE_ERR_INVALID),
     (dict(pdt=7), ops.SPARGE_ERR_INVALID),

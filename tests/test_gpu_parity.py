@@ -85,6 +85,22 @@ def test_combine_matches_oracle(dev, pdt, d, n):
     assert (np64(o)[1, 2, 5:9] == 0).all()
 
 
+def test_combine_many_parts(dev):
+    # 1024 parts, the most splits sparse_fmha_fwd makes, most of them empty on
+    # some rows.
+    n, b, h, s, d = 1024, 1, 2, 16, 64
+    g = torch.Generator(device=dev).manual_seed(11)
+    parts = torch.randn(n, b, h, s, d, generator=g, device=dev)
+    lse = torch.randn(n, b, h, s, generator=g, device=dev) * 4
+    lse[::3, 0, 1, :8] = -math.inf
+    o, l = ops.attn_combine(parts, lse)
+    _sync()
+    ro, rl = oracle.combine(list(np64(parts)), list(np64(lse)))
+    # fp32 sums of up to 1024 terms: up to ~1024 * 2^-24 relative error
+    check_o(o, ro, atol=1e-4, rtol=1e-4, what="combined O")
+    check_lse(l, rl, tol=1e-4)
+
+
 def test_combine_partials_with_stride_padding(dev):
     n, b, h, s, d = 3, 1, 2, 33, 128
     g = torch.Generator(device=dev).manual_seed(7)

@@ -27,7 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16 MFMA
+PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16 / bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the sparse FMHA (bytes per launch,
 # copy-calibrated); quoted only while it matches the current kernel source.
@@ -237,6 +237,20 @@ def extras(ops, synth, torch, steps, warmup):
         workload="b2 h32 s16384 d128 fp16, topk 0.4, pv_threshold 0 / 4 / 8",
         fmha_ms_no_skip=pv[0.0], fmha_ms_tau4=pv[4.0], fmha_ms_tau8=pv[8.0],
         speedup_tau4=pv[0.0] / pv[4.0], speedup_tau8=pv[0.0] / pv[8.0])
+    # The same shape in bf16 (topk 0.4): block map and sparse FMHA.
+    hb = synth.headline_case(dev, topk=0.4, dtype=torch.bfloat16)
+    bmb = ops.build_block_map(hb.q, hb.k, hb.topk, hb.simthreshd1)
+    ob = torch.empty_like(hb.q)
+    _, bmt = time_arm(lambda: ops.build_block_map(hb.q, hb.k, hb.topk, hb.simthreshd1, out=bmb), steps, warmup,
+                      torch)
+    _, ft = time_arm(lambda: ops.sparse_fmha_fwd(hb.q, hb.k, hb.v, bmb["lut"], bmb["count"], o=ob, lse=l),
+                     steps, warmup, torch)
+    pairs = int(bmb["count"].sum().item())
+    out["bf16_headline_topk_0.4"] = dict(
+        workload="b2 h32 s16384 d128 bf16, topk 0.4", block_map_ms=median(bmt), fmha_ms=median(ft),
+        pairs=pairs, fmha_tflops_computed=pairs * F_BLK / median(ft) / 1e9,
+        mfma_frac_fmha=pairs * F_BLK / median(ft) / 1e9 / PEAK_FP16_TFLOPS)
+    del hb, bmb, ob
     # int8 Q/K at the headline shape: the block map with the fused per-block
     # quantisation, then the int8-QK sparse FMHA (V and P stay fp16).
     for topk in (0.4, 0.1):

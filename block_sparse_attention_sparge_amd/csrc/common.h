@@ -27,8 +27,6 @@ constexpr int kWave = 64;
 struct F16 {
   typedef half_t T;
   typedef half8 V8;
-  // The attention row sum may add P after rounding to this type.
-  static constexpr bool kRowSumRounded = true;
   static __device__ __forceinline__ float to_f(T x) { return (float)x; }
   static __device__ __forceinline__ T from_f(float x) { return (T)x; }
   // Convert the low / high 16-bit lane of a packed word.
@@ -43,10 +41,6 @@ struct F16 {
   static __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v{a, b}), half2v));
   }
-  // acc + lo(w) + hi(w) in fp32 (one v_dot2c_f32_f16 against (1, 1)).
-  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, w), half2v{(half_t)1.0f, (half_t)1.0f}, acc, false);
-  }
   // acc + lo(x) lo(y) + hi(x) hi(y), products exact, in fp32.
   static __device__ __forceinline__ float dot2(uint32_t x, uint32_t y, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, x), __builtin_bit_cast(half2v, y), acc, false);
@@ -56,7 +50,6 @@ struct F16 {
 struct BF16 {
   typedef bf16_t T;
   typedef bf16x8 V8;
-  static constexpr bool kRowSumRounded = false;
   static __device__ __forceinline__ float to_f(T x) { return (float)x; }
   static __device__ __forceinline__ T from_f(float x) { return (T)x; }
   static __device__ __forceinline__ float lo(uint32_t w) {
@@ -67,10 +60,6 @@ struct BF16 {
   }
   static __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v{a, b}), bf16x2v));
-  }
-  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w), bf16x2v{(bf16_t)1.0f, (bf16_t)1.0f},
-                                           acc, false);
   }
   static __device__ __forceinline__ float dot2(uint32_t x, uint32_t y, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, x), __builtin_bit_cast(bf16x2v, y), acc, false);

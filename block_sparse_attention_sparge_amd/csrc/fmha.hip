@@ -280,10 +280,9 @@ void fmha_block_kernel(FmhaArgs a) {
       for (int i = 0; i < NMD; ++i) acc_o[i] *= alpha;
     }
     // P^T fragments (k-step ks uses registers 8ks .. 8ks+7), rounded to the
-    // input type.  With fp16 the row sum adds the rounded values, the ones PV
-    // uses (rounding moves a term by at most 2^-11 of itself).  bf16 rounds by
-    // up to 2^-8, which on a row dominated by one key would move the LSE by up
-    // to 4e-3 nats, so there the row sum adds the fp32 values.
+    // input type for PV.  The row sum adds the fp32 values: rounding to the
+    // input type moves a term by up to 2^-8 of itself (bf16), which on a row
+    // carried by one key would move the LSE by up to 4e-3 nats.
     // Causal rows may still have no key (m_run = -inf): their P is 0.
     const float mref = CAUSAL && m_run == -INFINITY ? 0.f : m_run;
     u32x4 pf[2];
@@ -294,8 +293,7 @@ void fmha_block_kernel(FmhaArgs a) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w], c2, -mref));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w + 1], c2, -mref));
         pf[ks][w] = E::pack2(p0, p1);
-        if constexpr (E::kRowSumRounded) l_run = E::sum2(pf[ks][w], l_run);
-        else l_run += p0 + p1;
+        l_run += p0 + p1;
       }
     }
 

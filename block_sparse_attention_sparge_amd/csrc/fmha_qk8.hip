@@ -253,8 +253,7 @@ void fmha_qk8_kernel(FmhaArgs a) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w], c2, -mref));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w + 1], c2, -mref));
         pf[ks][w] = E::pack2(p0, p1);
-        if constexpr (E::kRowSumRounded) l_run = E::sum2(pf[ks][w], l_run);
-        else l_run += p0 + p1;
+        l_run += p0 + p1;   // fp32 row sum, as in the fp16 / bf16 kernel
       }
     }
 #pragma unroll

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparge.so")
-SOURCES = ["abi.hip", "block_map.hip", "fmha.hip", "fmha_qk8.hip", "combine.hip"]
+SOURCES = ["abi.hip", "block_map.hip", "fmha.hip", "fmha_qk8.hip", "fmha_tokens.hip", "combine.hip"]
 ARCH = "gfx950"
 
 

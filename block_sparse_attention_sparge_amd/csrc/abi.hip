@@ -259,6 +259,7 @@ sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void*
   a.causal = causal ? 1 : 0;
   a.pv_tau2 = pv_threshold * 1.4426950408889634f;
   a.q_scale = nullptr; a.k_scale = nullptr;
+  a.tok_groups = 1;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   if (block_mode) {
@@ -278,12 +279,15 @@ sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void*
   if (lut_count) return fail(SPARGE_ERR_INVALID, "token-list mode takes no lut_count");
   if (lut_heads != h_kv)
     return fail(SPARGE_ERR_UNSUPPORTED, "token-list mode needs one list per KV head (lut_heads = h_kv)");
-  const int rows = a.ratio * s_q;
-  if (rows > 8)
-    return fail(SPARGE_ERR_UNSUPPORTED, "token-list mode serves at most 8 query rows per KV head (got %d)", rows);
+  const int64_t rows = (int64_t)a.ratio * s_q;
+  if (rows > 65536)
+    return fail(SPARGE_ERR_UNSUPPORTED, "token-list mode serves at most 65536 query rows per KV head (got %lld)",
+                (long long)rows);
+  a.tok_groups = (int)((rows + 7) / 8);
   a.nqt = s_q;
   a.nkb = s_k;
-  return hip_status(launch_fmha_tokens(a, dt, o_dt, d, rows, s), "sparse_fmha token launch");
+  return hip_status(launch_fmha_tokens(a, dt, o_dt, d, (int)std::min<int64_t>(rows, 8), s),
+                    "sparse_fmha token launch");
 }
 
 sparge_status sparse_fmha_fwd_qk_int8(const int8_t* q, const float* q_scale, const int8_t* k,
@@ -351,6 +355,7 @@ sparge_status sparse_fmha_fwd_qk_int8(const int8_t* q, const float* q_scale, con
   a.causal = causal ? 1 : 0;
   a.pv_tau2 = 0.f;
   a.q_scale = q_scale; a.k_scale = k_scale;
+  a.tok_groups = 1;
   a.nqt = s_q / 64;
   a.nkb = s_k / 64;
   return hip_status(launch_fmha_qk8(a, v_dt, o_dt, d, reinterpret_cast<hipStream_t>(stream)),

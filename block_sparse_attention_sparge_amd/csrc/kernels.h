@@ -78,6 +78,9 @@ struct FmhaArgs {
   // int8-QK block kernel: q and k hold int8 codes; their per-block scales.
   const float* q_scale;    // [b, hq, nqt]
   const float* k_scale;    // [b, hkv, nkb]
+  // Token-list mode: the query rows of a KV head are served in groups of up
+  // to 8, one workgroup per group.
+  int tok_groups;
 };
 
 struct CombineArgs {

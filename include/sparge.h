@@ -174,7 +174,9 @@ size_t sparge_build_block_map_workspace(int b, int h, int s_q, int s_k, int d,
  *   lists token positions in [0, s_k); -1 entries are skipped wherever they
  *   are; the same list serves every query position (decode: s_q = 1);
  *   lut_count must be NULL; lut_heads must be h_kv (one list per KV head,
- *   shared by its query heads); h_q / h_kv * s_q <= 8.
+ *   shared by its query heads).  The h_q / h_kv * s_q query rows of a KV
+ *   head (at most 65536) are served in groups of 8, each group gathering the
+ *   listed keys once.
  * In block mode lut_heads is h_q (one row per query head) or h_kv (a row
  * shared by the query heads of one KV head).
  *

@@ -168,7 +168,7 @@ def _fmha(lib, **kw):
     (dict(bq=1, bk=1, lut=None, cnt=None), ops.SPARGE_ERR_INVALID),
     (dict(bq=1, bk=1, cnt=FAKE, lh=2), ops.SPARGE_ERR_INVALID),
     (dict(bq=1, bk=1, cnt=None, lh=8), ops.SPARGE_ERR_UNSUPPORTED),
-    (dict(bq=1, bk=1, cnt=None, lh=2, sq=4), ops.SPARGE_ERR_UNSUPPORTED),   # 16 rows per KV head
+    (dict(bq=1, bk=1, cnt=None, lh=2, sq=16385), ops.SPARGE_ERR_UNSUPPORTED),   # 65540 rows per KV head (limit 65536)
 ])
 def test_fmha_rejections(lib, kw, status):
     st = _fmha(lib, **kw)

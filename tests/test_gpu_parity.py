@@ -459,11 +459,14 @@ def test_decode_ragged_lists(dev, dtype, d, splits):
     (8, 1, 1),     # 8 rows
     (4, 2, 2),     # 2 heads x 2 query positions
     (2, 1, 3),     # 2 heads x 3 positions: 6 rows in the 8-row kernel
+    (8, 2, 3),     # 12 rows: groups of 8 and 4
+    (8, 2, 4),     # 16 rows: two full groups
+    (16, 2, 5),    # 40 rows: five groups
 ])
 def test_decode_row_groups(dev, h_q, h_kv, s_q):
     # Every row count the token-list kernel is built for (1, 2, 4, 8 rows per
-    # KV head, up to the 8 allowed), with idle template rows and several query
-    # positions sharing one list.
+    # workgroup), with idle template rows, several query positions sharing one
+    # list, and more than 8 rows per KV head served by several workgroups.
     b, s_k, d, L = 3, 3000, 128, 200
     q = synth.normal((b, h_q, s_q, d), 61, 1, torch.bfloat16, dev, scale=4.0)
     k = synth.normal((b, h_kv, s_k, d), 61, 2, torch.bfloat16, dev)

@@ -275,13 +275,18 @@ def block_map(q: np.ndarray, k: np.ndarray, topk: Sequence[float],
               blk_q: int = 64, blk_k: int = 64, scale: Optional[float] = None,
               smooth_k: bool = False, causal: bool = False,
               attention_sink: bool = False) -> dict:
-    """Whole stage 1 for q [b, h, s_q, d] and k [b, h, s_k, d].
+    """Whole stage 1 for q [b, h, s_q, d] and k [b, h_kv, s_k, d], h % h_kv == 0.
 
+    With h_kv < h (grouped-query attention, reading R28) query head j pools
+    against KV head j // (h / h_kv), as attention does (aiter 6841 page, GQA
+    mapping): its pooled scores use that head's K block means, and the K gate
+    of row j compares that head's K block similarity with simthreshd1[j].
     `smooth_k` pools and gates K after `smooth_keys`; `causal` applies the
     causal block mask (requires s_q = s_k and blk_q = blk_k); `attention_sink`
-    forces block 0 in every row.  Returns a dict with q_mean, k_mean (of the
-    smoothed K when smoothing), sim_q_val, sim_k_val, sim_q, sim_k, scores,
-    prob, lut, count, bitmap.
+    forces block 0 in every row.  Returns a dict with q_mean [b, h, nq, d],
+    k_mean [b, h_kv, nk, d] (of the smoothed K when smoothing), sim_q_val,
+    sim_k_val [b, h_kv, nk], sim_q, sim_k [b, h, nk] (the K gate as row j sees
+    it), scores, prob, lut, count, bitmap.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -290,24 +295,29 @@ def block_map(q: np.ndarray, k: np.ndarray, topk: Sequence[float],
     if smooth_k:
         k = smooth_keys(k)
     b, h, s_q, d = q.shape
-    s_k = k.shape[2]
+    h_kv, s_k = k.shape[1], k.shape[2]
+    if h % h_kv:
+        raise ValueError("the query heads must be a multiple of the KV heads")
+    ratio = h // h_kv
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     nq, nk = s_q // blk_q, s_k // blk_k
     q_mean = np.zeros((b, h, nq, d))
-    k_mean = np.zeros((b, h, nk, d))
+    k_mean = np.zeros((b, h_kv, nk, d))
     sim_q_val = np.zeros((b, h, nq))
-    sim_k_val = np.zeros((b, h, nk))
+    sim_k_val = np.zeros((b, h_kv, nk))
     sim_q = np.zeros((b, h, nq), dtype=bool)
     sim_k = np.zeros((b, h, nk), dtype=bool)
     scores = np.zeros((b, h, nq, nk))
     for ib in range(b):
+        for ik in range(h_kv):
+            k_mean[ib, ik], sim_k_val[ib, ik], _ = pool_and_gate(k[ib, ik], blk_k, 0.0)
         for ih in range(h):
+            ik = ih // ratio
             q_mean[ib, ih], sim_q_val[ib, ih], sim_q[ib, ih] = pool_and_gate(
                 q[ib, ih], blk_q, simthreshd1[ih])
-            k_mean[ib, ih], sim_k_val[ib, ih], sim_k[ib, ih] = pool_and_gate(
-                k[ib, ih], blk_k, simthreshd1[ih])
-            scores[ib, ih] = pooled_scores(q_mean[ib, ih], k_mean[ib, ih],
+            sim_k[ib, ih] = sim_k_val[ib, ik] > simthreshd1[ih]
+            scores[ib, ih] = pooled_scores(q_mean[ib, ih], k_mean[ib, ik],
                                            sim_k[ib, ih], scale, causal)
     prob = row_softmax(scores)
     lut, count, bitmap = select_from_probs(prob, sim_q, sim_k, topk, cdfthreshd,

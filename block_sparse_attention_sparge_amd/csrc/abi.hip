@@ -61,7 +61,7 @@ sparge_status check_strides(const char* name, const int64_t* st) {
 bool is_half(sparge_dtype dt) { return dt == SPARGE_F16 || dt == SPARGE_BF16; }
 
 struct BlockMapLayout {
-  size_t q_mean, k_mean, sim_q, sim_k, km_part, total;
+  size_t q_mean, k_mean, sim_q, k_sim, km_part, total;
   int km_chunks;
 };
 
@@ -73,7 +73,7 @@ BlockMapLayout block_map_layout(int b, int h, int s_q, int s_k, int d) {
   l.q_mean = off; off = align256(off + bh * nq * d * sizeof(float));
   l.k_mean = off; off = align256(off + bh * nk * d * sizeof(float));
   l.sim_q = off;  off = align256(off + bh * nq);
-  l.sim_k = off;  off = align256(off + bh * nk);
+  l.k_sim = off;  off = align256(off + bh * nk * sizeof(float));
   l.km_part = off; off = align256(off + bh * (size_t)l.km_chunks * d * sizeof(float));
   l.total = off;
   return l;
@@ -83,7 +83,7 @@ BlockMapLayout block_map_layout(int b, int h, int s_q, int s_k, int d) {
 
 extern "C" {
 
-int sparge_abi_version(void) { return 4; }
+int sparge_abi_version(void) { return 5; }
 
 const char* sparge_last_error(void) { return g_error.c_str(); }
 
@@ -94,7 +94,7 @@ size_t sparge_build_block_map_workspace(int b, int h, int s_q, int s_k, int d, i
 }
 
 sparge_status sparge_build_block_map(
-    const void* q, const void* k, sparge_dtype dt, int b, int h, int s_q, int s_k, int d,
+    const void* q, const void* k, sparge_dtype dt, int b, int h, int h_kv, int s_q, int s_k, int d,
     const int64_t q_strides[3], const int64_t k_strides[3], int blk_q, int blk_k,
     const float* topk, const float* cdfthreshd, const float* simthreshd1, float softmax_scale,
     unsigned flags, int32_t* lut, int32_t* lut_count, uint8_t* block_map, float* pooled_prob, uint8_t* sim_q,
@@ -104,8 +104,10 @@ sparge_status sparge_build_block_map(
   if (!lut || !lut_count) return fail(SPARGE_ERR_INVALID, "lut and lut_count must be non-null");
   if (!topk || !simthreshd1) return fail(SPARGE_ERR_INVALID, "topk and simthreshd1 must be non-null");
   if (!is_half(dt)) return fail(SPARGE_ERR_UNSUPPORTED, "q/k dtype must be F16 or BF16");
-  if (b <= 0 || h <= 0 || s_q <= 0 || s_k <= 0 || d <= 0)
-    return fail(SPARGE_ERR_INVALID, "sizes must be positive (b=%d h=%d s_q=%d s_k=%d d=%d)", b, h, s_q, s_k, d);
+  if (b <= 0 || h <= 0 || h_kv <= 0 || s_q <= 0 || s_k <= 0 || d <= 0)
+    return fail(SPARGE_ERR_INVALID, "sizes must be positive (b=%d h=%d h_kv=%d s_q=%d s_k=%d d=%d)", b, h, h_kv,
+                s_q, s_k, d);
+  if (h % h_kv) return fail(SPARGE_ERR_INVALID, "h=%d is not a multiple of h_kv=%d", h, h_kv);
   if (d != 64 && d != 128) return fail(SPARGE_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", d);
   if (blk_q != 64 || blk_k != 64)
     return fail(SPARGE_ERR_UNSUPPORTED, "block map needs blk_q = blk_k = 64 (got %d, %d)", blk_q, blk_k);
@@ -145,6 +147,7 @@ sparge_status sparge_build_block_map(
     if (!isfinite(tk) || tk > 1.f) return fail(SPARGE_ERR_INVALID, "topk[%d]=%g must be finite and <= 1", i, tk);
     if (!isfinite(thr)) return fail(SPARGE_ERR_INVALID, "simthreshd1[%d] is not finite", i);
     pa.thr[i] = thr;
+    sa.thr[i] = thr;
     if (tk > 0.f) {
       long n = (long)floor((double)tk * (double)nk);
       if (n < 1) n = 1;
@@ -160,25 +163,26 @@ sparge_status sparge_build_block_map(
       sa.cdf[i] = c;
     }
   }
-  for (int i = h; i < SPARGE_MAX_HEADS; ++i) { pa.thr[i] = 0.f; sa.nsel[i] = 1; sa.cdf[i] = 0.f; }
+  for (int i = h; i < SPARGE_MAX_HEADS; ++i) { pa.thr[i] = 0.f; sa.thr[i] = 0.f; sa.nsel[i] = 1; sa.cdf[i] = 0.f; }
 
   char* ws = reinterpret_cast<char*>(workspace);
   pa.q = q;
   pa.k = k;
   for (int i = 0; i < 3; ++i) { pa.qs[i] = q_strides[i]; pa.ks[i] = k_strides[i]; }
-  pa.b = b; pa.h = h; pa.nq = nq; pa.nk = nk;
+  pa.b = b; pa.h = h; pa.h_kv = h_kv; pa.nq = nq; pa.nk = nk;
   pa.q_mean = q_mean ? q_mean : reinterpret_cast<float*>(ws + lay.q_mean);
   pa.k_mean = k_mean ? k_mean : reinterpret_cast<float*>(ws + lay.k_mean);
   pa.sim_q = sim_q ? sim_q : reinterpret_cast<uint8_t*>(ws + lay.sim_q);
-  pa.sim_k = sim_k ? sim_k : reinterpret_cast<uint8_t*>(ws + lay.sim_k);
+  pa.k_sim = reinterpret_cast<float*>(ws + lay.k_sim);
   const bool smooth = (flags & SPARGE_FLAG_SMOOTH_K) != 0;
   pa.km_part = smooth ? reinterpret_cast<float*>(ws + lay.km_part) : nullptr;
   pa.km_chunks = lay.km_chunks;
   pa.km_scale = 1.0f / (float)s_k;
   pa.q_i8 = q_i8; pa.k_i8 = k_i8; pa.q_i8_scale = q_i8_scale; pa.k_i8_scale = k_i8_scale;
 
-  sa.q_mean = pa.q_mean; sa.k_mean = pa.k_mean; sa.sim_q = pa.sim_q; sa.sim_k = pa.sim_k;
-  sa.b = b; sa.h = h; sa.nq = nq; sa.nk = nk;
+  sa.q_mean = pa.q_mean; sa.k_mean = pa.k_mean; sa.sim_q = pa.sim_q; sa.k_sim = pa.k_sim;
+  sa.sim_k = sim_k;
+  sa.b = b; sa.h = h; sa.h_kv = h_kv; sa.nq = nq; sa.nk = nk;
   sa.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
   sa.lut = lut; sa.count = lut_count; sa.bmap = block_map; sa.prob = pooled_prob;
   sa.causal = causal ? 1 : 0;

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void key_mean_kernel(PoolArgs a) {
   const int tid = threadIdx.x;
   const int64_t bh = blockIdx.x / a.km_chunks;
   const int chunk = (int)(blockIdx.x % a.km_chunks);
-  const int hh = (int)(bh % a.h), bb = (int)(bh / a.h);
+  const int hh = (int)(bh % a.h_kv), bb = (int)(bh / a.h_kv);
   const int r0 = chunk * kKmChunkRows;
   const int rows = min(kKmChunkRows, a.nk * 64 - r0);
   const int c = tid % CH, rsub = tid / CH;
@@ -81,16 +81,17 @@ __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t nqb = (int64_t)a.b * a.h * a.nq;
-  const int64_t total = nqb + (int64_t)a.b * a.h * a.nk;
+  const int64_t total = nqb + (int64_t)a.b * a.h_kv * a.nk;
   if (gw >= total) return;
 
   const bool is_k = gw >= nqb;
   const int64_t idx = is_k ? gw - nqb : gw;
   const int nb = is_k ? a.nk : a.nq;
-  const int64_t bh = idx / nb;
+  const int64_t bh = idx / nb;            // (b, head) over the Q heads or the K heads
   const int blk = (int)(idx % nb);
-  const int hh = (int)(bh % a.h);
-  const int bb = (int)(bh / a.h);
+  const int nh = is_k ? a.h_kv : a.h;
+  const int hh = (int)(bh % nh);
+  const int bb = (int)(bh / nh);
   const int64_t* st = is_k ? a.ks : a.qs;
   const typename E::T* base = reinterpret_cast<const typename E::T*>(is_k ? a.k : a.q);
 
@@ -163,9 +164,11 @@ __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
     *reinterpret_cast<floatx4*>(mean + c * 8 + 4) = m1;
   }
   if (lane == 0) {
+    // Q blocks are gated here; a K block's similarity is kept for the query
+    // heads that read it, each with its own threshold.
     const float sim = dot * (1.0f / 4096.0f);
-    uint8_t* flags = is_k ? a.sim_k : a.sim_q;
-    flags[bh * nb + blk] = sim > a.thr[hh] ? 1 : 0;
+    if (is_k) a.k_sim[bh * nb + blk] = sim;
+    else a.sim_q[bh * nb + blk] = sim > a.thr[hh] ? 1 : 0;
   }
 
   if constexpr (QUANT) {
@@ -290,7 +293,9 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
   const int qb0 = (int)(lin % groups) * kSelRows;
   const int rows = min(kSelRows, a.nq - qb0);
   const int hh = (int)(bh % a.h);
+  const int64_t bkv = (bh / a.h) * a.h_kv + hh / (a.h / a.h_kv);   // the K head query head hh reads
   const int nk = a.nk;
+  const float thr = a.thr[hh];
 
   // Pooled scores with fp32 MFMA (16x16x4: exact products, fp32 sums).  The
   // contraction over the head dimension may visit it in any order as long as
@@ -308,8 +313,8 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
       if (m16 < rows) qf[g] = *reinterpret_cast<const floatx4*>(qrow + 16 * g);
     }
   }
-  const float* km = a.k_mean + bh * nk * D;
-  const uint8_t* simk = a.sim_k + bh * nk;
+  const float* km = a.k_mean + bkv * nk * D;
+  const float* ksim = a.k_sim + bkv * nk;
   auto load_k = [&](floatx4 (&kf)[NG], int kb) {
     const float* krow = km + (int64_t)kb * D + 4 * k4;
 #pragma unroll
@@ -332,7 +337,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
     }
     // C: lane holds column kb for rows 4*k4 .. 4*k4+3.  Causal: block kb is
     // in the future of Q-tile qb0 + row when kb > qb0 + row.
-    const bool live = kb < nk && simk[kb] != 0;
+    const bool live = kb < nk && ksim[kb] > thr;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok = live && (!a.causal || kb <= qb0 + 4 * k4 + i);
@@ -348,7 +353,12 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
     const int e = lane * KPL + j;
-    kgate[j] = e < nk && simk[e] == 0;                 // K block forced on
+    kgate[j] = e < nk && !(ksim[e] > thr);             // K block forced on
+  }
+  if (a.sim_k && qb0 == 0 && wave == 0) {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j)
+      if (lane * KPL + j < nk) a.sim_k[bh * nk + lane * KPL + j] = kgate[j] ? 0 : 1;
   }
   const bool qflag_lane = lane < rows && a.sim_q[bh * a.nq + qb0 + lane] != 0;
   const uint64_t qflags = __ballot(qflag_lane);
@@ -571,7 +581,7 @@ static void launch_pool_v(const PoolArgs& a, int d, dim3 grid, hipStream_t st) {
 
 template <class E>
 static hipError_t launch_pool_t(const PoolArgs& a, int d, hipStream_t st) {
-  const int64_t waves = (int64_t)a.b * a.h * (a.nq + a.nk);
+  const int64_t waves = (int64_t)a.b * (a.h * a.nq + a.h_kv * a.nk);
   const dim3 grid((unsigned)((waves + 3) / 4));
   if (a.q_i8) launch_pool_v<E, true>(a, d, grid, st);
   else launch_pool_v<E, false>(a, d, grid, st);
@@ -580,7 +590,7 @@ static hipError_t launch_pool_t(const PoolArgs& a, int d, hipStream_t st) {
 
 template <class E>
 static hipError_t launch_key_mean_t(const PoolArgs& a, int d, hipStream_t st) {
-  const dim3 grid((unsigned)((int64_t)a.b * a.h * a.km_chunks));
+  const dim3 grid((unsigned)((int64_t)a.b * a.h_kv * a.km_chunks));
   if (d == 128) hipLaunchKernelGGL((key_mean_kernel<E, 128>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((key_mean_kernel<E, 64>), grid, dim3(256), 0, st, a);
   return hipGetLastError();

@@ -17,10 +17,11 @@ struct PoolArgs {
   int64_t qs[3];
   int64_t ks[3];
   int b, h, nq, nk;
+  int h_kv;          // K heads (h is a multiple)
   float* q_mean;     // [b, h, nq, d]
-  float* k_mean;     // [b, h, nk, d]
-  uint8_t* sim_q;    // [b, h, nq]
-  uint8_t* sim_k;    // [b, h, nk]
+  float* k_mean;     // [b, h_kv, nk, d]
+  uint8_t* sim_q;    // [b, h, nq] Q gate flags
+  float* k_sim;      // [b, h_kv, nk] K block similarity (each query head gates it)
   // K smoothing: per-chunk sums of K over the sequence, [b, h, km_chunks, d];
   // km = (sum over chunks) * km_scale.  Null when K is pooled as given.
   float* km_part;
@@ -40,10 +41,12 @@ constexpr int kKmChunkRows = 1024;
 
 struct SelectArgs {
   const float* q_mean;
-  const float* k_mean;
+  const float* k_mean;     // [b, h_kv, nk, d]
   const uint8_t* sim_q;
-  const uint8_t* sim_k;
+  const float* k_sim;      // [b, h_kv, nk]
+  uint8_t* sim_k;          // [b, h, nk] K gate flags as each query head sees them, or null
   int b, h, nq, nk;
+  int h_kv;
   float scale;
   int32_t* lut;      // [b, h, nq, nk]
   int32_t* count;    // [b, h, nq]
@@ -53,6 +56,7 @@ struct SelectArgs {
   int sink;          // block 0 forced on
   int nsel[SPARGE_MAX_HEADS];   // > 0: top-k count; <= 0: cdf mode
   float cdf[SPARGE_MAX_HEADS];
+  float thr[SPARGE_MAX_HEADS];  // simthreshd1
 };
 
 struct FmhaArgs {

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libsparge.so")
 SPARGE_OK, SPARGE_ERR_INVALID, SPARGE_ERR_UNSUPPORTED, SPARGE_ERR_HIP = 0, 1, 2, 3
 SPARGE_F16, SPARGE_BF16, SPARGE_F32 = 0, 1, 2
 SPARGE_FLAG_SMOOTH_K, SPARGE_FLAG_CAUSAL, SPARGE_FLAG_ATTN_SINK = 1, 2, 4
-ABI_VERSION = 4
+ABI_VERSION = 5
 MAX_HEADS = 128
 MAX_KBLOCKS = 1024
 
@@ -76,7 +76,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         lib.sparge_build_block_map_workspace.argtypes = [_i] * 7
         lib.sparge_build_block_map.restype = _i
         lib.sparge_build_block_map.argtypes = [
-            _p, _p, _i, _i, _i, _i, _i, _i, _I64x3, _I64x3, _i, _i,
+            _p, _p, _i, _i, _i, _i, _i, _i, _i, _I64x3, _I64x3, _i, _i,
             _p, _p, _p, _f, _u, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
         lib.sparse_fmha_fwd.restype = _i
         lib.sparse_fmha_fwd.argtypes = [
@@ -167,21 +167,24 @@ def build_block_map(q: torch.Tensor, k: torch.Tensor, topk, simthreshd1, cdfthre
                     return_debug: bool = False, workspace: Optional[torch.Tensor] = None,
                     out: Optional[dict] = None, smooth_k: bool = False, causal: bool = False,
                     attention_sink: bool = False, quantize_int8: bool = False) -> dict:
-    """Stage 1 (sparge_build_block_map).  q [b, h, s_q, d], k [b, h, s_k, d].
+    """Stage 1 (sparge_build_block_map).  q [b, h, s_q, d], k [b, h_kv, s_k, d]
+    with h a multiple of h_kv (query head j reads K head j // (h / h_kv)).
 
     Returns a dict with 'lut' int32 [b, h, nq, nk], 'count' int32 [b, h, nq],
     and with return_debug also 'bitmap', 'prob', 'sim_q', 'sim_k', 'q_mean',
     'k_mean'.  `out` may hold preallocated tensors under the same keys (plus
     'workspace').  smooth_k / causal / attention_sink set SPARGE_FLAG_SMOOTH_K /
     SPARGE_FLAG_CAUSAL / SPARGE_FLAG_ATTN_SINK.  quantize_int8 also returns the
-    per-block int8 codes 'q_i8' [b, h, s_q, d], 'k_i8' [b, h, s_k, d] and their
-    scales 'q_i8_scale' [b, h, nq], 'k_i8_scale' [b, h, nk].
+    per-block int8 codes 'q_i8' [b, h, s_q, d], 'k_i8' [b, h_kv, s_k, d] and their
+    scales 'q_i8_scale' [b, h, nq], 'k_i8_scale' [b, h_kv, nk]; 'k_mean' is
+    [b, h_kv, nk, d] and 'sim_k' [b, h, nk] (the K gate as each query head
+    sees it).
     """
     lib = load_library()
     dev = _on_gpu(q, k)
     b, h, s_q, d = q.shape
-    s_k = k.shape[2]
-    if k.shape[0] != b or k.shape[1] != h or k.shape[3] != d:
+    h_kv, s_k = k.shape[1], k.shape[2]
+    if k.shape[0] != b or k.shape[3] != d or h_kv == 0 or h % h_kv:
         raise SpargeError(SPARGE_ERR_INVALID, "q and k shapes disagree")
     if q.dtype != k.dtype:
         raise SpargeError(SPARGE_ERR_INVALID, "q and k dtypes disagree")
@@ -204,13 +207,13 @@ def build_block_map(q: torch.Tensor, k: torch.Tensor, topk, simthreshd1, cdfthre
                    sim_q=get("sim_q", (b, h, nq), torch.uint8),
                    sim_k=get("sim_k", (b, h, nk), torch.uint8),
                    q_mean=get("q_mean", (b, h, nq, d), torch.float32),
-                   k_mean=get("k_mean", (b, h, nk, d), torch.float32))
+                   k_mean=get("k_mean", (b, h_kv, nk, d), torch.float32))
     qz = {}
     if quantize_int8:
         qz = dict(q_i8=get("q_i8", (b, h, s_q, d), torch.int8),
                   q_i8_scale=get("q_i8_scale", (b, h, nq), torch.float32),
-                  k_i8=get("k_i8", (b, h, s_k, d), torch.int8),
-                  k_i8_scale=get("k_i8_scale", (b, h, nk), torch.float32))
+                  k_i8=get("k_i8", (b, h_kv, s_k, d), torch.int8),
+                  k_i8_scale=get("k_i8_scale", (b, h_kv, nk), torch.float32))
         for key in ("q_i8", "k_i8"):
             if not qz[key].is_contiguous():
                 raise SpargeError(SPARGE_ERR_INVALID, f"{key} must be contiguous")
@@ -221,7 +224,7 @@ def build_block_map(q: torch.Tensor, k: torch.Tensor, topk, simthreshd1, cdfthre
         workspace = torch.empty(max(int(ws_bytes), 256), dtype=torch.uint8, device=dev)
         out["workspace"] = workspace
     st = lib.sparge_build_block_map(
-        _ptr(q), _ptr(k), _dt(q.dtype), b, h, s_q, s_k, d, _strides(q), _strides(k), blk_q, blk_k,
+        _ptr(q), _ptr(k), _dt(q.dtype), b, h, h_kv, s_q, s_k, d, _strides(q), _strides(k), blk_q, blk_k,
         _f32_array(topk, h, "topk"), _f32_array(cdfthreshd, h, "cdfthreshd"),
         _f32_array(simthreshd1, h, "simthreshd1"), float(softmax_scale),
         _flags(smooth_k=smooth_k, causal=causal, attention_sink=attention_sink),

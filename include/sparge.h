@@ -69,7 +69,7 @@ typedef enum {
 #define SPARGE_FLAG_CAUSAL 2u     /* block map and block-mode FMHA: causal masks   */
 #define SPARGE_FLAG_ATTN_SINK 4u  /* block map: K block 0 selected in every row    */
 
-/* Library ABI version (this header: 4). */
+/* Library ABI version (this header: 5). */
 int sparge_abi_version(void);
 
 /* Message for the last failed call on this thread ("" if none). */
@@ -79,8 +79,11 @@ const char* sparge_last_error(void);
  * Stage 1: block map.  (CK page, "Status vs Upstream": mean-pool, cosine
  * similarity, pooled QK, top-k / cdfthreshd selection, per-head knobs.)
  *
- * q [b, h, s_q, d], k [b, h, s_k, d] in `dt` (F16 or BF16), strides in
- * elements for (b, h, s).  blk_q = blk_k = 64; s_q and s_k multiples of 64;
+ * q [b, h, s_q, d], k [b, h_kv, s_k, d] in `dt` (F16 or BF16), strides in
+ * elements for (b, h, s); h is a multiple of h_kv.  With h_kv < h (grouped
+ * query attention) query head j pools against K head j / (h / h_kv), the
+ * mapping attention uses (aiter 6841 page), and gates that head's K blocks
+ * with its own simthreshd1[j]; h_kv = h is the plain per-head map.  blk_q = blk_k = 64; s_q and s_k multiples of 64;
  * nq = s_q / 64, nk = s_k / 64 <= SPARGE_MAX_KBLOCKS; h <= SPARGE_MAX_HEADS.
  *
  * For every 64-token block x_1..x_n of Q and of K:
@@ -118,11 +121,12 @@ const char* sparge_last_error(void);
  *   lut_count  int32 [b, h, nq]: number of selected blocks.
  *   block_map  uint8 [b, h, nq, nk] or NULL: 1 = selected.
  *   pooled_prob float [b, h, nq, nk] or NULL: P exactly as the selection saw it.
- *   sim_q, sim_k uint8 [b, h, nq] / [b, h, nk] or NULL: gate flags.
- *   q_mean, k_mean float [b, h, nq, d] / [b, h, nk, d] or NULL.
- *   q_i8, k_i8 int8 [b, h, s_q, d] / [b, h, s_k, d] contiguous, 16-byte
+ *   sim_q, sim_k uint8 [b, h, nq] / [b, h, nk] or NULL: gate flags (sim_k
+ *              as query head j sees its K head's blocks).
+ *   q_mean, k_mean float [b, h, nq, d] / [b, h_kv, nk, d] or NULL.
+ *   q_i8, k_i8 int8 [b, h, s_q, d] / [b, h_kv, s_k, d] contiguous, 16-byte
  *              aligned, with q_i8_scale, k_i8_scale float [b, h, nq] /
- *              [b, h, nk]: all four or none.  (CK page, "Status vs Upstream",
+ *              [b, h_kv, nk]: all four or none.  (CK page, "Status vs Upstream",
  *              not-yet-ported list: Q/K int8 quantisation fused into the pool
  *              kernel, for an int8 QK product in the attention kernel.)  Per
  *              64-token block of the inputs as given (K not smoothed):
@@ -135,7 +139,7 @@ const char* sparge_last_error(void);
  */
 sparge_status sparge_build_block_map(
     const void* q, const void* k, sparge_dtype dt,
-    int b, int h, int s_q, int s_k, int d,
+    int b, int h, int h_kv, int s_q, int s_k, int d,
     const int64_t q_strides[3], const int64_t k_strides[3],
     int blk_q, int blk_k,
     const float* topk, const float* cdfthreshd, const float* simthreshd1,
@@ -146,7 +150,7 @@ sparge_status sparge_build_block_map(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace sparge_build_block_map needs for these sizes
- * (0 if the sizes are invalid). */
+ * (0 if the sizes are invalid); enough for any h_kv dividing h. */
 size_t sparge_build_block_map_workspace(int b, int h, int s_q, int s_k, int d,
                                         int blk_q, int blk_k);
 

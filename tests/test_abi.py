@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert lib.sparge_abi_version() == ops.ABI_VERSION == 4
+    assert lib.sparge_abi_version() == ops.ABI_VERSION == 5
 
 
 def _s3(a, b, c):
@@ -62,22 +62,23 @@ def _err(lib):
 
 def test_workspace_size(lib):
     n = lib.sparge_build_block_map_workspace(2, 32, 16384, 16384, 128, 64, 64)
-    # q_mean + k_mean (fp32) + two flag arrays + K-mean partials (16 chunks of
-    # 1024 rows per head, fp32), each rounded up to 256 bytes
-    assert n == (2 * (2 * 32 * 256 * 128 * 4) + 2 * ((2 * 32 * 256 + 255) // 256 * 256)
+    # q_mean + k_mean (fp32) + Q gate flags (u8) + K block similarities (fp32)
+    # + K-mean partials (16 chunks of 1024 rows per head, fp32), each rounded
+    # up to 256 bytes; sized for as many K heads as Q heads
+    assert n == (2 * (2 * 32 * 256 * 128 * 4) + 2 * 32 * 256 + 2 * 32 * 256 * 4
                  + 2 * 32 * 16 * 128 * 4)
     assert lib.sparge_build_block_map_workspace(1, 1, 100, 64, 64, 64, 64) == 0
     assert lib.sparge_build_block_map_workspace(1, 1, 64, 64, 96, 64, 64) == 0
 
 
 def _bm(lib, **kw):
-    args = dict(q=FAKE, k=FAKE, dt=ops.SPARGE_F16, b=1, h=2, s_q=512, s_k=512, d=64,
+    args = dict(q=FAKE, k=FAKE, dt=ops.SPARGE_F16, b=1, h=2, hkv=2, s_q=512, s_k=512, d=64,
                 qs=_s3(65536, 32768, 64), ks=_s3(65536, 32768, 64), blk_q=64, blk_k=64,
                 topk=_arr([0.5, 0.5]), cdf=None, sim=_arr([0.001, 0.001]), scale=0.0, flags=0,
                 lut=FAKE, cnt=FAKE, q8=None, q8s=None, k8=None, k8s=None, ws=FAKE, ws_bytes=1 << 20)
     args.update(kw)
     return lib.sparge_build_block_map(
-        args["q"], args["k"], args["dt"], args["b"], args["h"], args["s_q"], args["s_k"], args["d"],
+        args["q"], args["k"], args["dt"], args["b"], args["h"], args["hkv"], args["s_q"], args["s_k"], args["d"],
         args["qs"], args["ks"], args["blk_q"], args["blk_k"], args["topk"], args["cdf"], args["sim"],
         args["scale"], args["flags"], args["lut"], args["cnt"], None, None, None, None, None, None,
         args["q8"], args["q8s"], args["k8"], args["k8s"], args["ws"], args["ws_bytes"], None)
@@ -93,6 +94,8 @@ def _bm(lib, **kw):
     (dict(blk_q=128), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(h=0), ops.SPARGE_ERR_INVALID),
     (dict(b=0), ops.SPARGE_ERR_INVALID),                             # empty batch
+    (dict(hkv=0), ops.SPARGE_ERR_INVALID),
+    (dict(h=3, hkv=2, topk=_arr([0.5] * 3), sim=_arr([0.0] * 3)), ops.SPARGE_ERR_INVALID),   # 3 not a multiple of 2
     (dict(s_q=0), ops.SPARGE_ERR_INVALID),                           # empty sequence
     (dict(s_k=0), ops.SPARGE_ERR_INVALID),
     (dict(h=200), ops.SPARGE_ERR_UNSUPPORTED),

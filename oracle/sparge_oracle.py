@@ -45,8 +45,9 @@ def block_mean(x_blk: np.ndarray) -> np.ndarray:
     """Mean token of one block: (1/n) * sum_i x_i.
 
     CK page, "Status vs Upstream": per-block mean-pool.  Reading R1: a plain
-    mean over the block's tokens (every supported length is a multiple of the
-    block size, so there is no partial block).
+    mean over the block's tokens; the last block of a sequence whose length is
+    not a multiple of the block size holds fewer tokens, and its mean divides
+    by that count.
     """
     x = np.asarray(x_blk, dtype=np.float64)
     return x.sum(axis=0) / x.shape[0]
@@ -75,13 +76,12 @@ def pool_and_gate(x: np.ndarray, blk: int, simthreshd1: float):
     """Pool one (b, h) slice x [s, d] into blocks of `blk` tokens.
 
     Returns (means [nb, d], sims [nb], flags [nb] bool) where
-    flag = sim > simthreshd1 (reading R3: strict comparison).
+    flag = sim > simthreshd1 (reading R3: strict comparison).  nb =
+    ceil(s / blk); a partial last block pools its own tokens (reading R1).
     """
     x = np.asarray(x, dtype=np.float64)
     s, _ = x.shape
-    if s % blk != 0:
-        raise ValueError("sequence length must be a multiple of the block size")
-    nb = s // blk
+    nb = -(-s // blk)
     means = np.stack([block_mean(x[i * blk:(i + 1) * blk]) for i in range(nb)])
     sims = np.array([block_self_similarity(x[i * blk:(i + 1) * blk]) for i in range(nb)])
     flags = sims > float(simthreshd1)
@@ -301,7 +301,7 @@ def block_map(q: np.ndarray, k: np.ndarray, topk: Sequence[float],
     ratio = h // h_kv
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    nq, nk = s_q // blk_q, s_k // blk_k
+    nq, nk = -(-s_q // blk_q), -(-s_k // blk_k)       # a partial last block counts
     q_mean = np.zeros((b, h, nq, d))
     k_mean = np.zeros((b, h_kv, nk, d))
     sim_q_val = np.zeros((b, h, nq))
@@ -370,8 +370,10 @@ def block_sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     j // (h_q / h_kv) (aiter 6841 page, GQA mapping).  lut [b, h_lut, nq, L]
     with count [b, h_lut, nq]; h_lut = h_kv when `lut_per_kv_head`, else h_q.
     lut = None means every block (dense).  With `causal` (s_q = s_k, reading
-    R23) query position i attends only to listed keys j <= i.  Returns O
-    [b, h_q, s_q, d], LSE [b, h_q, s_q].
+    R23) query position i attends only to listed keys j <= i.  Lengths need
+    not be multiples of the blocks: the last Q-tile and the last K block are
+    partial, and a listed partial block contributes only its existing keys.
+    Returns O [b, h_q, s_q, d], LSE [b, h_q, s_q].
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -381,7 +383,7 @@ def block_sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     ratio = h_q // h_kv
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    nq, nk = s_q // blk_q, s_k // blk_k
+    nq, nk = -(-s_q // blk_q), -(-s_k // blk_k)
     o = np.zeros((b, h_q, s_q, v.shape[3]))
     lse = np.zeros((b, h_q, s_q))
     for ib in range(b):
@@ -395,10 +397,11 @@ def block_sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                     n = int(count[ib, hl, qb])
                     blocks = np.asarray(lut[ib, hl, qb, :n], dtype=np.int64)
                 idx = (blocks[:, None] * blk_k + np.arange(blk_k)[None, :]).reshape(-1)
-                rows = slice(qb * blk_q, (qb + 1) * blk_q)
+                idx = idx[idx < s_k]
+                rows = slice(qb * blk_q, min((qb + 1) * blk_q, s_q))
                 allowed = None
                 if causal:
-                    qpos = np.arange(qb * blk_q, (qb + 1) * blk_q)
+                    qpos = np.arange(rows.start, rows.stop)
                     allowed = idx[None, :] <= qpos[:, None]
                 o[ib, ih, rows], lse[ib, ih, rows] = attend(
                     q[ib, ih, rows], k[ib, hk, idx], v[ib, hk, idx], scale, allowed)
@@ -472,7 +475,10 @@ def block_sparse_attention_pv_skip(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     with m_i the maximum over all of row i's keys.  The LSE therefore equals the
     exact one, and |O_i - O_exact,i| <= (skipped keys of row i) * exp(-tau) *
     max |v|, since every skipped score lies more than tau below m_i.  The blocks
-    of 64 queries and 64 keys are the ones of block_sparse_attention.
+    of 64 queries and 64 keys are the ones of block_sparse_attention.  A
+    partial last K block is completed with masked keys (score -inf) and a
+    partial last Q-tile with copies of its last row: a copy repeats a decision
+    the row group already takes, so the units are decided by the tile's rows.
     With `return_skips`, also returns the number of skipped units and of all
     units; with `return_margins`, then [b, h_q, nq, 64 // q_unit] the smallest
     |margin| (pv_skip_units) of the row group's units: decisions closer than
@@ -487,7 +493,7 @@ def block_sparse_attention_pv_skip(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     blk = 64
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    nq, nk = s_q // blk, s_k // blk
+    nq, nk = -(-s_q // blk), -(-s_k // blk)
     o = np.zeros((b, h_q, s_q, v.shape[3]))
     lse = np.zeros((b, h_q, s_q))
     n_skip = n_units = 0
@@ -501,16 +507,19 @@ def block_sparse_attention_pv_skip(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                     blocks = np.arange(nk)
                 else:
                     blocks = np.asarray(lut[ib, hl, qb, :int(count[ib, hl, qb])], dtype=np.int64)
-                rows = slice(qb * blk, (qb + 1) * blk)
+                rows = slice(qb * blk, min((qb + 1) * blk, s_q))
+                nr = rows.stop - rows.start
                 n = len(blocks)
                 if n == 0:
                     o[ib, ih, rows], lse[ib, ih, rows] = 0.0, NEG_INF
                     continue
                 idx = (blocks[:, None] * blk + np.arange(blk)[None, :]).reshape(-1)
-                s = scale * (q[ib, ih, rows] @ k[ib, hk, idx].T)          # [64, n * 64]
-                if causal:
-                    qpos = np.arange(qb * blk, (qb + 1) * blk)
-                    s = np.where(idx[None, :] <= qpos[:, None], s, NEG_INF)
+                exists = idx < s_k                                         # keys of a partial block
+                idx = np.where(exists, idx, 0)
+                qpos = np.minimum(np.arange(qb * blk, (qb + 1) * blk), s_q - 1)   # copies of the last row
+                s = scale * (q[ib, ih, qpos] @ k[ib, hk, idx].T)          # [64, n * 64]
+                allowed = exists[None, :] & (idx[None, :] <= qpos[:, None] if causal else True)
+                s = np.where(allowed, s, NEG_INF)
                 skip, margin = pv_skip_units(s.reshape(blk, n, blk), pv_threshold, q_unit,
                                              k_unit, num_splits, return_margin=True)
                 near[ib, ih, qb] = np.abs(margin).min(axis=(1, 2))
@@ -525,8 +534,8 @@ def block_sparse_attention_pv_skip(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                 l = e.sum(axis=1, keepdims=True)
                 l_safe = np.where(empty[:, None], 1.0, l)
                 num = (e * kept.reshape(blk, n * blk)) @ v[ib, hk, idx]
-                o[ib, ih, rows] = np.where(empty[:, None], 0.0, num / l_safe)
-                lse[ib, ih, rows] = np.where(empty, NEG_INF, (m + np.log(l_safe))[:, 0])
+                o[ib, ih, rows] = np.where(empty[:, None], 0.0, num / l_safe)[:nr]
+                lse[ib, ih, rows] = np.where(empty, NEG_INF, (m + np.log(l_safe))[:, 0])[:nr]
     out = (o, lse)
     if return_skips:
         out += (n_skip, n_units)
@@ -558,14 +567,16 @@ def quantize_block_int8(x_blk: np.ndarray):
 
 
 def quantize_int8(x: np.ndarray, blk: int = 64):
-    """quantize_block_int8 over every block of `blk` tokens of x [b, h, s, d].
-    Returns codes [b, h, s, d] int8 and scales [b, h, s // blk] fp32."""
+    """quantize_block_int8 over every block of `blk` tokens of x [b, h, s, d]
+    (a partial last block quantises its own tokens, reading R1).
+    Returns codes [b, h, s, d] int8 and scales [b, h, ceil(s / blk)] fp32."""
     b, h, s, d = x.shape
+    nb = -(-s // blk)
     codes = np.zeros((b, h, s, d), np.int8)
-    scales = np.zeros((b, h, s // blk), np.float32)
+    scales = np.zeros((b, h, nb), np.float32)
     for ib in range(b):
         for ih in range(h):
-            for j in range(s // blk):
+            for j in range(nb):
                 rows = slice(j * blk, (j + 1) * blk)
                 codes[ib, ih, rows], scales[ib, ih, j] = quantize_block_int8(x[ib, ih, rows])
     return codes, scales
@@ -573,7 +584,8 @@ def quantize_int8(x: np.ndarray, blk: int = 64):
 
 def dequantize_int8(codes: np.ndarray, scales: np.ndarray, blk: int = 64) -> np.ndarray:
     """codes * scale of their block, in fp64 (exact: an int8 times an fp32)."""
-    return codes.astype(np.float64) * np.repeat(scales.astype(np.float64), blk, axis=2)[..., None]
+    per_row = np.repeat(scales.astype(np.float64), blk, axis=2)[:, :, :codes.shape[2]]
+    return codes.astype(np.float64) * per_row[..., None]
 
 
 def block_sparse_attention_qk_int8(q: np.ndarray, k: np.ndarray, v: np.ndarray,

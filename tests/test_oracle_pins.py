@@ -72,9 +72,14 @@ def test_random_tokens_similarity_near_one_over_n():
     assert 0.008 < min(vals) and max(vals) < 0.03
 
 
-def test_pool_partial_block_rejected():
-    with pytest.raises(ValueError):
-        oracle.pool_and_gate(np.ones((65, 4)), 64, 0.001)
+def test_pool_partial_block_pools_its_own_tokens():
+    # 65 tokens: a full block of ones and a one-token block of twos (reading R1).
+    x = np.ones((65, 4))
+    x[64] = [2.0, -2.0, 0.0, 0.0]
+    means, sims, flags = oracle.pool_and_gate(x, 64, 0.999)
+    assert means.shape == (2, 4)
+    assert np.array_equal(means[1], [2.0, -2.0, 0.0, 0.0])
+    assert abs(sims[1] - 1.0) < 1e-15 and flags[1]
 
 
 # --------------------------------------------------------------------------

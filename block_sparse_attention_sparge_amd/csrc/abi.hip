@@ -66,7 +66,7 @@ struct BlockMapLayout {
 };
 
 BlockMapLayout block_map_layout(int b, int h, int s_q, int s_k, int d) {
-  const size_t nq = (size_t)s_q / 64, nk = (size_t)s_k / 64, bh = (size_t)b * h;
+  const size_t nq = ((size_t)s_q + 63) / 64, nk = ((size_t)s_k + 63) / 64, bh = (size_t)b * h;
   BlockMapLayout l;
   l.km_chunks = (s_k + sparge::kKmChunkRows - 1) / sparge::kKmChunkRows;
   size_t off = 0;
@@ -89,7 +89,7 @@ const char* sparge_last_error(void) { return g_error.c_str(); }
 
 size_t sparge_build_block_map_workspace(int b, int h, int s_q, int s_k, int d, int blk_q, int blk_k) {
   if (b <= 0 || h <= 0 || s_q <= 0 || s_k <= 0 || (d != 64 && d != 128)) return 0;
-  if (blk_q != 64 || blk_k != 64 || s_q % 64 || s_k % 64) return 0;
+  if (blk_q != 64 || blk_k != 64) return 0;
   return block_map_layout(b, h, s_q, s_k, d).total;
 }
 
@@ -111,10 +111,8 @@ sparge_status sparge_build_block_map(
   if (d != 64 && d != 128) return fail(SPARGE_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", d);
   if (blk_q != 64 || blk_k != 64)
     return fail(SPARGE_ERR_UNSUPPORTED, "block map needs blk_q = blk_k = 64 (got %d, %d)", blk_q, blk_k);
-  if (s_q % 64 || s_k % 64)
-    return fail(SPARGE_ERR_UNSUPPORTED, "ragged sequence (s_q=%d, s_k=%d) is not a multiple of 64", s_q, s_k);
   if (h > SPARGE_MAX_HEADS) return fail(SPARGE_ERR_UNSUPPORTED, "h=%d exceeds %d", h, SPARGE_MAX_HEADS);
-  const int nq = s_q / 64, nk = s_k / 64;
+  const int nq = (s_q + 63) / 64, nk = (s_k + 63) / 64;   // a partial last block counts
   if (nk > SPARGE_MAX_KBLOCKS)
     return fail(SPARGE_ERR_UNSUPPORTED, "nk=%d K blocks exceeds %d", nk, SPARGE_MAX_KBLOCKS);
   sparge_status st;
@@ -169,7 +167,7 @@ sparge_status sparge_build_block_map(
   pa.q = q;
   pa.k = k;
   for (int i = 0; i < 3; ++i) { pa.qs[i] = q_strides[i]; pa.ks[i] = k_strides[i]; }
-  pa.b = b; pa.h = h; pa.h_kv = h_kv; pa.nq = nq; pa.nk = nk;
+  pa.b = b; pa.h = h; pa.h_kv = h_kv; pa.nq = nq; pa.nk = nk; pa.sq = s_q; pa.sk = s_k;
   pa.q_mean = q_mean ? q_mean : reinterpret_cast<float*>(ws + lay.q_mean);
   pa.k_mean = k_mean ? k_mean : reinterpret_cast<float*>(ws + lay.k_mean);
   pa.sim_q = sim_q ? sim_q : reinterpret_cast<uint8_t*>(ws + lay.sim_q);
@@ -267,10 +265,8 @@ sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void*
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   if (block_mode) {
-    if (s_q % 64 || s_k % 64)
-      return fail(SPARGE_ERR_UNSUPPORTED, "ragged sequence (s_q=%d, s_k=%d) is not a multiple of 64", s_q, s_k);
-    a.nqt = s_q / 64;
-    a.nkb = s_k / 64;
+    a.nqt = (s_q + 63) / 64;   // a partial last tile / block counts
+    a.nkb = (s_k + 63) / 64;
     // The kernel addresses a 64-row K or V block with 32-bit byte offsets.
     const int64_t elem = 2, span = 64 * std::max(k_strides[2], v_strides[2]) * elem;
     if (span >= (int64_t(1) << 31))
@@ -311,8 +307,6 @@ sparge_status sparse_fmha_fwd_qk_int8(const int8_t* q, const float* q_scale, con
     return fail(SPARGE_ERR_INVALID, "sizes must be positive");
   if (h_q % h_kv != 0) return fail(SPARGE_ERR_INVALID, "h_q=%d is not a multiple of h_kv=%d", h_q, h_kv);
   if (d != 64 && d != 128) return fail(SPARGE_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", d);
-  if (s_q % 64 || s_k % 64)
-    return fail(SPARGE_ERR_UNSUPPORTED, "ragged sequence (s_q=%d, s_k=%d) is not a multiple of 64", s_q, s_k);
   sparge_status st;
   if ((st = check_strides("q", q_strides)) != SPARGE_OK) return st;
   if ((st = check_strides("k", k_strides)) != SPARGE_OK) return st;
@@ -360,8 +354,8 @@ sparge_status sparse_fmha_fwd_qk_int8(const int8_t* q, const float* q_scale, con
   a.pv_tau2 = 0.f;
   a.q_scale = q_scale; a.k_scale = k_scale;
   a.tok_groups = 1;
-  a.nqt = s_q / 64;
-  a.nkb = s_k / 64;
+  a.nqt = (s_q + 63) / 64;
+  a.nkb = (s_k + 63) / 64;
   return hip_status(launch_fmha_qk8(a, v_dt, o_dt, d, reinterpret_cast<hipStream_t>(stream)),
                     "sparse_fmha_qk_int8 launch");
 }

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void key_mean_kernel(PoolArgs a) {
   const int chunk = (int)(blockIdx.x % a.km_chunks);
   const int hh = (int)(bh % a.h_kv), bb = (int)(bh / a.h_kv);
   const int r0 = chunk * kKmChunkRows;
-  const int rows = min(kKmChunkRows, a.nk * 64 - r0);
+  const int rows = min(kKmChunkRows, a.sk - r0);
   const int c = tid % CH, rsub = tid / CH;
   const typename E::T* base = reinterpret_cast<const typename E::T*>(a.k) + bb * a.ks[0] + hh * a.ks[1] + c * 8;
   float acc[8];
@@ -73,6 +73,9 @@ __global__ __launch_bounds__(256) void key_mean_kernel(PoolArgs a) {
 // ---------------------------------------------------------------------------
 // pool_sim
 // ---------------------------------------------------------------------------
+// A sequence whose length is not a multiple of 64 ends in a partial block: it
+// loads only its own tokens, and its mean and mean pairwise cosine divide by
+// its token count (for a full block, by the exact powers of two 64 and 4096).
 template <class E, int D, bool SMOOTH, bool QUANT>
 __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
   constexpr int CH = D / 8;          // 16-byte chunks per token
@@ -94,6 +97,8 @@ __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
   const int bb = (int)(bh / nh);
   const int64_t* st = is_k ? a.ks : a.qs;
   const typename E::T* base = reinterpret_cast<const typename E::T*>(is_k ? a.k : a.q);
+  const int ntok = is_k ? a.sk : a.sq;
+  const int cnt = min(64, ntok - blk * 64);   // tokens in this block
 
   const int c = lane % CH;
   const int t0 = lane / CH;
@@ -101,7 +106,10 @@ __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
 
   u32x4 raw[NP];
 #pragma unroll
-  for (int p = 0; p < NP; ++p) raw[p] = load16(p0 + (int64_t)(p * TPP) * st[2]);
+  for (int p = 0; p < NP; ++p) {
+    raw[p] = u32x4{0u, 0u, 0u, 0u};
+    if (p * TPP + t0 < cnt) raw[p] = load16(p0 + (int64_t)(p * TPP) * st[2]);
+  }
 
   // K smoothing: this lane's 8 entries of km (zero when not smoothing).
   float kmv[8];
@@ -127,6 +135,10 @@ __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
     for (int w = 0; w < 4; ++w) {
       x[2 * w] = E::lo(raw[p][w]) - kmv[2 * w];
       x[2 * w + 1] = E::hi(raw[p][w]) - kmv[2 * w + 1];
+    }
+    if (SMOOTH && p * TPP + t0 >= cnt) {   // a missing token of a partial block
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = 0.f;
     }
     float n2 = 0.f;
 #pragma unroll
@@ -157,7 +169,7 @@ __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
 
   float* mean = (is_k ? a.k_mean : a.q_mean) + (bh * nb + blk) * D;
   if (t0 == 0) {
-    const float r = 1.0f / 64.0f;
+    const float r = 1.0f / (float)cnt;
     floatx4 m0 = {sx[0] * r, sx[1] * r, sx[2] * r, sx[3] * r};
     floatx4 m1 = {sx[4] * r, sx[5] * r, sx[6] * r, sx[7] * r};
     *reinterpret_cast<floatx4*>(mean + c * 8) = m0;
@@ -166,7 +178,7 @@ __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
   if (lane == 0) {
     // Q blocks are gated here; a K block's similarity is kept for the query
     // heads that read it, each with its own threshold.
-    const float sim = dot * (1.0f / 4096.0f);
+    const float sim = dot * (1.0f / (float)(cnt * cnt));
     if (is_k) a.k_sim[bh * nb + blk] = sim;
     else a.sim_q[bh * nb + blk] = sim > a.thr[hh] ? 1 : 0;
   }
@@ -191,7 +203,7 @@ __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
     for (int m = 32; m >= 1; m >>= 1) amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, m, kWave));
     const float amax = E::lo(amax_bits);
     const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-    int8_t* codes = (is_k ? a.k_i8 : a.q_i8) + ((bh * nb + blk) * 64 + t0) * (int64_t)D + c * 8;
+    int8_t* codes = (is_k ? a.k_i8 : a.q_i8) + (bh * ntok + blk * 64 + t0) * (int64_t)D + c * 8;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       uint32_t wd[2];
@@ -207,7 +219,7 @@ __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
         }
         wd[half] = acc;
       }
-      *reinterpret_cast<u32x2*>(codes + (int64_t)(p * TPP) * D) = u32x2{wd[0], wd[1]};
+      if (p * TPP + t0 < cnt) *reinterpret_cast<u32x2*>(codes + (int64_t)(p * TPP) * D) = u32x2{wd[0], wd[1]};
     }
     if (lane == 0) (is_k ? a.k_i8_scale : a.q_i8_scale)[bh * nb + blk] = amax / 127.0f;
   }

@@ -66,7 +66,13 @@ namespace sparge {
 // The running maximum is only moved when a row's new maximum exceeds it by
 // more than 2^8 (base-2 units), so most blocks skip rescaling O; the exported
 // LSE and O are exact for any reference maximum, and P stays below 2^8.
-template <class E, int D, bool OUT_F32, bool CAUSAL, bool PVSKIP>
+//
+// Lengths need not be multiples of 64.  A partial last Q-tile loads its
+// missing rows as copies of its last row and stores only its own rows.  The
+// MASKED kernel removes keys by position: past the query (causal) and past
+// the end of a ragged K sequence, whose last block is loaded with its missing
+// rows repeating its last row (finite values whose scores are then -inf).
+template <class E, int D, bool OUT_F32, bool MASKED, bool PVSKIP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fmha_block_kernel(FmhaArgs a) {
   typedef typename E::T T;
@@ -106,7 +112,7 @@ void fmha_block_kernel(FmhaArgs a) {
     list = a.lut + row * a.lut_row_len;
     n = a.cnt ? a.cnt[row] : first_negative(list, a.lut_row_len, lane);
   } else {
-    n = CAUSAL ? min(a.nkb, qt + 1) : a.nkb;   // dense causal: blocks 0..qt
+    n = MASKED && a.causal ? min(a.nkb, qt + 1) : a.nkb;   // dense causal: blocks 0..qt
   }
   // The row length is the same for every lane; saying so keeps the loop
   // uniform and lets the LUT entries come through scalar loads.
@@ -116,12 +122,13 @@ void fmha_block_kernel(FmhaArgs a) {
   const int nloc = max(0, min(n, beg + chunk) - beg);
 
   const int q0 = qt * 64 + qh * 32;
+  const bool row_ok = q0 + l32 < a.sq;       // false past the end of a ragged last tile
   const int64_t orow = (int64_t)split * a.o_split_stride + bb * a.os[0] + hh * a.os[1] +
                        (int64_t)(q0 + l32) * a.os[2];
   float* lse_row = a.lse ? a.lse + (((int64_t)split * a.b + bb) * a.hq + hh) * a.sq : nullptr;
 
   if (nloc == 0) {
-    if (kh == 0) {
+    if (kh == 0 && row_ok) {
       for (int d0 = hl * (D / 2); d0 < (hl + 1) * (D / 2); d0 += 4)
         store4<E, OUT_F32>(a.o, orow + d0, 0.f, 0.f, 0.f, 0.f);
       if (lse_row && hl == 0) lse_row[q0 + l32] = -INFINITY;
@@ -131,7 +138,7 @@ void fmha_block_kernel(FmhaArgs a) {
 
   // Q^T fragments (B operand): lane (query l32, half hl) holds d = 16kk + 8hl .. +7.
   const T* qp = reinterpret_cast<const T*>(a.q) + bb * a.qs[0] + hh * a.qs[1] +
-                (int64_t)(q0 + l32) * a.qs[2] + 8 * hl;
+                (int64_t)min(q0 + l32, a.sq - 1) * a.qs[2] + 8 * hl;
   u32x4 qf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) qf[kk] = load16(qp + 16 * kk);
@@ -163,6 +170,20 @@ void fmha_block_kernel(FmhaArgs a) {
   auto issue_block = [&](int kb, int buf) {
     const char* kp = kbase + kb * kblk;
     const char* vp = vbase + kb * vblk;
+    if (MASKED && 64 * kb + 64 > a.sk) {
+      // The last block of a ragged K sequence: LDS row r takes global row
+      // min(r, last), swizzled for its own position r.
+      const int last = a.sk - 1 - 64 * kb;
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j) {
+        const int gi = 64 * (wave * NDMA + j) + lane;
+        const int r = gi / G16, sl = gi % G16, rc = min(r, last);
+        const uint32_t off = (uint32_t)((buf * TILE + (wave * NDMA + j) * 64 * 8) * sizeof(T));
+        dma16(kp, (uint32_t)((rc * a.ks[2] + (sl ^ (r % G16)) * 8) * (int64_t)sizeof(T)), sk_lds + off);
+        dma16(vp, (uint32_t)((rc * a.vs[2] + (sl ^ ((VSW * r) % G16)) * 8) * (int64_t)sizeof(T)), sv_lds + off);
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
       const uint32_t off = (uint32_t)((buf * TILE + (wave * NDMA + j) * 64 * 8) * sizeof(T));
@@ -195,7 +216,7 @@ void fmha_block_kernel(FmhaArgs a) {
   wait_dma();
   __syncthreads();
   int kb_ahead = nloc > 1 ? kb_of(1) : 0;
-  int kb_cur = CAUSAL ? kb_of(0) : 0;
+  int kb_cur = MASKED ? kb_of(0) : 0;
 
   // One 64-key block out of LDS buffer `cur` (a compile-time constant, so
   // every LDS address is a fixed register plus an immediate offset).
@@ -244,16 +265,18 @@ void fmha_block_kernel(FmhaArgs a) {
     // The other buffer held block it-1, released by the last barrier.
     if (it + 1 < nloc) issue_block(kb_ahead, 1 - cur);
 
-    if constexpr (CAUSAL) {
+    if constexpr (MASKED) {
       // Key 64 kb + 32 kh + 8 (r/4) + 4 hl + r%4 of register r against query
-      // 64 qt + 32 qh + l32: keys past the query are removed.  Only the
-      // diagonal block and blocks past it (listed by hand) can hold any.
-      if (kb_cur >= qt) {
+      // 64 qt + 32 qh + l32: keys past the query (causal) and keys past the
+      // end of the sequence are removed.  Only the diagonal block, blocks
+      // past it (listed by hand) and a partial last block can hold any.
+      if (64 * kb_cur + 64 > a.sk || (a.causal && kb_cur >= qt)) {
         const int qpos = 64 * qt + 32 * qh + l32;
+        const int lim = a.causal ? min(qpos + 1, a.sk) : a.sk;   // first removed key
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = 64 * kb_cur + 32 * kh + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key > qpos) s[r] = -INFINITY;
+          if (key >= lim) s[r] = -INFINITY;
         }
       }
     }
@@ -278,8 +301,8 @@ void fmha_block_kernel(FmhaArgs a) {
     // input type for PV.  The row sum adds the fp32 values: rounding to the
     // input type moves a term by up to 2^-8 of itself (bf16), which on a row
     // carried by one key would move the LSE by up to 4e-3 nats.
-    // Causal rows may still have no key (m_run = -inf): their P is 0.
-    const float mref = CAUSAL && m_run == -INFINITY ? 0.f : m_run;
+    // Masked rows may still have no key (m_run = -inf): their P is 0.
+    const float mref = MASKED && m_run == -INFINITY ? 0.f : m_run;
     u32x4 pf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -314,7 +337,7 @@ void fmha_block_kernel(FmhaArgs a) {
     // Block it+1 must have landed before the barrier hands the buffers over.
     wait_dma();
     __syncthreads();
-    if constexpr (CAUSAL) kb_cur = kb_ahead;
+    if constexpr (MASKED) kb_cur = kb_ahead;
     kb_ahead = kb_next;
   };
 
@@ -345,7 +368,8 @@ void fmha_block_kernel(FmhaArgs a) {
   float m = fmaxf(m_run, m1);
   // Causal: a query row whose listed keys all lie past it has no key at all
   // (both halves at -inf): O = 0, LSE = -inf.
-  const bool empty = CAUSAL && m == -INFINITY;
+  const bool empty = MASKED && m == -INFINITY;
+  if (!row_ok) return;
   if (empty) m = 0.f;
   const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
   const float l_tot = l_w * a0 + l1 * a1;
@@ -373,7 +397,7 @@ void fmha_block_kernel(FmhaArgs a) {
 // ---------------------------------------------------------------------------
 template <class E, int D, bool PVSKIP>
 static void launch_block_v(const FmhaArgs& a, bool out_f32, dim3 grid, hipStream_t st) {
-  if (a.causal) {
+  if (a.causal || a.sk % 64) {
     if (out_f32) hipLaunchKernelGGL((fmha_block_kernel<E, D, true, true, PVSKIP>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((fmha_block_kernel<E, D, false, true, PVSKIP>), grid, dim3(256), 0, st, a);
   } else {

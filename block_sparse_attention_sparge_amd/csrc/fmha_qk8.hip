@@ -19,7 +19,10 @@
 //   * the K scale of every block comes through the scalar cache, requested
 //     one step ahead next to a LUT entry, after the block's last LDS wait.
 // V and P stay in fp16 / bf16 and the PV product is the one of the fp16 / bf16
-// kernel.
+// kernel, and ragged lengths are handled as there: a partial last Q-tile
+// repeats its last row and stores only its own rows; the MASKED kernel
+// (causal, or a ragged K sequence) repeats the last K/V row in a partial last
+// block and removes keys by position.
 #include "attn_common.h"
 #include "common.h"
 #include "kernels.h"
@@ -42,7 +45,7 @@ __device__ __forceinline__ int k8_swz(int r) {
   return (r / (16 / GK)) % GK;
 }
 
-template <class E, int D, bool OUT_F32, bool CAUSAL>
+template <class E, int D, bool OUT_F32, bool MASKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fmha_qk8_kernel(FmhaArgs a) {
   typedef typename E::T T;
@@ -84,7 +87,7 @@ void fmha_qk8_kernel(FmhaArgs a) {
     list = a.lut + row * a.lut_row_len;
     n = a.cnt ? a.cnt[row] : first_negative(list, a.lut_row_len, lane);
   } else {
-    n = CAUSAL ? min(a.nkb, qt + 1) : a.nkb;
+    n = MASKED && a.causal ? min(a.nkb, qt + 1) : a.nkb;
   }
   n = __builtin_amdgcn_readfirstlane(n);
   const int chunk = (n + a.splits - 1) / a.splits;
@@ -92,12 +95,13 @@ void fmha_qk8_kernel(FmhaArgs a) {
   const int nloc = max(0, min(n, beg + chunk) - beg);
 
   const int q0 = qt * 64 + qh * 32;
+  const bool row_ok = q0 + l32 < a.sq;       // false past the end of a ragged last tile
   const int64_t orow = (int64_t)split * a.o_split_stride + bb * a.os[0] + hh * a.os[1] +
                        (int64_t)(q0 + l32) * a.os[2];
   float* lse_row = a.lse ? a.lse + (((int64_t)split * a.b + bb) * a.hq + hh) * a.sq : nullptr;
 
   if (nloc == 0) {
-    if (kh == 0) {
+    if (kh == 0 && row_ok) {
       for (int d0 = hl * (D / 2); d0 < (hl + 1) * (D / 2); d0 += 4)
         store4<E, OUT_F32>(a.o, orow + d0, 0.f, 0.f, 0.f, 0.f);
       if (lse_row && hl == 0) lse_row[q0 + l32] = -INFINITY;
@@ -107,7 +111,7 @@ void fmha_qk8_kernel(FmhaArgs a) {
 
   // Q^T codes (B operand): lane (query l32, half hl) holds d = 32kk + 16hl .. +15.
   const int8_t* qp = reinterpret_cast<const int8_t*>(a.q) + bb * a.qs[0] + hh * a.qs[1] +
-                     (int64_t)(q0 + l32) * a.qs[2] + 16 * hl;
+                     (int64_t)min(q0 + l32, a.sq - 1) * a.qs[2] + 16 * hl;
   u32x4 qf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) qf[kk] = load16(qp + 32 * kk);
@@ -142,6 +146,26 @@ void fmha_qk8_kernel(FmhaArgs a) {
   auto issue_block = [&](int kb, int buf) {
     const char* kp = kbase + kb * kblk;
     const char* vp = vbase + kb * vblk;
+    if (MASKED && 64 * kb + 64 > a.sk) {
+      // The last block of a ragged K sequence: LDS row r takes global row
+      // min(r, last), swizzled for its own position r.
+      const int last = a.sk - 1 - 64 * kb;
+#pragma unroll
+      for (int j = 0; j < NDMA_K; ++j) {
+        const int gi = 64 * (wave * NDMA_K + j) + lane;
+        const int r = gi / GK, sl = gi % GK, rc = min(r, last);
+        dma16(kp, (uint32_t)(rc * a.ks[2] + (sl ^ k8_swz<GK>(r)) * 16),
+              sk_lds + (uint32_t)(buf * TILE + (wave * NDMA_K + j) * 64 * 16));
+      }
+#pragma unroll
+      for (int j = 0; j < NDMA_V; ++j) {
+        const int gi = 64 * (wave * NDMA_V + j) + lane;
+        const int r = gi / G16, sl = gi % G16, rc = min(r, last);
+        dma16(vp, (uint32_t)((rc * a.vs[2] + (sl ^ ((VSW * r) % G16)) * 8) * (int64_t)sizeof(T)),
+              sv_lds + (uint32_t)((buf * TILE + (wave * NDMA_V + j) * 64 * 8) * sizeof(T)));
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < NDMA_K; ++j)
       dma16(kp, koff[j], sk_lds + (uint32_t)(buf * TILE + (wave * NDMA_K + j) * 64 * 16));
@@ -171,7 +195,7 @@ void fmha_qk8_kernel(FmhaArgs a) {
   __syncthreads();
   int kb_ahead = nloc > 1 ? kb_of(1) : 0;
   float sk_cur = ksc[kb_of(0)];
-  int kb_cur = CAUSAL ? kb_of(0) : 0;
+  int kb_cur = MASKED ? kb_of(0) : 0;
 
   auto step = [&](int it, auto cur_tag) {
     constexpr int cur = decltype(cur_tag)::value;
@@ -218,18 +242,24 @@ void fmha_qk8_kernel(FmhaArgs a) {
     float s[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = (float)si[r];
-    if constexpr (CAUSAL) {
-      if (kb_cur >= qt) {
+    if constexpr (MASKED) {
+      if (64 * kb_cur + 64 > a.sk || (a.causal && kb_cur >= qt)) {
         const int qpos = 64 * qt + 32 * qh + l32;
+        const int lim = a.causal ? min(qpos + 1, a.sk) : a.sk;   // first removed key
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = 64 * kb_cur + 32 * kh + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key > qpos) s[r] = -INFINITY;
+          if (key >= lim) s[r] = -INFINITY;
         }
       }
     }
 
-    const float c2 = c2q * sk_cur;   // this block's factor from code product to base-2 score
+    // This block's factor from code product to base-2 score.  It is 0 when a
+    // scale is 0 (an all-zero block, whose codes and products are all 0); the
+    // masked kernel lifts it to the least normal float so that a removed key
+    // (-inf) still scores -inf and not -inf * 0.  The unmasked scores it then
+    // gives, at most 2^21 * 2^-126, vanish next to any score that matters.
+    const float c2 = MASKED ? fmaxf(c2q * sk_cur, 1.17549435e-38f) : c2q * sk_cur;
     float rmax = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) rmax = fmaxf(rmax, s[r]);
@@ -244,7 +274,7 @@ void fmha_qk8_kernel(FmhaArgs a) {
 #pragma unroll
       for (int i = 0; i < NMD; ++i) acc_o[i] *= alpha;
     }
-    const float mref = CAUSAL && m_run == -INFINITY ? 0.f : m_run;
+    const float mref = MASKED && m_run == -INFINITY ? 0.f : m_run;
     u32x4 pf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -271,7 +301,7 @@ void fmha_qk8_kernel(FmhaArgs a) {
     // Block it+1 must have landed before the barrier hands the buffers over.
     wait_dma();
     __syncthreads();
-    if constexpr (CAUSAL) kb_cur = kb_ahead;
+    if constexpr (MASKED) kb_cur = kb_ahead;
     sk_cur = sk_next;
     kb_ahead = kb_next;
   };
@@ -302,7 +332,8 @@ void fmha_qk8_kernel(FmhaArgs a) {
   if (kh == 1) return;
   const float m1 = ml[l32], l1 = ml[32 + l32];
   float m = fmaxf(m_run, m1);
-  const bool empty = CAUSAL && m == -INFINITY;
+  const bool empty = MASKED && m == -INFINITY;
+  if (!row_ok) return;
   if (empty) m = 0.f;
   const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
   const float l_tot = l_w * a0 + l1 * a1;
@@ -329,7 +360,7 @@ template <class E, int D>
 static hipError_t launch_qk8_t(const FmhaArgs& a, bool out_f32, hipStream_t st) {
   const int64_t G = (int64_t)a.nqt * a.hq * a.b * a.splits;
   const dim3 grid((unsigned)(((G + 7) / 8) * 8));
-  if (a.causal) {
+  if (a.causal || a.sk % 64) {
     if (out_f32) hipLaunchKernelGGL((fmha_qk8_kernel<E, D, true, true>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((fmha_qk8_kernel<E, D, false, true>), grid, dim3(256), 0, st, a);
   } else {

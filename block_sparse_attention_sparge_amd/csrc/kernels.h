@@ -18,6 +18,7 @@ struct PoolArgs {
   int64_t ks[3];
   int b, h, nq, nk;
   int h_kv;          // K heads (h is a multiple)
+  int sq, sk;        // tokens; the last block of each may be partial
   float* q_mean;     // [b, h, nq, d]
   float* k_mean;     // [b, h_kv, nk, d]
   uint8_t* sim_q;    // [b, h, nq] Q gate flags

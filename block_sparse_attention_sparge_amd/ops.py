@@ -157,6 +157,15 @@ def _flags(smooth_k: bool = False, causal: bool = False, attention_sink: bool = 
             (SPARGE_FLAG_ATTN_SINK if attention_sink else 0))
 
 
+def _check_lut_rows(lut, count, b, nq):
+    """A block LUT holds one row per (b, LUT head, Q-tile); the kernels read
+    nq of them per head, so a shorter LUT is refused here."""
+    if lut.dim() != 4 or lut.shape[0] != b or lut.shape[2] != nq:
+        raise SpargeError(SPARGE_ERR_INVALID, f"lut must be [b={b}, heads, nq={nq}, L] (got {tuple(lut.shape)})")
+    if count is not None and tuple(count.shape) != tuple(lut.shape[:3]):
+        raise SpargeError(SPARGE_ERR_INVALID, f"count must be {tuple(lut.shape[:3])} (got {tuple(count.shape)})")
+
+
 def block_map_workspace_bytes(b: int, h: int, s_q: int, s_k: int, d: int, blk_q: int = 64,
                               blk_k: int = 64) -> int:
     return int(load_library().sparge_build_block_map_workspace(b, h, s_q, s_k, d, blk_q, blk_k))
@@ -170,7 +179,8 @@ def build_block_map(q: torch.Tensor, k: torch.Tensor, topk, simthreshd1, cdfthre
     """Stage 1 (sparge_build_block_map).  q [b, h, s_q, d], k [b, h_kv, s_k, d]
     with h a multiple of h_kv (query head j reads K head j // (h / h_kv)).
 
-    Returns a dict with 'lut' int32 [b, h, nq, nk], 'count' int32 [b, h, nq],
+    nq = ceil(s_q / 64), nk = ceil(s_k / 64): a partial last block pools its
+    own tokens.  Returns a dict with 'lut' int32 [b, h, nq, nk], 'count' int32 [b, h, nq],
     and with return_debug also 'bitmap', 'prob', 'sim_q', 'sim_k', 'q_mean',
     'k_mean'.  `out` may hold preallocated tensors under the same keys (plus
     'workspace').  smooth_k / causal / attention_sink set SPARGE_FLAG_SMOOTH_K /
@@ -188,7 +198,7 @@ def build_block_map(q: torch.Tensor, k: torch.Tensor, topk, simthreshd1, cdfthre
         raise SpargeError(SPARGE_ERR_INVALID, "q and k shapes disagree")
     if q.dtype != k.dtype:
         raise SpargeError(SPARGE_ERR_INVALID, "q and k dtypes disagree")
-    nq, nk = s_q // blk_q if blk_q else 0, s_k // blk_k if blk_k else 0
+    nq, nk = -(-s_q // blk_q) if blk_q else 0, -(-s_k // blk_k) if blk_k else 0   # partial last blocks count
     out = dict(out or {})
 
     def get(key, shape, dtype):
@@ -248,8 +258,8 @@ def sparse_fmha_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                     return_lse: bool = True, causal: bool = False, pv_threshold: float = 0.0):
     """Stage 2 (sparse_fmha_fwd).  q [b, h_q, s_q, d]; k, v [b, h_kv, s_k, d].
 
-    Block mode (64, 64): lut [b, h_lut, s_q/64, L] (+ count [b, h_lut, s_q/64]);
-    lut None = dense.  Token mode (1, 1): lut [b, h_kv, L] token positions.
+    Block mode (64, 64): lut [b, h_lut, nq, L] (+ count [b, h_lut, nq]),
+    nq = ceil(s_q / 64); lut None = dense.  Lengths need not be multiples of 64.  Token mode (1, 1): lut [b, h_kv, L] token positions.
     With num_splits > 1 the outputs are partials o [S, b, h_q, s_q, d] and
     lse [S, b, h_q, s_q] (fp32 unless out_dtype says otherwise).  causal sets
     SPARGE_FLAG_CAUSAL (block mode, s_q = s_k).  pv_threshold > 0 lets the
@@ -284,6 +294,8 @@ def sparse_fmha_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         lut_heads = lut.shape[1]
     if count is not None and (count.dtype != torch.int32 or not count.is_contiguous()):
         raise SpargeError(SPARGE_ERR_INVALID, "count must be contiguous int32")
+    if blk_q == 64 and lut is not None:
+        _check_lut_rows(lut, count, b, -(-s_q // 64))
     st = lib.sparse_fmha_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dt(q.dtype), _dt(o.dtype),
         b, h_q, h_kv, s_q, s_k, d, _strides(q), _strides(k), _strides(v), _strides(o4),
@@ -303,8 +315,8 @@ def sparse_fmha_fwd_qk_int8(q_i8: torch.Tensor, q_scale: torch.Tensor, k_i8: tor
                             causal: bool = False):
     """Stage 2 on int8 Q/K codes (sparse_fmha_fwd_qk_int8), block mode.
 
-    q_i8 [b, h_q, s_q, d] int8 with q_scale [b, h_q, s_q/64]; k_i8 [b, h_kv,
-    s_k, d] int8 with k_scale [b, h_kv, s_k/64] (as build_block_map(...,
+    q_i8 [b, h_q, s_q, d] int8 with q_scale [b, h_q, ceil(s_q/64)]; k_i8 [b, h_kv,
+    s_k, d] int8 with k_scale [b, h_kv, ceil(s_k/64)] (as build_block_map(...,
     quantize_int8=True) returns them); v [b, h_kv, s_k, d] fp16/bf16.  The LUT,
     splits and outputs are as in sparse_fmha_fwd.  Returns (o, lse).
     """
@@ -314,7 +326,7 @@ def sparse_fmha_fwd_qk_int8(q_i8: torch.Tensor, q_scale: torch.Tensor, k_i8: tor
     h_kv, s_k = k_i8.shape[1], k_i8.shape[2]
     if q_i8.dtype != torch.int8 or k_i8.dtype != torch.int8:
         raise SpargeError(SPARGE_ERR_INVALID, "q_i8 and k_i8 must be int8")
-    for name, t, shape in (("q_scale", q_scale, (b, h_q, s_q // 64)), ("k_scale", k_scale, (b, h_kv, s_k // 64))):
+    for name, t, shape in (("q_scale", q_scale, (b, h_q, -(-s_q // 64))), ("k_scale", k_scale, (b, h_kv, -(-s_k // 64)))):
         if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shape:
             raise SpargeError(SPARGE_ERR_INVALID, f"{name} must be contiguous float32 {shape}")
     if out_dtype is None:
@@ -334,6 +346,7 @@ def sparse_fmha_fwd_qk_int8(q_i8: torch.Tensor, q_scale: torch.Tensor, k_i8: tor
         if lut.dtype != torch.int32 or not lut.is_contiguous():
             raise SpargeError(SPARGE_ERR_INVALID, "lut must be contiguous int32")
         lut_row_len, lut_heads = lut.shape[-1], lut.shape[1]
+        _check_lut_rows(lut, count, b, -(-s_q // 64))
     if count is not None and (count.dtype != torch.int32 or not count.is_contiguous()):
         raise SpargeError(SPARGE_ERR_INVALID, "count must be contiguous int32")
     st = lib.sparse_fmha_fwd_qk_int8(

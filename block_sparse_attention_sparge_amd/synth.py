@@ -48,13 +48,13 @@ def normal(shape, seed: int, tensor_id: int, dtype=torch.float16, device="cpu",
 def centroid_noise(b: int, h: int, s: int, d: int, blk: int, gammas, sigma: float,
                    seed: int, tensor_id: int, dtype=torch.float16,
                    device="cpu") -> torch.Tensor:
-    """Block-centroid + noise tokens [b, h, s, d]; gammas has one entry per head."""
-    assert s % blk == 0
+    """Block-centroid + noise tokens [b, h, s, d]; gammas has one entry per head.
+    When s is not a multiple of blk the last block is partial (same centroid)."""
     g = _gen(device, seed, tensor_id)
     gam = torch.as_tensor(list(gammas), dtype=torch.float32, device=device).view(1, h, 1, 1)
-    c = torch.randn(b, h, s // blk, d, generator=g, device=device, dtype=torch.float32) * gam
+    c = torch.randn(b, h, -(-s // blk), d, generator=g, device=device, dtype=torch.float32) * gam
     n = torch.randn(b, h, s, d, generator=g, device=device, dtype=torch.float32)
-    x = c.repeat_interleave(blk, dim=2) + sigma * n
+    x = c.repeat_interleave(blk, dim=2)[:, :, :s] + sigma * n
     return x.to(dtype)
 
 

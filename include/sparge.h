@@ -83,10 +83,13 @@ const char* sparge_last_error(void);
  * elements for (b, h, s); h is a multiple of h_kv.  With h_kv < h (grouped
  * query attention) query head j pools against K head j / (h / h_kv), the
  * mapping attention uses (aiter 6841 page), and gates that head's K blocks
- * with its own simthreshd1[j]; h_kv = h is the plain per-head map.  blk_q = blk_k = 64; s_q and s_k multiples of 64;
- * nq = s_q / 64, nk = s_k / 64 <= SPARGE_MAX_KBLOCKS; h <= SPARGE_MAX_HEADS.
+ * with its own simthreshd1[j]; h_kv = h is the plain per-head map.
+ * blk_q = blk_k = 64; nq = ceil(s_q / 64), nk = ceil(s_k / 64) <=
+ * SPARGE_MAX_KBLOCKS; h <= SPARGE_MAX_HEADS.  Lengths need not be multiples
+ * of 64: the last block then holds n < 64 tokens and pools only those (the
+ * plain reading of a per-block mean pool).
  *
- * For every 64-token block x_1..x_n of Q and of K:
+ * For every block x_1..x_n of Q and of K (n = 64 but for a partial last one):
  *   mean  = (1/n) sum_i x_i                     (fp32)
  *   sim   = |sum_i x_i/|x_i| |^2 / n^2           (mean pairwise cosine, i = j
  *                                                 included; zero rows add 0)
@@ -165,14 +168,15 @@ size_t sparge_build_block_map_workspace(int b, int h, int s_q, int s_k, int d,
  *   s_j = scale * <q_i, k_j>,  LSE_i = ln sum_j exp(s_j),
  *   O_i = sum_j exp(s_j - LSE_i) v_j;   J empty => O_i = 0, LSE_i = -inf.
  *
- * Block mode (blk_q = blk_k = 64): s_q, s_k multiples of 64, and 64 rows of
- * K or V must span less than 2^31 bytes (SPARGE_ERR_UNSUPPORTED otherwise;
- * the LUT is read-only for the duration of the call).  A LUT row
- * belongs to (b, lut head, q tile of 64 rows) and lists K blocks (keys
- * [64 kb, 64 kb + 64)):
- *   lut        int32 [b, lut_heads, s_q / 64, lut_row_len], or NULL = dense
+ * Block mode (blk_q = blk_k = 64): 64 rows of K or V must span less than
+ * 2^31 bytes (SPARGE_ERR_UNSUPPORTED otherwise; the LUT is read-only for the
+ * duration of the call).  A LUT row belongs to (b, lut head, q tile of 64
+ * rows) and lists K blocks kb in [0, nk), nk = ceil(s_k / 64) (keys
+ * [64 kb, min(64 kb + 64, s_k))); nq = ceil(s_q / 64) tiles, the last one
+ * partial when s_q is not a multiple of 64 (it writes only rows < s_q):
+ *   lut        int32 [b, lut_heads, nq, lut_row_len], or NULL = dense
  *              (every block, in order; the dense baseline);
- *   lut_count  int32 [b, lut_heads, s_q / 64], or NULL = entries up to the
+ *   lut_count  int32 [b, lut_heads, nq], or NULL = entries up to the
  *              first -1 (or the whole row).
  * Token-list mode (blk_q = blk_k = 1): a LUT row belongs to (b, lut head) and
  *   lists token positions in [0, s_k); -1 entries are skipped wherever they
@@ -232,9 +236,10 @@ sparge_status sparse_fmha_fwd(
  * num_splits, o_split_stride and flags (0 or SPARGE_FLAG_CAUSAL) are as in
  * sparse_fmha_fwd; v_dt is F16 or BF16 and o_dt is v_dt or F32.
  *   q        int8 [b, h_q, s_q, d], strides (elements) for (b, h, s);
- *   q_scale  float [b, h_q, s_q / 64] contiguous;
+ *   q_scale  float [b, h_q, ceil(s_q / 64)] contiguous;
  *   k        int8 [b, h_kv, s_k, d], strides for (b, h, s);
- *   k_scale  float [b, h_kv, s_k / 64] contiguous.
+ *   k_scale  float [b, h_kv, ceil(s_k / 64)] contiguous.
+ * A partial last block has its own scale (as the block map writes it).
  * d is 64 or 128; q, k, v, o 16-byte aligned; 64 rows of K or V must span
  * less than 2^31 bytes.
  */

@@ -67,7 +67,9 @@ def test_workspace_size(lib):
     # up to 256 bytes; sized for as many K heads as Q heads
     assert n == (2 * (2 * 32 * 256 * 128 * 4) + 2 * 32 * 256 + 2 * 32 * 256 * 4
                  + 2 * 32 * 16 * 128 * 4)
-    assert lib.sparge_build_block_map_workspace(1, 1, 100, 64, 64, 64, 64) == 0
+    # A length that is not a multiple of 64 counts its partial last block.
+    assert (lib.sparge_build_block_map_workspace(1, 1, 100, 65, 64, 64, 64)
+            == lib.sparge_build_block_map_workspace(1, 1, 128, 128, 64, 64, 64) > 0)
     assert lib.sparge_build_block_map_workspace(1, 1, 64, 64, 96, 64, 64) == 0
 
 
@@ -89,8 +91,7 @@ def _bm(lib, **kw):
     (dict(lut=None), ops.SPARGE_ERR_INVALID),
     (dict(dt=ops.SPARGE_F32), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(d=96), ops.SPARGE_ERR_UNSUPPORTED),
-    (dict(s_q=500), ops.SPARGE_ERR_UNSUPPORTED),
-    (dict(s_k=100), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(flags=ops.SPARGE_FLAG_CAUSAL, s_q=500, s_k=520), ops.SPARGE_ERR_UNSUPPORTED),   # ragged, causal, unequal
     (dict(blk_q=128), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(h=0), ops.SPARGE_ERR_INVALID),
     (dict(b=0), ops.SPARGE_ERR_INVALID),                             # empty batch
@@ -100,6 +101,7 @@ def _bm(lib, **kw):
     (dict(s_k=0), ops.SPARGE_ERR_INVALID),
     (dict(h=200), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(s_k=64 * 1025), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(s_k=64 * 1024 + 1), ops.SPARGE_ERR_UNSUPPORTED),           # 1025 blocks, the last partial
     (dict(qs=_s3(65536, 32768, 60)), ops.SPARGE_ERR_INVALID),
     (dict(topk=_arr([1.5, 0.5])), ops.SPARGE_ERR_INVALID),
     (dict(topk=_arr([float("nan"), 0.5])), ops.SPARGE_ERR_INVALID),
@@ -142,8 +144,7 @@ def _fmha(lib, **kw):
     (dict(d=80), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(dt=ops.SPARGE_F32), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(odt=ops.SPARGE_F16), ops.SPARGE_ERR_UNSUPPORTED),
-    (dict(sq=500), ops.SPARGE_ERR_UNSUPPORTED),
-    (dict(sk=520), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(flags=ops.SPARGE_FLAG_CAUSAL, sq=500, sk=520), ops.SPARGE_ERR_UNSUPPORTED),   # ragged, causal, unequal
     (dict(bq=128, bk=128), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(bq=64, bk=1), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(lh=4), ops.SPARGE_ERR_INVALID),
@@ -200,7 +201,7 @@ def _fmha8(lib, **kw):
     (dict(vdt=ops.SPARGE_F32), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(odt=ops.SPARGE_F16), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(d=96), ops.SPARGE_ERR_UNSUPPORTED),
-    (dict(sk=520), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(flags=ops.SPARGE_FLAG_CAUSAL, sq=500, sk=520), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(hkv=3), ops.SPARGE_ERR_INVALID),
     (dict(qs=_s3(8 * 512 * 128, 512 * 136, 136)), ops.SPARGE_ERR_INVALID),       # 136 B rows: not 16-aligned steps
     (dict(k=FAKE + 4), ops.SPARGE_ERR_INVALID),

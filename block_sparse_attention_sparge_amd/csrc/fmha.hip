@@ -317,8 +317,16 @@ void fmha_block_kernel(FmhaArgs a) {
 
     // O^T += V^T P^T over this wave's 32 keys, unless every query row of the
     // wave lies more than the threshold below its running maximum.
+    // The PV MFMAs are issued at raised wave priority: of the two wavefronts
+    // sharing a SIMD (one from each resident workgroup), the one ready to
+    // finish its block goes first and the other's softmax fills the MFMA
+    // shadows (measured: 1.5-2.4% faster at topk 0.4, about 4% at topk 0.1,
+    // bit-identical; raising it for the S MFMAs as well gains nothing).
     bool pv = true;
     if constexpr (PVSKIP) pv = __any(!(m_cand < m_top - a.pv_tau2));
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
     if (pv) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -326,6 +334,8 @@ void fmha_block_kernel(FmhaArgs a) {
         for (int md = 0; md < NMD; ++md) acc_o[md] = mfma32<E>(vf[ks][md], pf[ks], acc_o[md]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
 
     // The LUT entry of block it+2 is requested only now, after this block's
     // last LDS wait: scalar loads share the LDS wait counter but may return

@@ -230,11 +230,20 @@ void fmha_qk8_kernel(FmhaArgs a) {
     read_vt(0);
     __builtin_amdgcn_sched_barrier(0);
 
-    // S^T (32 keys x 32 queries) = K Q^T on the codes, exact in int32.
+    // S^T (32 keys x 32 queries) = K Q^T on the codes, exact in int32.  These
+    // MFMAs are issued at raised wave priority (of the two wavefronts on a
+    // SIMD, the one starting a block goes first; measured 1.8% faster at topk
+    // 0.4 and 2.5% at topk 0.1, bit-identical.  The fp16 / bf16 kernel, with
+    // twice the S^T MFMAs, gains instead from raising it for PV).
     i32x16 si = i32x16{};
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) si = mfma_i8(kf[kk], qf[kk], si);
     read_vt(1);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     // The other buffer held block it-1, released by the last barrier.
     if (it + 1 < nloc) issue_block(kb_ahead, 1 - cur);

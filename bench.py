@@ -237,6 +237,24 @@ def extras(ops, synth, torch, steps, warmup):
         workload="b2 h32 s16384 d128 fp16, topk 0.4, pv_threshold 0 / 4 / 8",
         fmha_ms_no_skip=pv[0.0], fmha_ms_tau4=pv[4.0], fmha_ms_tau8=pv[8.0],
         speedup_tau4=pv[0.0] / pv[4.0], speedup_tau8=pv[0.0] / pv[8.0])
+    # A ragged length at the headline shape: s = 16347 (255 full blocks and
+    # one of 27 tokens), the same tensors viewed shorter.  The block map pools
+    # the partial block; the FMHA runs its masked kernel for it.
+    SR = 16347
+    qr, kr, vr = hc.q[:, :, :SR], hc.k[:, :, :SR], hc.v[:, :, :SR]
+    bmr = ops.build_block_map(qr, kr, hc.topk, hc.simthreshd1)
+    orr = torch.empty((B, H, SR, qr.shape[3]), dtype=qr.dtype, device=dev)
+    lr = torch.empty((B, H, SR), device=dev)
+    _, bmt = time_arm(lambda: ops.build_block_map(qr, kr, hc.topk, hc.simthreshd1, out=bmr), steps, warmup,
+                      torch)
+    _, ft = time_arm(lambda: ops.sparse_fmha_fwd(qr, kr, vr, bmr["lut"], bmr["count"], o=orr, lse=lr),
+                     steps, warmup, torch)
+    pairs = int(bmr["count"].sum().item())
+    out["ragged_headline"] = dict(
+        workload="b2 h32 s16347 d128 fp16 (last block 27 tokens), topk 0.4",
+        block_map_ms=median(bmt), fmha_ms=median(ft), pairs=pairs,
+        fmha_tflops_computed=pairs * F_BLK / median(ft) / 1e9)
+    del bmr, orr, lr
     # The same shape in bf16 (topk 0.4): block map and sparse FMHA.
     hb = synth.headline_case(dev, topk=0.4, dtype=torch.bfloat16)
     bmb = ops.build_block_map(hb.q, hb.k, hb.topk, hb.simthreshd1)

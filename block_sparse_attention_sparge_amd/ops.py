@@ -259,7 +259,8 @@ def sparse_fmha_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """Stage 2 (sparse_fmha_fwd).  q [b, h_q, s_q, d]; k, v [b, h_kv, s_k, d].
 
     Block mode (64, 64): lut [b, h_lut, nq, L] (+ count [b, h_lut, nq]),
-    nq = ceil(s_q / 64); lut None = dense.  Lengths need not be multiples of 64.  Token mode (1, 1): lut [b, h_kv, L] token positions.
+    nq = ceil(s_q / 64); lut None = dense.  Lengths need not be multiples of
+    64.  Token mode (1, 1): lut [b, h_kv, L] token positions.
     With num_splits > 1 the outputs are partials o [S, b, h_q, s_q, d] and
     lse [S, b, h_q, s_q] (fp32 unless out_dtype says otherwise).  causal sets
     SPARGE_FLAG_CAUSAL (block mode, s_q = s_k).  pv_threshold > 0 lets the

@@ -332,6 +332,40 @@ def test_fmha_strided_views_and_fp32_out(dev):
     _fmha_vs_oracle(q, k, v, lut, cnt, o, lse)
 
 
+def _packed_qk(dev, b, h, s, d, seed):
+    """Q and K as views into a packed (b, s, 3h, d) buffer, the layout a fused
+    QKV projection writes: sequence stride 3hd, head stride d."""
+    gam = [1.0 + 0.5 * i for i in range(h)]
+    q0 = synth.centroid_noise(b, h, s, d, 64, gam, 0.5, seed, 1, torch.bfloat16, dev)
+    k0 = synth.centroid_noise(b, h, s, d, 64, gam, 0.5, seed, 2, torch.bfloat16, dev)
+    base = torch.zeros((b, s, 3 * h, d), dtype=torch.bfloat16, device=dev)
+    base[:, :, 0:h] = q0.permute(0, 2, 1, 3)
+    base[:, :, h:2 * h] = k0.permute(0, 2, 1, 3)
+    return base[:, :, 0:h].permute(0, 2, 1, 3), base[:, :, h:2 * h].permute(0, 2, 1, 3), q0, k0
+
+
+def test_block_map_strided_views(dev):
+    q, k, _, _ = _packed_qk(dev, 2, 4, 640, 128, 14)
+    v = torch.zeros_like(q)
+    case = synth.BlockSparseCase("packed", q, k, v, [0.3, 0.4, 0.5, 0.6], [0.001] * 4)
+    _block_map_case(dev, case)
+
+
+@pytest.mark.parametrize("opts", [dict(smooth_k=True), dict(quantize_int8=True),
+                                  dict(smooth_k=True, causal=True, attention_sink=True)])
+def test_block_map_strided_views_match_contiguous(dev, opts):
+    # The layout must not change a single bit of any output, with the K-mean
+    # pass (smoothing) and the int8 codes reading through the strides too.
+    q, k, q0, k0 = _packed_qk(dev, 1, 4, 1000, 64, 15)
+    topk = [0.3, 0.4, 0.5, 0.6]
+    a = ops.build_block_map(q, k, topk, [0.001] * 4, return_debug=True, **opts)
+    c = ops.build_block_map(q0, k0, topk, [0.001] * 4, return_debug=True, **opts)
+    _sync()
+    for key in c:
+        if key != "workspace":
+            assert torch.equal(a[key], c[key]), key
+
+
 @pytest.mark.parametrize("splits", [2, 3, 7])
 def test_fmha_splits_then_combine(dev, splits):
     b, hq, hkv, sq, sk, d = 1, 4, 4, 128, 1024, 128

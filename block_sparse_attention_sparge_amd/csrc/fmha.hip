@@ -302,40 +302,45 @@ void fmha_block_kernel(FmhaArgs a) {
     // input type moves a term by up to 2^-8 of itself (bf16), which on a row
     // carried by one key would move the LSE by up to 4e-3 nats.
     // Masked rows may still have no key (m_run = -inf): their P is 0.
+    //
+    // O^T += V^T P^T over this wave's 32 keys, unless every query row of the
+    // wave lies more than the threshold below its running maximum.  The four
+    // PV MFMAs of k-step 0 are issued as soon as its 8 P values exist, so the
+    // exponentials of k-step 1 run in their shadow.  From the first PV MFMA to
+    // the last the wave runs at raised priority: of the two wavefronts sharing
+    // a SIMD (one from each resident workgroup), the one about to finish its
+    // block goes first and the other's softmax fills the MFMA shadows
+    // (measured, bit-identical: the priority 1.5-2.4% at topk 0.4 and about 4%
+    // at topk 0.1; the split issue 1% and 2% more; priority on the S MFMAs as
+    // well gains nothing).
     const float mref = MASKED && m_run == -INFINITY ? 0.f : m_run;
+    bool pv = true;
+    if constexpr (PVSKIP) pv = __any(!(m_cand < m_top - a.pv_tau2));
     u32x4 pf[2];
+    float p[16];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w], c2, -mref));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w + 1], c2, -mref));
-        pf[ks][w] = E::pack2(p0, p1);
-        l_run += p0 + p1;
+        p[8 * ks + 2 * w] = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w], c2, -mref));
+        p[8 * ks + 2 * w + 1] = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w + 1], c2, -mref));
+        pf[ks][w] = E::pack2(p[8 * ks + 2 * w], p[8 * ks + 2 * w + 1]);
       }
-    }
-
-    // O^T += V^T P^T over this wave's 32 keys, unless every query row of the
-    // wave lies more than the threshold below its running maximum.
-    // The PV MFMAs are issued at raised wave priority: of the two wavefronts
-    // sharing a SIMD (one from each resident workgroup), the one ready to
-    // finish its block goes first and the other's softmax fills the MFMA
-    // shadows (measured: 1.5-2.4% faster at topk 0.4, about 4% at topk 0.1,
-    // bit-identical; raising it for the S MFMAs as well gains nothing).
-    bool pv = true;
-    if constexpr (PVSKIP) pv = __any(!(m_cand < m_top - a.pv_tau2));
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (pv) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks == 0) {
+        __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (pv) {
 #pragma unroll
         for (int md = 0; md < NMD; ++md) acc_o[md] = mfma32<E>(vf[ks][md], pf[ks], acc_o[md]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int w = 0; w < 8; ++w) l_run += p[2 * w] + p[2 * w + 1];
 
     // The LUT entry of block it+2 is requested only now, after this block's
     // last LDS wait: scalar loads share the LDS wait counter but may return

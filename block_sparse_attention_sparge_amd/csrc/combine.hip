@@ -96,12 +96,79 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   if (a.lse_out && c == 0) a.lse_out[row] = live ? m + logf(wsum) : -INFINITY;
 }
 
+// The same combine for grids too small to hide memory latency by occupancy
+// (split-K decode: a few thousand rows).  The kernel above walks the parts one
+// dependent load at a time, twice; here every LSE is requested at once, then
+// every live part's 8 values, so a thread waits about two memory latencies
+// instead of 2 * n_parts.  The arithmetic is the same, in the same order, so
+// the results are bit-identical.  n_parts <= PN.
+template <class P, class O, int D, int PN>
+__global__ __launch_bounds__(256) void combine_small_kernel(CombineArgs a) {
+  constexpr int TPR = D / 8;   // threads per row
+  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gt / TPR;
+  if (row >= a.rows) return;
+  const int c = (int)(gt % TPR);
+
+  float l[PN];
+#pragma unroll
+  for (int i = 0; i < PN; ++i) l[i] = i < a.n_parts ? a.lse_parts[(int64_t)i * a.rows + row] : -INFINITY;
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < PN; ++i) m = fmaxf(m, l[i]);
+
+  float x[PN][8];
+#pragma unroll
+  for (int i = 0; i < PN; ++i) {
+    if (l[i] > -INFINITY) {
+      PartLoad<P>::load8(a.parts, (int64_t)i * a.part_stride + row * D + c * 8, x[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
+    }
+  }
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+  if (m > -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < PN; ++i) {
+      if (!(l[i] > -INFINITY)) continue;
+      const float w = expf(l[i] - m);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, x[i][e], acc[e]);
+      wsum += w;
+    }
+  }
+  const bool live = wsum > 0.f;
+  const float inv = live ? 1.0f / wsum : 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] *= inv;
+  OutStore<O>::store8(a.o, row * D + c * 8, acc);
+  if (a.lse_out && c == 0) a.lse_out[row] = live ? m + logf(wsum) : -INFINITY;
+}
+
+// Grids of at most this many workgroups (8 per CU) take the small-grid kernel
+// when the parts fit its registers.
+constexpr int64_t kCombineSmallGrid = 2048;
+
+template <class P, class O, int D>
+static void launch_combine_pod(const CombineArgs& a, dim3 grid, hipStream_t st) {
+  if ((int64_t)grid.x <= kCombineSmallGrid && a.n_parts <= 4)
+    hipLaunchKernelGGL((combine_small_kernel<P, O, D, 4>), grid, dim3(256), 0, st, a);
+  else if ((int64_t)grid.x <= kCombineSmallGrid && a.n_parts <= 16)
+    hipLaunchKernelGGL((combine_small_kernel<P, O, D, 16>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<P, O, D>), grid, dim3(256), 0, st, a);
+}
+
 template <class P, class O>
 static hipError_t launch_combine_po(const CombineArgs& a, int d, hipStream_t st) {
   const int64_t threads = a.rows * (d / 8);
   const dim3 grid((unsigned)((threads + 255) / 256));
-  if (d == 128) hipLaunchKernelGGL((combine_kernel<P, O, 128>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((combine_kernel<P, O, 64>), grid, dim3(256), 0, st, a);
+  if (d == 128) launch_combine_pod<P, O, 128>(a, grid, st);
+  else launch_combine_pod<P, O, 64>(a, grid, st);
   return hipGetLastError();
 }
 

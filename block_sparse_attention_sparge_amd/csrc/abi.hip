@@ -267,10 +267,10 @@ sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void*
   if (block_mode) {
     a.nqt = (s_q + 63) / 64;   // a partial last tile / block counts
     a.nkb = (s_k + 63) / 64;
-    // The kernel addresses a 64-row K or V block with 32-bit byte offsets.
-    const int64_t elem = 2, span = 64 * std::max(k_strides[2], v_strides[2]) * elem;
+    // The kernel addresses a 64-row Q tile or K/V block with 32-bit byte offsets.
+    const int64_t elem = 2, span = 64 * std::max({q_strides[2], k_strides[2], v_strides[2]}) * elem;
     if (span >= (int64_t(1) << 31))
-      return fail(SPARGE_ERR_UNSUPPORTED, "a 64-row K/V block spans %lld bytes (limit 2^31)", (long long)span);
+      return fail(SPARGE_ERR_UNSUPPORTED, "a 64-row Q/K/V block spans %lld bytes (limit 2^31)", (long long)span);
     if (!lut && lut_count) return fail(SPARGE_ERR_INVALID, "lut_count given without lut");
     return hip_status(launch_fmha_block(a, dt, o_dt, d, s), "sparse_fmha launch");
   }

@@ -72,6 +72,16 @@ namespace sparge {
 // MASKED kernel removes keys by position: past the query (causal) and past
 // the end of a ragged K sequence, whose last block is loaded with its missing
 // rows repeating its last row (finite values whose scores are then -inf).
+// Element type of O: fp32 partials or the input type.
+template <class T, bool F32>
+struct OutType {
+  typedef T type;
+};
+template <class T>
+struct OutType<T, true> {
+  typedef float type;
+};
+
 template <class E, int D, bool OUT_F32, bool MASKED, bool PVSKIP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fmha_block_kernel(FmhaArgs a) {
@@ -84,6 +94,7 @@ void fmha_block_kernel(FmhaArgs a) {
   constexpr int VSW = G16 / 4;               // V row r's granules are XOR-swizzled by VSW * r
   __shared__ __attribute__((aligned(16))) T sK[2 * TILE];
   __shared__ __attribute__((aligned(16))) T sV[2 * TILE];
+  __shared__ float s_ml[128];                // (m, l) of the kh = 1 waves, per query half
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -135,19 +146,6 @@ void fmha_block_kernel(FmhaArgs a) {
     }
     return;
   }
-
-  // Q^T fragments (B operand): lane (query l32, half hl) holds d = 16kk + 8hl .. +7.
-  const T* qp = reinterpret_cast<const T*>(a.q) + bb * a.qs[0] + hh * a.qs[1] +
-                (int64_t)min(q0 + l32, a.sq - 1) * a.qs[2] + 8 * hl;
-  u32x4 qf[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) qf[kk] = load16(qp + 16 * kk);
-  // Consume the Q loads here.  The K/V loads below are invisible to the
-  // compiler's wait counting; if Q were still pending at the loop, the waits
-  // it places before the first S^T MFMAs would also wait for the K/V
-  // prefetches in flight (the hardware counter does not tell them apart).
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qf[kk]));
 
   const char* kbase = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k) + bb * a.ks[0] + hk * a.ks[1]);
   const char* vbase = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v) + bb * a.vs[0] + hk * a.vs[1]);
@@ -211,9 +209,38 @@ void fmha_block_kernel(FmhaArgs a) {
   const int vrow0 = 32 * kh + 4 * (vgrp >> 1) + (vs16 >> 2);
   const int vcol0 = 16 * (vgrp & 1) + 4 * (vs16 & 3);
 
-  // Prologue: block 0 in LDS, LUT entry of block 1 read.
+  // Prologue: the Q tile and block 0 by direct loads.  Q goes to V buffer 1,
+  // which the first step refills only after every wave has taken its Q^T
+  // fragments (the second barrier).  Loaded this way each instruction moves
+  // whole rows; loads of the fragments straight from memory would touch 32
+  // rows with 32 bytes each.  Q uses K's layout (granule g of row r at slot
+  // g ^ (r mod G16)) and the rows of a partial last tile repeat its last row.
+  {
+    const char* qbase = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.q) + bb * a.qs[0] +
+                                                      hh * a.qs[1] + (int64_t)(64 * qt) * a.qs[2]);
+    const int last = a.sq - 1 - 64 * qt;
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) {
+      const int gi = 64 * (wave * NDMA + j) + lane;
+      const int r = gi / G16, sl = gi % G16, rc = min(r, last);
+      const uint32_t off = (uint32_t)((TILE + (wave * NDMA + j) * 64 * 8) * sizeof(T));
+      dma16(qbase, (uint32_t)((rc * a.qs[2] + (sl ^ (r % G16)) * 8) * (int64_t)sizeof(T)), sv_lds + off);
+    }
+  }
   issue_block(kb_of(0), 0);
   wait_dma();
+  __syncthreads();
+  // Q^T fragments (B operand): lane (query l32, half hl) holds d = 16kk + 8hl .. +7
+  // of tile row 32 qh + l32.
+  u32x4 qf[NKK];
+  {
+    const int qrow = 32 * qh + l32, qsw = qrow % G16;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qf[kk] = *reinterpret_cast<const u32x4*>(&sV[TILE + (qrow * G16 + ((2 * kk + hl) ^ qsw)) * 8]);
+  }
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qf[kk]));
   __syncthreads();
   int kb_ahead = nloc > 1 ? kb_of(1) : 0;
   int kb_cur = MASKED ? kb_of(0) : 0;
@@ -363,10 +390,19 @@ void fmha_block_kernel(FmhaArgs a) {
     step(it + 1, Buf<1>{});
   }
 
-  // Merge the two key halves: waves kh = 1 publish (m, l, O^T); waves kh = 0 combine.
+  // Merge the two key halves: waves kh = 1 publish (m, l, O^T); waves kh = 0
+  // combine and write the finished tile, in the output type, to LDS; then all
+  // four waves store it with 16 bytes per lane, whole rows per instruction
+  // (storing from the O^T fragments directly writes 8 or 16 bytes into each
+  // of 32 rows per instruction).  Staged rows are [64][OG] 16-byte granules,
+  // granule g of row r at slot g ^ (r mod OG), so neither the fragment writes
+  // (32 rows, one column) nor the row reads meet the same banks.
+  typedef typename OutType<T, OUT_F32>::type OT;
+  constexpr int OG = D * (int)sizeof(OT) / 16;   // 16-byte granules per O row
   const float l_w = l_run + __shfl_xor(l_run, 32, kWave);
   float* mrg = reinterpret_cast<float*>(sK) + qh * (NMD * 16 * 64);
-  float* ml = reinterpret_cast<float*>(sV) + qh * 64;
+  float* ml = s_ml + qh * 64;
+  char* stg = reinterpret_cast<char*>(sV);
   if (kh == 1) {
 #pragma unroll
     for (int md = 0; md < NMD; ++md)
@@ -378,33 +414,55 @@ void fmha_block_kernel(FmhaArgs a) {
     }
   }
   __syncthreads();
-  if (kh == 1) return;
-  const float m1 = ml[l32], l1 = ml[32 + l32];
-  float m = fmaxf(m_run, m1);
-  // Causal: a query row whose listed keys all lie past it has no key at all
-  // (both halves at -inf): O = 0, LSE = -inf.
-  const bool empty = MASKED && m == -INFINITY;
-  if (!row_ok) return;
-  if (empty) m = 0.f;
-  const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
-  const float l_tot = l_w * a0 + l1 * a1;
-  const float inv = empty ? 0.f : 1.0f / l_tot;
-  const float s0 = a0 * inv, s1 = a1 * inv;
+  if (kh == 0) {
+    const float m1 = ml[l32], l1 = ml[32 + l32];
+    float m = fmaxf(m_run, m1);
+    // Causal: a query row whose listed keys all lie past it has no key at all
+    // (both halves at -inf): O = 0, LSE = -inf.
+    const bool empty = MASKED && m == -INFINITY;
+    if (empty) m = 0.f;
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+    const float l_tot = l_w * a0 + l1 * a1;
+    const float inv = empty ? 0.f : 1.0f / l_tot;
+    const float s0 = a0 * inv, s1 = a1 * inv;
+    const int tr = 32 * qh + l32;                  // row of the tile
+    char* srow = stg + tr * (OG * 16);
 #pragma unroll
-  for (int md = 0; md < NMD; ++md) {
+    for (int md = 0; md < NMD; ++md) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      float x[4];
+      for (int g = 0; g < 4; ++g) {
+        float x[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g + i;
-        x[i] = acc_o[md][r] * s0 + mrg[(md * 16 + r) * 64 + lane] * s1;
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g + i;
+          x[i] = acc_o[md][r] * s0 + mrg[(md * 16 + r) * 64 + lane] * s1;
+        }
+        // Columns 32 md + 8 g + 4 hl .. +3.
+        if constexpr (OUT_F32) {
+          const int gr = 8 * md + 2 * g + hl;
+          *reinterpret_cast<floatx4*>(srow + ((gr ^ (tr % OG)) * 16)) = floatx4{x[0], x[1], x[2], x[3]};
+        } else {
+          const int gr = 4 * md + g;
+          *reinterpret_cast<u32x2*>(srow + ((gr ^ (tr % OG)) * 16) + 8 * hl) =
+              u32x2{E::pack2(x[0], x[1]), E::pack2(x[2], x[3])};
+        }
       }
-      const int d0 = 32 * md + 8 * g + 4 * hl;
-      store4<E, OUT_F32>(a.o, orow + d0, x[0], x[1], x[2], x[3]);
+    }
+    if (lse_row && hl == 0 && row_ok) lse_row[q0 + l32] = empty ? -INFINITY : (m + __log2f(l_tot)) * kLn2;
+  }
+  __syncthreads();
+  const int nrows = min(64, a.sq - 64 * qt);     // rows of a partial last tile
+  OT* obase = reinterpret_cast<OT*>(a.o) + (int64_t)split * a.o_split_stride + bb * a.os[0] + hh * a.os[1] +
+              (int64_t)(64 * qt) * a.os[2];
+#pragma unroll
+  for (int k = 0; k < OG / 4; ++k) {
+    const int idx = tid + 256 * k;
+    const int r = idx / OG, gs = idx % OG;
+    if (r < nrows) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * (OG * 16) + ((gs ^ (r % OG)) * 16));
+      store16(obase + (int64_t)r * a.os[2] + gs * (16 / (int)sizeof(OT)), v);
     }
   }
-  if (lse_row && hl == 0) lse_row[q0 + l32] = empty ? -INFINITY : (m + __log2f(l_tot)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------

@@ -168,7 +168,7 @@ size_t sparge_build_block_map_workspace(int b, int h, int s_q, int s_k, int d,
  *   s_j = scale * <q_i, k_j>,  LSE_i = ln sum_j exp(s_j),
  *   O_i = sum_j exp(s_j - LSE_i) v_j;   J empty => O_i = 0, LSE_i = -inf.
  *
- * Block mode (blk_q = blk_k = 64): 64 rows of K or V must span less than
+ * Block mode (blk_q = blk_k = 64): 64 rows of Q, K or V must span less than
  * 2^31 bytes (SPARGE_ERR_UNSUPPORTED otherwise; the LUT is read-only for the
  * duration of the call).  A LUT row belongs to (b, lut head, q tile of 64
  * rows) and lists K blocks kb in [0, nk), nk = ceil(s_k / 64) (keys

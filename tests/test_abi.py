@@ -161,6 +161,7 @@ def _fmha(lib, **kw):
     (dict(lut=None, cnt=FAKE), ops.SPARGE_ERR_INVALID),
     (dict(scale=float("nan")), ops.SPARGE_ERR_INVALID),
     (dict(vs=_s3(2 * 512 * 128, 512 * 128, 1 << 24)), ops.SPARGE_ERR_UNSUPPORTED),   # 64 rows span 2^31 bytes
+    (dict(qs=_s3(8 * 512 * 128, 512 * 128, 1 << 24)), ops.SPARGE_ERR_UNSUPPORTED),   # 64 Q rows likewise
     (dict(flags=ops.SPARGE_FLAG_SMOOTH_K), ops.SPARGE_ERR_INVALID),                  # block-map flag only
     (dict(flags=ops.SPARGE_FLAG_CAUSAL, sk=1024), ops.SPARGE_ERR_UNSUPPORTED),       # causal, s_q != s_k
     (dict(flags=ops.SPARGE_FLAG_CAUSAL, bq=1, bk=1, cnt=None, lh=2), ops.SPARGE_ERR_INVALID),   # token mode

@@ -16,6 +16,10 @@ source so that bench.py stops quoting it once the kernel changes.
 
 A third report, bytes, gives copy-calibrated HBM bytes per dispatch for
 every kernel of the library in two counter runs, grouped by kernel and grid.
+A fourth, counters, gives the per-arm mean of every counter of one --pmc run
+over the sparse FMHA launches (e.g. MfmaUtil, LdsUtil, LDSBankConflict and
+SQ_INSTS_VALU_MFMA_MOPS_F16, whose count times 512 is the MFMA flops), next
+to the launch's algorithmic flops when the arm's block pairs are given.
 
 Usage:
   python -m block_sparse_attention_sparge_amd.profile_summary trace DIR \
@@ -101,6 +105,37 @@ def _counter_means(dirpath: str, steps: int, warmup: int):
         if v:
             res[name] = sum(v) / len(v)
     return res
+
+
+def counters_report(dirpath: str, steps: int, warmup: int, command: str, pairs: dict,
+                    flops_per_pair: float) -> str:
+    rows = list(csv.DictReader(open(_one(dirpath, "*counter_collection.csv"))))
+    fm = _fmha_dispatches(rows)
+    per = {}
+    for r in fm:
+        d = per.setdefault(int(r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ids = sorted(per)
+    names = sorted({n for d in per.values() for n in d})
+    out = ["# Hardware counters of the sparse FMHA (rocprofv3 --pmc)", "", "Command:", "", "```",
+           command, "```", "",
+           f"Per-arm means over the FMHA launches of the bench (dispatch order; steps {steps}, warmup {warmup}).",
+           "", "| arm | launches | " + " | ".join(names) + " |",
+           "|---|---|" + "---|" * len(names)]
+    extra = []
+    for name, a, b in arm_slices(steps, warmup):
+        sel = [per[i] for i in ids[a:b]]
+        if not sel:
+            continue
+        means = {n: statistics.fmean(d.get(n, 0.0) for d in sel) for n in names}
+        out.append(f"| {name} | {len(sel)} | " + " | ".join(f"{means[n]:.4g}" for n in names) + " |")
+        if "SQ_INSTS_VALU_MFMA_MOPS_F16" in means and name in pairs:
+            alg = flops_per_pair * pairs[name]
+            extra.append(f"- {name}: MFMA flops counted {means['SQ_INSTS_VALU_MFMA_MOPS_F16'] * 512:.4e}, "
+                         f"algorithmic {alg:.4e} ({pairs[name]} block pairs x {flops_per_pair:.4g})")
+    if extra:
+        out += ["", "MFMA work per launch against the algorithmic work:", ""] + extra
+    return "\n".join(out) + "\n"
 
 
 def _copy_kib(dirpath: str) -> float:
@@ -201,6 +236,13 @@ def main(argv=None) -> int:
     f.add_argument("--steps", type=int, required=True)
     f.add_argument("--warmup", type=int, required=True)
     f.add_argument("--command", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--steps", type=int, required=True)
+    c.add_argument("--warmup", type=int, required=True)
+    c.add_argument("--command", required=True)
+    c.add_argument("--pairs", default="{}", help='JSON {"topk 0.4": pairs, ...}')
+    c.add_argument("--flops-per-pair", type=float, default=4.0 * 64 * 64 * 128)
     bt = sub.add_parser("bytes")
     for opt in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--command"):
         bt.add_argument(opt, required=True)
@@ -208,6 +250,9 @@ def main(argv=None) -> int:
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         sys.stdout.write(trace_report(a.dir, a.steps, a.warmup, a.command))
+    elif a.cmd == "counters":
+        sys.stdout.write(counters_report(a.dir, a.steps, a.warmup, a.command, json.loads(a.pairs),
+                                         a.flops_per_pair))
     elif a.cmd == "bytes":
         sys.stdout.write(bytes_report(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes, a.command))
     else:

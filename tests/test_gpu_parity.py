@@ -101,6 +101,31 @@ def test_combine_many_parts(dev):
     check_lse(l, rl, tol=1e-4)
 
 
+@pytest.mark.parametrize("n,d,pdt", [(8, 128, torch.float32), (16, 64, torch.bfloat16), (3, 128, torch.float16)])
+def test_combine_small_grid_matches_streaming_kernel(dev, n, d, pdt):
+    # Grids of up to 2048 workgroups with up to 16 parts take the kernel that
+    # puts every part in flight at once; larger grids stream the parts.  Both
+    # must give the same bits for the same rows: merge 64 or 128 heads of rows
+    # (over 2048 workgroups), then the first 2 heads alone (a small grid).
+    b, h, s = 1, 64 if d == 128 else 128, 1024
+    g = torch.Generator(device=dev).manual_seed(300 + n)
+    parts = torch.randn(n, b, h, s, d, generator=g, device=dev).to(pdt)
+    lse = torch.randn(n, b, h, s, generator=g, device=dev) * 3
+    lse[torch.rand(n, b, h, s, generator=g, device=dev) < 0.3] = -math.inf
+    lse[:, 0, 1, :7] = -math.inf                      # every part empty on some rows
+    assert b * h * s * (d // 8) // 256 > 2048
+    o_big, l_big = ops.attn_combine(parts, lse, out_dtype=torch.float32)
+    o_small, l_small = ops.attn_combine(parts[:, :, :2].contiguous(), lse[:, :, :2].contiguous(),
+                                        out_dtype=torch.float32)
+    _sync()
+    assert torch.equal(o_small, o_big[:, :2])
+    assert torch.equal(l_small, l_big[:, :2])
+    ro, rl = oracle.combine(list(np64(parts[:, :, :2])), list(np64(lse[:, :, :2])))
+    tol = 2e-6 if pdt == torch.float32 else 8e-3
+    check_o(o_small, ro, atol=tol, rtol=tol, what="combined O")
+    check_lse(l_small, rl, tol=1e-5)
+
+
 def test_combine_partials_with_stride_padding(dev):
     n, b, h, s, d = 3, 1, 2, 33, 128
     g = torch.Generator(device=dev).manual_seed(7)

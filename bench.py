@@ -107,7 +107,7 @@ def run_step_arm(ops, case, topk, steps, warmup, torch):
                 fmha_spread=(max(fm_ms) - min(fm_ms)) / median(fm_ms), pairs=pairs)
 
 
-def cpu_baseline(case, topk, heads=8):
+def cpu_baseline(case, topk, heads=16):
     """The fp64 oracle on `heads` heads (b=0, h=0..heads-1) of the workload:
     block map + attention over the selected blocks."""
     import numpy as np
@@ -379,7 +379,7 @@ def main(argv=None) -> int:
         log("extras: two-pass combine, combine at headline size, decode")
         res["other_rows"] = extras(ops, synth, torch, args.steps, args.warmup)
     if not args.no_cpu:
-        log("cpu baseline (oracle, one head)")
+        log("cpu baseline (oracle, 16 heads)")
         res["cpu_baseline"] = cpu_baseline(case, 0.4)
     print(json.dumps(res), flush=True)
     return 0

@@ -285,7 +285,7 @@ __device__ __forceinline__ int count_at_least(const uint32_t (&pb)[KPL], const b
 }
 
 template <int D, int KPL>
-__global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void score_select_kernel(SelectArgs a) {
   constexpr int NKP = 64 * KPL;
   constexpr int SP = NKP + 4;            // padded pitch of a score row (floats)
   constexpr int NG = D / 16;             // 16-wide slices of the head dimension
@@ -327,6 +327,17 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
   }
   const float* km = a.k_mean + bkv * nk * D;
   const float* ksim = a.k_sim + bkv * nk;
+  // The small per-block inputs this wave needs are requested early so that
+  // their latencies overlap the loads of the pooled means: the K gate value
+  // of the column this lane scores (one column step ahead, like the means),
+  // the K gate values of the row elements this lane selects, and the Q gate
+  // flag of row `lane`.
+  auto ksim_at = [&](int kb) { return kb < nk ? ksim[kb] : 0.f; };
+  float ksim_el[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) ksim_el[j] = ksim_at(lane * KPL + j);
+  const bool qflag_lane = lane < rows && a.sim_q[bh * a.nq + qb0 + lane] != 0;
+  float ks_cur = ksim_at(16 * wave + m16), ks_nxt = 0.f;
   auto load_k = [&](floatx4 (&kf)[NG], int kb) {
     const float* krow = km + (int64_t)kb * D + 4 * k4;
 #pragma unroll
@@ -340,7 +351,10 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
 #pragma unroll 1
   for (int c = 0; c < KPL; ++c) {
     const int kb = 64 * c + 16 * wave + m16;
-    if (c + 1 < KPL) load_k(kn, kb + 64);
+    if (c + 1 < KPL) {
+      load_k(kn, kb + 64);
+      ks_nxt = ksim_at(kb + 64);
+    }
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -349,7 +363,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
     }
     // C: lane holds column kb for rows 4*k4 .. 4*k4+3.  Causal: block kb is
     // in the future of Q-tile qb0 + row when kb > qb0 + row.
-    const bool live = kb < nk && ksim[kb] > thr;
+    const bool live = kb < nk && ks_cur > thr;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok = live && (!a.causal || kb <= qb0 + 4 * k4 + i);
@@ -357,6 +371,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
     }
 #pragma unroll
     for (int g = 0; g < NG; ++g) kf[g] = kn[g];
+    ks_cur = ks_nxt;
   }
   __syncthreads();
 
@@ -365,14 +380,13 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
     const int e = lane * KPL + j;
-    kgate[j] = e < nk && !(ksim[e] > thr);             // K block forced on
+    kgate[j] = e < nk && !(ksim_el[j] > thr);          // K block forced on
   }
   if (a.sim_k && qb0 == 0 && wave == 0) {
 #pragma unroll
     for (int j = 0; j < KPL; ++j)
       if (lane * KPL + j < nk) a.sim_k[bh * nk + lane * KPL + j] = kgate[j] ? 0 : 1;
   }
-  const bool qflag_lane = lane < rows && a.sim_q[bh * a.nq + qb0 + lane] != 0;
   const uint64_t qflags = __ballot(qflag_lane);
 
   const int nsel_h = a.nsel[hh];

@@ -73,7 +73,7 @@ void fmha_qk8_kernel(FmhaArgs a) {
   if (lin >= G) return;
   // Causal rows grow with the tile index: the rows of a head are taken last
   // tile first, so that each XCD ends on short rows rather than on a few long
-  // ones (measured 1.6% faster sparse, 2.0% dense, at the headline shape).
+  // ones (measured 1.6% faster sparse, 2.0% dense, at b2 h32 s16384 d128).
   const int qt = MASKED && a.causal ? a.nqt - 1 - (int)(lin % a.nqt) : (int)(lin % a.nqt);
   lin /= a.nqt;
   const int hh = (int)(lin % a.hq);

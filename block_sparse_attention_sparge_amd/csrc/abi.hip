@@ -334,9 +334,9 @@ sparge_status sparse_fmha_fwd_qk_int8(const int8_t* q, const float* q_scale, con
   } else if (lut_count) {
     return fail(SPARGE_ERR_INVALID, "lut_count given without lut");
   }
-  const int64_t span = std::max(64 * k_strides[2], 64 * v_strides[2] * 2);
+  const int64_t span = std::max({64 * q_strides[2], 64 * k_strides[2], 64 * v_strides[2] * 2});
   if (span >= (int64_t(1) << 31))
-    return fail(SPARGE_ERR_UNSUPPORTED, "a 64-row K/V block spans %lld bytes (limit 2^31)", (long long)span);
+    return fail(SPARGE_ERR_UNSUPPORTED, "a 64-row Q/K/V block spans %lld bytes (limit 2^31)", (long long)span);
 
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
   FmhaArgs a;

@@ -59,6 +59,7 @@ void fmha_qk8_kernel(FmhaArgs a) {
   constexpr int VSW = G16 / 4;
   __shared__ __attribute__((aligned(16))) int8_t sK[2 * TILE];
   __shared__ __attribute__((aligned(16))) T sV[2 * TILE];
+  __shared__ float s_ml[128];                // (m, l) of the kh = 1 waves, per query half
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -111,15 +112,6 @@ void fmha_qk8_kernel(FmhaArgs a) {
     }
     return;
   }
-
-  // Q^T codes (B operand): lane (query l32, half hl) holds d = 32kk + 16hl .. +15.
-  const int8_t* qp = reinterpret_cast<const int8_t*>(a.q) + bb * a.qs[0] + hh * a.qs[1] +
-                     (int64_t)min(q0 + l32, a.sq - 1) * a.qs[2] + 16 * hl;
-  u32x4 qf[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) qf[kk] = load16(qp + 32 * kk);
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qf[kk]));
 
   // Scales: the tile's Q scale and the softmax scale are folded once; the K
   // scale of each block joins them per block.
@@ -193,8 +185,34 @@ void fmha_qk8_kernel(FmhaArgs a) {
   // Block 0 in LDS; the LUT entry of block 1 and the K scale of block 0 read.
   // Block it+1's K/V loads are issued in the middle of step it (as in the
   // fp16 / bf16 kernel).
+  // The Q codes arrive by direct loads into K buffer 1 (refilled only after
+  // the second barrier below), in K's layout, with the rows of a partial
+  // last tile repeating its last row; each instruction then moves whole rows.
+  {
+    const char* qbase = reinterpret_cast<const char*>(a.q) + bb * a.qs[0] + hh * a.qs[1] + (int64_t)(64 * qt) * a.qs[2];
+    const int last = a.sq - 1 - 64 * qt;
+#pragma unroll
+    for (int j = 0; j < NDMA_K; ++j) {
+      const int gi = 64 * (wave * NDMA_K + j) + lane;
+      const int r = gi / GK, sl = gi % GK, rc = min(r, last);
+      dma16(qbase, (uint32_t)(rc * a.qs[2] + (sl ^ k8_swz<GK>(r)) * 16),
+            sk_lds + (uint32_t)(TILE + (wave * NDMA_K + j) * 64 * 16));
+    }
+  }
   issue_block(kb_of(0), 0);
   wait_dma();
+  __syncthreads();
+  // Q^T codes (B operand): lane (query l32, half hl) holds d = 32kk + 16hl .. +15
+  // of tile row 32 qh + l32.
+  u32x4 qf[NKK];
+  {
+    const int qrow = 32 * qh + l32, qsw = k8_swz<GK>(qrow);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qf[kk] = *reinterpret_cast<const u32x4*>(&sK[TILE + qrow * D + ((2 * kk + hl) ^ qsw) * 16]);
+  }
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qf[kk]));
   __syncthreads();
   int kb_ahead = nloc > 1 ? kb_of(1) : 0;
   float sk_cur = ksc[kb_of(0)];
@@ -326,10 +344,14 @@ void fmha_qk8_kernel(FmhaArgs a) {
   }
 
   // Merge the two key halves (as in the fp16 / bf16 kernel; the partial O^T
-  // goes to the V buffers, the larger ones here).
+  // goes to the V buffers, the larger ones here).  A 16-bit O tile is then
+  // staged in the K buffers (exactly its size) and stored as whole rows, as in
+  // the fp16 / bf16 kernel; fp32 partials are stored from the fragments.
   const float l_w = l_run + __shfl_xor(l_run, 32, kWave);
   float* mrg = reinterpret_cast<float*>(sV) + qh * (NMD * 16 * 64);
-  float* ml = reinterpret_cast<float*>(sK) + qh * 64;
+  float* ml = s_ml + qh * 64;
+  constexpr int OG = D * 2 / 16;                 // 16-byte granules per 16-bit O row
+  char* stg = reinterpret_cast<char*>(sK);
   if (kh == 1) {
 #pragma unroll
     for (int md = 0; md < NMD; ++md)
@@ -341,31 +363,54 @@ void fmha_qk8_kernel(FmhaArgs a) {
     }
   }
   __syncthreads();
-  if (kh == 1) return;
-  const float m1 = ml[l32], l1 = ml[32 + l32];
-  float m = fmaxf(m_run, m1);
-  const bool empty = MASKED && m == -INFINITY;
-  if (!row_ok) return;
-  if (empty) m = 0.f;
-  const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
-  const float l_tot = l_w * a0 + l1 * a1;
-  const float inv = empty ? 0.f : 1.0f / l_tot;
-  const float s0 = a0 * inv, s1 = a1 * inv;
+  if (kh == 0) {
+    const float m1 = ml[l32], l1 = ml[32 + l32];
+    float m = fmaxf(m_run, m1);
+    const bool empty = MASKED && m == -INFINITY;
+    if (empty) m = 0.f;
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+    const float l_tot = l_w * a0 + l1 * a1;
+    const float inv = empty ? 0.f : 1.0f / l_tot;
+    const float s0 = a0 * inv, s1 = a1 * inv;
+    const int tr = 32 * qh + l32;
+    char* srow = stg + tr * (OG * 16);
 #pragma unroll
-  for (int md = 0; md < NMD; ++md) {
+    for (int md = 0; md < NMD; ++md) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      float x[4];
+      for (int g = 0; g < 4; ++g) {
+        float x[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g + i;
-        x[i] = acc_o[md][r] * s0 + mrg[(md * 16 + r) * 64 + lane] * s1;
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g + i;
+          x[i] = acc_o[md][r] * s0 + mrg[(md * 16 + r) * 64 + lane] * s1;
+        }
+        const int d0 = 32 * md + 8 * g + 4 * hl;
+        if constexpr (OUT_F32) {
+          if (row_ok) store4<E, true>(a.o, orow + d0, x[0], x[1], x[2], x[3]);
+        } else {
+          const int gr = 4 * md + g;
+          *reinterpret_cast<u32x2*>(srow + ((gr ^ (tr % OG)) * 16) + 8 * hl) =
+              u32x2{E::pack2(x[0], x[1]), E::pack2(x[2], x[3])};
+        }
       }
-      const int d0 = 32 * md + 8 * g + 4 * hl;
-      store4<E, OUT_F32>(a.o, orow + d0, x[0], x[1], x[2], x[3]);
+    }
+    if (lse_row && hl == 0 && row_ok) lse_row[q0 + l32] = empty ? -INFINITY : (m + __log2f(l_tot)) * kLn2;
+  }
+  if constexpr (!OUT_F32) {
+    __syncthreads();
+    const int nrows = min(64, a.sq - 64 * qt);
+    T* obase = reinterpret_cast<T*>(a.o) + (int64_t)split * a.o_split_stride + bb * a.os[0] + hh * a.os[1] +
+               (int64_t)(64 * qt) * a.os[2];
+#pragma unroll
+    for (int k = 0; k < OG / 4; ++k) {
+      const int idx = tid + 256 * k;
+      const int r = idx / OG, gs = idx % OG;
+      if (r < nrows) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * (OG * 16) + ((gs ^ (r % OG)) * 16));
+        store16(obase + (int64_t)r * a.os[2] + gs * 8, v);
+      }
     }
   }
-  if (lse_row && hl == 0) lse_row[q0 + l32] = empty ? -INFINITY : (m + __log2f(l_tot)) * kLn2;
 }
 
 template <class E, int D>

@@ -240,7 +240,7 @@ sparge_status sparse_fmha_fwd(
  *   k        int8 [b, h_kv, s_k, d], strides for (b, h, s);
  *   k_scale  float [b, h_kv, ceil(s_k / 64)] contiguous.
  * A partial last block has its own scale (as the block map writes it).
- * d is 64 or 128; q, k, v, o 16-byte aligned; 64 rows of K or V must span
+ * d is 64 or 128; q, k, v, o 16-byte aligned; 64 rows of Q, K or V must span
  * less than 2^31 bytes.
  */
 sparge_status sparse_fmha_fwd_qk_int8(

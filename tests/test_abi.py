@@ -212,6 +212,7 @@ def _fmha8(lib, **kw):
     (dict(lut=None, cnt=FAKE), ops.SPARGE_ERR_INVALID),
     (dict(lh=4), ops.SPARGE_ERR_INVALID),
     (dict(vs=_s3(2 * 512 * 128, 512 * 128, 1 << 24)), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(qs=_s3(8 * 512 * 128, 512 * 128, 1 << 25)), ops.SPARGE_ERR_UNSUPPORTED),   # 64 Q code rows span 2^31 bytes
 ])
 def test_fmha_qk_int8_rejections(lib, kw, status):
     st = _fmha8(lib, **kw)

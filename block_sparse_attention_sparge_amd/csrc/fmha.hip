@@ -10,7 +10,8 @@
 // (Q-tile, head, batch, split); each wavefront owns 32 query rows and 32 keys
 // of every block and works in the transposed orientation S^T = K Q^T,
 // O^T += V^T P^T on the 32x32x16 fp16/bf16 MFMA:
-//   * Q^T stays in registers as the B operand for the whole row;
+//   * Q^T stays in registers as the B operand for the whole row; the Q tile
+//     itself arrives by direct global->LDS loads, whole rows per instruction;
 //   * K and V blocks arrive by direct global->LDS loads into double buffers;
 //     K is read row-major (A operand of S^T), V through the transposing LDS
 //     read (A operand of O^T);
@@ -20,7 +21,8 @@
 //   * the softmax runs in base 2 with the scale folded in once (aiter 4919
 //     page: one FMA per score, exp2), and the row sum is finished only at the
 //     end (one reciprocal per row);
-//   * the two key halves of a tile are merged at the end with the LSE rule;
+//   * the two key halves of a tile are merged at the end with the LSE rule,
+//     and the finished tile leaves through LDS as whole rows;
 //   * with a pv_threshold (CK page, "Status vs Upstream": a per-Q-tile skip
 //     in the attention kernel), a wavefront drops the PV product of a block
 //     when each of its 32 query rows scores, over the wavefront's 32 keys,
@@ -28,7 +30,7 @@
 //     of its half seen so far in the pass; those P still count in the row sum;
 //   * workgroups are renumbered so that consecutive rows of one head land on
 //     one XCD and share its L2 (aiter 4919 page: workgroups round-robin over
-//     the 8 XCDs by linear id).
+//     the 8 XCDs by linear id); causal rows are taken last tile first.
 // The token-list (decode) kernel is in fmha_tokens.hip.
 #include "attn_common.h"
 #include "common.h"

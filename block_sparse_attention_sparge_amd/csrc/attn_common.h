@@ -64,6 +64,15 @@ __device__ __forceinline__ void dma16(const void* gbase, uint32_t goff, uint32_t
                : "memory", "m0");
 }
 
+// The same load marked non-temporal, for data read once (a Q tile): it then
+// displaces less of the K/V blocks that other rows reuse from the caches.
+__device__ __forceinline__ void dma16_nt(const void* gbase, uint32_t goff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+               :
+               : "s"(lds_base), "v"(goff), "s"(gbase)
+               : "memory", "m0");
+}
+
 // max(x, x of lane l ^ 32).  v_permlane32_swap exchanges lanes 32..63 of its
 // first operand with lanes 0..31 of its second; with x in both, every lane
 // then holds its own value in one register and its partner's in the other.

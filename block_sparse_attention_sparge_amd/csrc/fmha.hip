@@ -220,6 +220,9 @@ void fmha_block_kernel(FmhaArgs a) {
   // whole rows; loads of the fragments straight from memory would touch 32
   // rows with 32 bytes each.  Q uses K's layout (granule g of row r at slot
   // g ^ (r mod G16)) and the rows of a partial last tile repeat its last row.
+  // Q and O are touched once, so their loads and stores are non-temporal and
+  // leave more of the caches to the K/V blocks that other rows reuse
+  // (measured 1.0-1.3% faster at topk 0.1, bit-identical).
   {
     const char* qbase = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.q) + bb * a.qs[0] +
                                                       hh * a.qs[1] + (int64_t)(64 * qt) * a.qs[2]);
@@ -229,7 +232,7 @@ void fmha_block_kernel(FmhaArgs a) {
       const int gi = 64 * (wave * NDMA + j) + lane;
       const int r = gi / G16, sl = gi % G16, rc = min(r, last);
       const uint32_t off = (uint32_t)((TILE + (wave * NDMA + j) * 64 * 8) * sizeof(T));
-      dma16(qbase, (uint32_t)((rc * a.qs[2] + (sl ^ (r % G16)) * 8) * (int64_t)sizeof(T)), sv_lds + off);
+      dma16_nt(qbase, (uint32_t)((rc * a.qs[2] + (sl ^ (r % G16)) * 8) * (int64_t)sizeof(T)), sv_lds + off);
     }
   }
   issue_block(kb_of(0), 0);
@@ -465,7 +468,7 @@ void fmha_block_kernel(FmhaArgs a) {
     const int r = idx / OG, gs = idx % OG;
     if (r < nrows) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * (OG * 16) + ((gs ^ (r % OG)) * 16));
-      store16(obase + (int64_t)r * a.os[2] + gs * (16 / (int)sizeof(OT)), v);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(obase + (int64_t)r * a.os[2] + gs * (16 / (int)sizeof(OT))));
     }
   }
 }

@@ -408,81 +408,69 @@ def block_sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     return o, lse
 
 
-def pv_skip_units(scores: np.ndarray, tau: float, q_unit: int, k_unit: int,
-                  num_splits: int = 1, return_margin: bool = False):
-    """Which P.V products the pv_threshold rule drops, for one Q-tile.
+def pv_skip_blocks(scores: np.ndarray, tau: float, return_margin: bool = False):
+    """Which listed blocks of one Q-tile the pv_threshold rule drops.
 
-    CK page, "Status vs Upstream": pv_threshold is a per-Q-tile skip inside the
-    attention kernel, a pure speed measure.  The pages give no test; reading
-    R25 takes the plainest one that leaves the result an approximation of the
-    same attention:
+    CK page, "Status vs Upstream", not-yet-ported list: pv_threshold is a
+    per-Q-tile skip inside the attention kernel, a pure speed measure.  The
+    unit is therefore one Q-tile against one listed block.  The pages give no
+    test; reading R25 takes the plainest one that leaves the result an
+    approximation of the same attention:
 
-    * the listed blocks are visited in LUT order, as by an online softmax,
-      split into `num_splits` consecutive chunks of ceil(n / num_splits)
-      blocks, each chunk a pass of its own (its running maximum starts at
-      -inf);
-    * the keys of every block are cut into streams of `k_unit` keys (key j of a
-      block is in stream j // k_unit) and the query rows into groups of
-      `q_unit`; each (row group, stream) keeps its own running maximum per row,
-      M_i = max of the scores of row i over that stream's keys of the blocks
-      visited so far in the pass, this block included;
-    * the unit (row group, stream, block) is skipped when every row i of the
-      group has r_i < M_i - tau, r_i its maximum score over the unit's keys.
+    * the listed blocks are visited in LUT order, as by an online softmax, in
+      one pass over the row;
+    * for query row i of the tile, M_i is its running maximum: the largest
+      score of row i over the keys of the blocks visited so far, this block
+      included; r_i is its largest score over this block's keys;
+    * the block is dropped for the whole tile when r_i < M_i - tau holds for
+      every row i of the tile.
 
-    q_unit = k_unit = 64 is the whole Q-tile against the whole block.  A row
-    with no key in the unit has r_i = -inf; while M_i is still -inf nothing is
-    skipped.
+    A row with no key in the block has r_i = -inf; while M_i is still -inf
+    (the row has met no key yet) the block is kept.
 
     scores [rows, n_blocks, blk_k] (scaled, -inf where masked).  Returns a bool
-    array [rows // q_unit, n_blocks, blk_k // k_unit], True = skipped.  With
-    `return_margin`, also max_i (r_i - (M_i - tau)) per unit over the rows with
-    a key in the unit (-inf if none): how far the decision is from flipping.
+    array [n_blocks], True = dropped.  With `return_margin`, also, per block,
+    max_i (r_i - (M_i - tau)) over the rows with a key in the block (-inf if
+    none): the decision flips where this crosses 0, so it says how far the
+    decision lies from the threshold.
     """
-    rows, n, blk_k = scores.shape
-    n_groups, n_streams = rows // q_unit, blk_k // k_unit
-    skip = np.zeros((n_groups, n, n_streams), dtype=bool)
-    margin = np.full((n_groups, n, n_streams), NEG_INF)
-    if n == 0:
-        return (skip, margin) if return_margin else skip
-    chunk = -(-n // num_splits)
-    for u in range(n_groups):
-        for g in range(n_streams):
-            part = scores[u * q_unit:(u + 1) * q_unit, :, g * k_unit:(g + 1) * k_unit]
-            r = part.max(axis=2)                            # [q_unit, n]
-            for t in range(n):
-                if t % chunk == 0:
-                    run = np.full(q_unit, NEG_INF)          # a new pass starts
-                run = np.maximum(run, r[:, t])
-                skip[u, t, g] = bool(np.all(r[:, t] < run - tau))
-                live = r[:, t] > NEG_INF
-                if live.any():
-                    margin[u, t, g] = float(np.max(r[live, t] - (run[live] - tau)))
+    rows, n, _ = scores.shape
+    skip = np.zeros(n, dtype=bool)
+    margin = np.full(n, NEG_INF)
+    run = np.full(rows, NEG_INF)
+    for t in range(n):
+        r = scores[:, t, :].max(axis=1)                 # [rows]
+        run = np.maximum(run, r)
+        skip[t] = bool(np.all(r < run - tau))
+        live = r > NEG_INF
+        if live.any():
+            margin[t] = float(np.max(r[live] - (run[live] - tau)))
     return (skip, margin) if return_margin else skip
 
 
 def block_sparse_attention_pv_skip(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                                    lut: Optional[np.ndarray], count: Optional[np.ndarray],
-                                   pv_threshold: float, q_unit: int = 64, k_unit: int = 64,
-                                   num_splits: int = 1, scale: Optional[float] = None,
+                                   pv_threshold: float, scale: Optional[float] = None,
                                    lut_per_kv_head: bool = False, causal: bool = False,
                                    return_skips: bool = False, return_margins: bool = False):
     """block_sparse_attention with the pv_threshold skip (reading R25).
 
-    A skipped unit's keys still count in each row's softmax denominator and in
+    A dropped block's keys still count in each row's softmax denominator and in
     its LSE; only their P.V terms leave the numerator:
         O_i = sum_{j kept} exp(s_ij - m_i) v_j / sum_{j all} exp(s_ij - m_i),
         LSE_i = m_i + ln sum_{j all} exp(s_ij - m_i),
     with m_i the maximum over all of row i's keys.  The LSE therefore equals the
-    exact one, and |O_i - O_exact,i| <= (skipped keys of row i) * exp(-tau) *
-    max |v|, since every skipped score lies more than tau below m_i.  The blocks
+    exact one, and |O_i - O_exact,i| <= (dropped keys of row i) * exp(-tau) *
+    max |v|, since every dropped score lies more than tau below m_i.  The blocks
     of 64 queries and 64 keys are the ones of block_sparse_attention.  A
     partial last K block is completed with masked keys (score -inf) and a
     partial last Q-tile with copies of its last row: a copy repeats a decision
-    the row group already takes, so the units are decided by the tile's rows.
-    With `return_skips`, also returns the number of skipped units and of all
-    units; with `return_margins`, then [b, h_q, nq, 64 // q_unit] the smallest
-    |margin| (pv_skip_units) of the row group's units: decisions closer than
-    rounding to the threshold may fall either way in another precision.
+    the tile already takes, so the blocks are decided by the tile's own rows.
+    With `return_skips`, also returns the number of dropped (tile, block)
+    pairs and of all listed pairs; with `return_margins`, then [b, h_q, nq]
+    the smallest |margin| (pv_skip_blocks) over the tile's blocks: decisions
+    closer than rounding to the threshold may fall either way in another
+    precision.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -496,8 +484,8 @@ def block_sparse_attention_pv_skip(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     nq, nk = -(-s_q // blk), -(-s_k // blk)
     o = np.zeros((b, h_q, s_q, v.shape[3]))
     lse = np.zeros((b, h_q, s_q))
-    n_skip = n_units = 0
-    near = np.full((b, h_q, nq, blk // q_unit), math.inf)
+    n_skip = n_pairs = 0
+    near = np.full((b, h_q, nq), math.inf)
     for ib in range(b):
         for ih in range(h_q):
             hk = ih // ratio
@@ -520,25 +508,24 @@ def block_sparse_attention_pv_skip(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                 s = scale * (q[ib, ih, qpos] @ k[ib, hk, idx].T)          # [64, n * 64]
                 allowed = exists[None, :] & (idx[None, :] <= qpos[:, None] if causal else True)
                 s = np.where(allowed, s, NEG_INF)
-                skip, margin = pv_skip_units(s.reshape(blk, n, blk), pv_threshold, q_unit,
-                                             k_unit, num_splits, return_margin=True)
-                near[ib, ih, qb] = np.abs(margin).min(axis=(1, 2))
+                skip, margin = pv_skip_blocks(s.reshape(blk, n, blk), pv_threshold, return_margin=True)
+                near[ib, ih, qb] = np.abs(margin).min()
                 n_skip += int(skip.sum())
-                n_units += skip.size
-                # kept[i, t, j]: key j of block t stays in row i's numerator
-                kept = ~np.repeat(np.repeat(skip, q_unit, axis=0), k_unit, axis=2)
+                n_pairs += n
+                # kept[j]: key j of the row's list stays in the numerator
+                kept = ~np.repeat(skip, blk)
                 m = s.max(axis=1, keepdims=True)
                 empty = m[:, 0] == NEG_INF
                 m = np.where(empty[:, None], 0.0, m)
                 e = np.exp(s - m)
                 l = e.sum(axis=1, keepdims=True)
                 l_safe = np.where(empty[:, None], 1.0, l)
-                num = (e * kept.reshape(blk, n * blk)) @ v[ib, hk, idx]
+                num = (e * kept[None, :]) @ v[ib, hk, idx]
                 o[ib, ih, rows] = np.where(empty[:, None], 0.0, num / l_safe)[:nr]
                 lse[ib, ih, rows] = np.where(empty, NEG_INF, (m + np.log(l_safe))[:, 0])[:nr]
     out = (o, lse)
     if return_skips:
-        out += (n_skip, n_units)
+        out += (n_skip, n_pairs)
     if return_margins:
         out += (near,)
     return out

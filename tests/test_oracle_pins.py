@@ -329,6 +329,28 @@ def test_gqa_head_mapping():
         assert np.allclose(o2[0, i], i // 4, atol=1e-13)
 
 
+@pytest.mark.parametrize("ratio", [1, 2, 4])
+def test_dense_attention_is_sdpa_on_expanded_kv_heads(ratio):
+    # aiter 6841 page: query head j reads KV head j // ratio.  Every KV head
+    # holds different keys and values, so a wrong head map (j % h_kv, or no
+    # map) gives a different result; torch's SDPA over K/V with each head
+    # repeated for its query heads is the independent routine.
+    rng = np.random.default_rng(30 + ratio)
+    b, hkv, s_q, s_k, d = 2, 3, 70, 130, 16
+    q = rng.standard_normal((b, hkv * ratio, s_q, d))
+    k = rng.standard_normal((b, hkv, s_k, d))
+    v = rng.standard_normal((b, hkv, s_k, d))
+    o, lse = oracle.dense_attention(q, k, v)
+    kk = np.repeat(k, ratio, axis=1)
+    vv = np.repeat(v, ratio, axis=1)
+    ro, rl = _sdpa(q, kk, vv, 1 / math.sqrt(d))
+    assert np.abs(o - ro).max() < 1e-12
+    assert np.abs(lse - rl).max() < 1e-12
+    o2, l2 = oracle.dense_attention(q, k, v, scale=0.3)
+    ro2, rl2 = _sdpa(q, kk, vv, 0.3)
+    assert np.abs(o2 - ro2).max() < 1e-12 and np.abs(l2 - rl2).max() < 1e-12
+
+
 def test_token_lists_skip_minus_one_and_match_sdpa():
     rng = np.random.default_rng(12)
     b, hq, hkv, s, d = 2, 4, 2, 300, 16

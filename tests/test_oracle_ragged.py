@@ -169,16 +169,19 @@ def test_int8_partial_block_scale_is_its_own():
 def test_pv_skip_ragged_reduces_to_exact_and_keeps_lse():
     s_q, s_k = 100, 170
     q, k, v = _rand((1, 2, s_q, 16), 14, 2.0), _rand((1, 2, s_k, 16), 15), _rand((1, 2, s_k, 16), 16)
+    # K block t scaled by 4^-t: later blocks, the partial one of 42 keys
+    # included, fall below the running maximum of every row of a tile.
+    k = k * (4.0 ** -(np.arange(s_k) // 64))[None, None, :, None]
     ro, rl = _sdpa(q, k, v)
     # A threshold nothing falls below: exact attention, no unit skipped.
-    o, lse, n_skip, _ = oracle.block_sparse_attention_pv_skip(q, k, v, None, None, 1e9, q_unit=32,
-                                                              k_unit=32, return_skips=True)
+    o, lse, n_skip, _ = oracle.block_sparse_attention_pv_skip(q, k, v, None, None, 1e9,
+                                                              return_skips=True)
     assert n_skip == 0
     np.testing.assert_allclose(o, ro, atol=1e-12, rtol=1e-12)
     np.testing.assert_allclose(lse, rl, atol=1e-12)
     # A small one: the LSE stays exact and O moves within the skip bound.
-    o, lse, n_skip, _ = oracle.block_sparse_attention_pv_skip(q, k, v, None, None, 1.0, q_unit=32,
-                                                              k_unit=32, return_skips=True)
+    o, lse, n_skip, _ = oracle.block_sparse_attention_pv_skip(q, k, v, None, None, 1.0,
+                                                              return_skips=True)
     assert n_skip > 0
     np.testing.assert_allclose(lse, rl, atol=1e-12)
     bound = s_k * math.exp(-1.0) * np.abs(v).max()

@@ -237,6 +237,11 @@ sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void*
     return fail(SPARGE_ERR_INVALID, "pv_threshold must be finite and >= 0");
   if (pv_threshold > 0.f && token_mode)
     return fail(SPARGE_ERR_UNSUPPORTED, "pv_threshold applies to block mode only");
+  // The skip test compares each block with the maximum over the blocks of
+  // the row visited before it; a split would start without that maximum.
+  if (pv_threshold > 0.f && num_splits > 1)
+    return fail(SPARGE_ERR_UNSUPPORTED, "pv_threshold decides over a row's whole list in one pass: "
+                "it needs num_splits = 1 (got %d)", num_splits);
   if (causal && token_mode) return fail(SPARGE_ERR_INVALID, "causal masking applies to block mode only");
   if (causal && s_q != s_k)
     return fail(SPARGE_ERR_UNSUPPORTED, "causal attention needs s_q = s_k (got %d, %d)", s_q, s_k);

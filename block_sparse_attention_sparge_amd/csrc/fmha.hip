@@ -24,10 +24,12 @@
 //   * the two key halves of a tile are merged at the end with the LSE rule,
 //     and the finished tile leaves through LDS as whole rows;
 //   * with a pv_threshold (CK page, "Status vs Upstream": a per-Q-tile skip
-//     in the attention kernel), a wavefront drops the PV product of a block
-//     when each of its 32 query rows scores, over the wavefront's 32 keys,
-//     more than the threshold below that row's running maximum over the keys
-//     of its half seen so far in the pass; those P still count in the row sum;
+//     in the attention kernel), the workgroup drops the PV product of a whole
+//     listed block when every one of the tile's 64 query rows scores, over
+//     the block's 64 keys, more than the threshold below that row's running
+//     maximum over the blocks already visited; the four wavefronts pool
+//     their row maxima in LDS and all take the same decision, and a dropped
+//     block reads no V^T either; its P still count in the row sum;
 //   * workgroups are renumbered so that consecutive rows of one head land on
 //     one XCD and share its L2 (aiter 4919 page: workgroups round-robin over
 //     the 8 XCDs by linear id); causal rows are taken last tile first.
@@ -97,6 +99,9 @@ void fmha_block_kernel(FmhaArgs a) {
   __shared__ __attribute__((aligned(16))) T sK[2 * TILE];
   __shared__ __attribute__((aligned(16))) T sV[2 * TILE];
   __shared__ float s_ml[128];                // (m, l) of the kh = 1 waves, per query half
+  // pv_threshold vote: (block maximum, running maximum) of each wave's 32
+  // query rows over its 32 keys, scaled base-2 units.
+  __shared__ float2v s_vote[PVSKIP ? 128 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -288,14 +293,15 @@ void fmha_block_kernel(FmhaArgs a) {
         }
       }
     };
-    read_vt(0);
+    // (With a pv_threshold the V^T reads wait for the tile's decision.)
+    if constexpr (!PVSKIP) read_vt(0);
     __builtin_amdgcn_sched_barrier(0);
 
     // S^T (32 keys x 32 queries) = K Q^T.
     floatx16 s = floatx16{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) s = mfma32<E>(kf[kk], qf[kk], s);
-    read_vt(1);
+    if constexpr (!PVSKIP) read_vt(1);
     __builtin_amdgcn_sched_barrier(0);
     // The other buffer held block it-1, released by the last barrier.
     if (it + 1 < nloc) issue_block(kb_ahead, 1 - cur);
@@ -322,7 +328,6 @@ void fmha_block_kernel(FmhaArgs a) {
     for (int r = 1; r < 16; ++r) rmax = fmaxf(rmax, s[r]);
     rmax = half_swap_max(rmax);
     const float m_cand = rmax * c2;
-    if constexpr (PVSKIP) m_top = fmaxf(m_top, m_cand);
     const bool need = m_cand > m_run + kRescaleSlack;
     if (__any(need)) {
       const float m_new = need ? m_cand : m_run;
@@ -338,8 +343,8 @@ void fmha_block_kernel(FmhaArgs a) {
     // carried by one key would move the LSE by up to 4e-3 nats.
     // Masked rows may still have no key (m_run = -inf): their P is 0.
     //
-    // O^T += V^T P^T over this wave's 32 keys, unless every query row of the
-    // wave lies more than the threshold below its running maximum.  The four
+    // O^T += V^T P^T over this wave's 32 keys, unless the tile skips the
+    // block (pv_threshold).  The four
     // PV MFMAs of k-step 0 are issued as soon as its 8 P values exist, so the
     // exponentials of k-step 1 run in their shadow.  From the first PV MFMA to
     // the last the wave runs at raised priority: of the two wavefronts sharing
@@ -350,7 +355,25 @@ void fmha_block_kernel(FmhaArgs a) {
     // well gains nothing).
     const float mref = MASKED && m_run == -INFINITY ? 0.f : m_run;
     bool pv = true;
-    if constexpr (PVSKIP) pv = __any(!(m_cand < m_top - a.pv_tau2));
+    if constexpr (PVSKIP) {
+      // Query row i of the tile (lane i of each wave after the exchange):
+      // r_i = its maximum over the block's 64 keys, M_i = its running
+      // maximum over the blocks visited so far, this one included.  The
+      // block is dropped when r_i < M_i - tau for all 64 rows; every wave
+      // reads the same values and takes the same decision.  The vote slots
+      // are rewritten only after the barrier that ends this step.
+      m_top = fmaxf(m_top, m_cand);
+      if (hl == 0) s_vote[wave * 32 + l32] = float2v{m_cand, m_top};
+      __syncthreads();
+      const int vq = lane >> 5, vr = lane & 31;
+      const float2v h0 = s_vote[vq * 32 + vr], h1 = s_vote[(2 + vq) * 32 + vr];
+      const float r_i = fmaxf(h0[0], h1[0]), m_i = fmaxf(h0[1], h1[1]);
+      pv = __any(!(r_i < m_i - a.pv_tau2));
+      if (pv) {
+        read_vt(0);
+        read_vt(1);
+      }
+    }
     u32x4 pf[2];
     float p[16];
 #pragma unroll

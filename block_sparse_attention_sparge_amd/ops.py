@@ -166,6 +166,28 @@ def _check_lut_rows(lut, count, b, nq):
         raise SpargeError(SPARGE_ERR_INVALID, f"count must be {tuple(lut.shape[:3])} (got {tuple(count.shape)})")
 
 
+def _check_attn_shapes(q, k, v, o, lse, num_splits):
+    """q [b, h_q, s_q, d]; k, v [b, h_kv, s_k, d]; o [(S,) b, h_q, s_q, d] and lse
+    [(S,) b, h_q, s_q] contiguous fp32, the split axis S present when num_splits
+    > 1.  The C ABI takes a single b, s_k and d for all of them, so any other
+    shape would send the kernels past the end of a buffer."""
+    b, h_q, s_q, d = q.shape
+    if k.dim() != 4 or v.dim() != 4:
+        raise SpargeError(SPARGE_ERR_INVALID, "k and v must be [b, h_kv, s_k, d]")
+    if k.shape[0] != b or k.shape[3] != d:
+        raise SpargeError(SPARGE_ERR_INVALID, f"k {tuple(k.shape)} does not match q {tuple(q.shape)} in b or d")
+    if tuple(v.shape) != tuple(k.shape):
+        raise SpargeError(SPARGE_ERR_INVALID, f"v {tuple(v.shape)} must have the shape of k {tuple(k.shape)}")
+    lead = () if num_splits == 1 else (int(num_splits),)
+    if o is not None and tuple(o.shape) != lead + (b, h_q, s_q, d):
+        raise SpargeError(SPARGE_ERR_INVALID, f"o must be {lead + (b, h_q, s_q, d)} (got {tuple(o.shape)})")
+    if lse is not None:
+        if tuple(lse.shape) != lead + (b, h_q, s_q):
+            raise SpargeError(SPARGE_ERR_INVALID, f"lse must be {lead + (b, h_q, s_q)} (got {tuple(lse.shape)})")
+        if lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise SpargeError(SPARGE_ERR_INVALID, "lse must be contiguous float32")
+
+
 def block_map_workspace_bytes(b: int, h: int, s_q: int, s_k: int, d: int, blk_q: int = 64,
                               blk_k: int = 64) -> int:
     return int(load_library().sparge_build_block_map_workspace(b, h, s_q, s_k, d, blk_q, blk_k))
@@ -264,23 +286,27 @@ def sparse_fmha_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     With num_splits > 1 the outputs are partials o [S, b, h_q, s_q, d] and
     lse [S, b, h_q, s_q] (fp32 unless out_dtype says otherwise).  causal sets
     SPARGE_FLAG_CAUSAL (block mode, s_q = s_k).  pv_threshold > 0 lets the
-    kernel skip the P.V product of 32x32 units scoring more than that far
-    below their running maximum (block mode).  Returns (o, lse).
+    kernel skip the P.V product of a listed block for a whole Q-tile when
+    every row of the tile scores more than that far below its running
+    maximum (block mode, num_splits = 1).  Returns (o, lse).
     """
     lib = load_library()
     dev = _on_gpu(q, k, v, lut, count, o, lse)
+    if q.dim() != 4:
+        raise SpargeError(SPARGE_ERR_INVALID, f"q must be [b, h_q, s_q, d], got {tuple(q.shape)}")
     b, h_q, s_q, d = q.shape
     h_kv, s_k = k.shape[1], k.shape[2]
     if not (q.dtype == k.dtype == v.dtype):
         raise SpargeError(SPARGE_ERR_INVALID, "q, k, v dtypes disagree")
+    _check_attn_shapes(q, k, v, o, lse, num_splits)
     if out_dtype is None:
         out_dtype = q.dtype if num_splits == 1 else torch.float32
     split_stride = 0
     if o is None:
         if num_splits == 1:
-            o = torch.empty((b, h_q, s_q, v.shape[3]), dtype=out_dtype, device=dev)
+            o = torch.empty((b, h_q, s_q, d), dtype=out_dtype, device=dev)
         else:
-            o = torch.empty((num_splits, b, h_q, s_q, v.shape[3]), dtype=out_dtype, device=dev)
+            o = torch.empty((num_splits, b, h_q, s_q, d), dtype=out_dtype, device=dev)
     o4 = o if o.dim() == 4 else o[0]
     if num_splits > 1:
         split_stride = o.stride(0)
@@ -297,6 +323,8 @@ def sparse_fmha_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise SpargeError(SPARGE_ERR_INVALID, "count must be contiguous int32")
     if blk_q == 64 and lut is not None:
         _check_lut_rows(lut, count, b, -(-s_q // 64))
+    if blk_q == 1 and lut is not None and (lut.dim() != 3 or tuple(lut.shape[:2]) != (b, h_kv)):
+        raise SpargeError(SPARGE_ERR_INVALID, f"token lists must be [b={b}, h_kv={h_kv}, L] (got {tuple(lut.shape)})")
     st = lib.sparse_fmha_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dt(q.dtype), _dt(o.dtype),
         b, h_q, h_kv, s_q, s_k, d, _strides(q), _strides(k), _strides(v), _strides(o4),
@@ -323,10 +351,13 @@ def sparse_fmha_fwd_qk_int8(q_i8: torch.Tensor, q_scale: torch.Tensor, k_i8: tor
     """
     lib = load_library()
     dev = _on_gpu(q_i8, q_scale, k_i8, k_scale, v, lut, count, o, lse)
+    if q_i8.dim() != 4:
+        raise SpargeError(SPARGE_ERR_INVALID, f"q_i8 must be [b, h_q, s_q, d], got {tuple(q_i8.shape)}")
     b, h_q, s_q, d = q_i8.shape
     h_kv, s_k = k_i8.shape[1], k_i8.shape[2]
     if q_i8.dtype != torch.int8 or k_i8.dtype != torch.int8:
         raise SpargeError(SPARGE_ERR_INVALID, "q_i8 and k_i8 must be int8")
+    _check_attn_shapes(q_i8, k_i8, v, o, lse, num_splits)
     for name, t, shape in (("q_scale", q_scale, (b, h_q, -(-s_q // 64))), ("k_scale", k_scale, (b, h_kv, -(-s_k // 64)))):
         if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shape:
             raise SpargeError(SPARGE_ERR_INVALID, f"{name} must be contiguous float32 {shape}")
@@ -334,7 +365,7 @@ def sparse_fmha_fwd_qk_int8(q_i8: torch.Tensor, q_scale: torch.Tensor, k_i8: tor
         out_dtype = v.dtype if num_splits == 1 else torch.float32
     split_stride = 0
     if o is None:
-        shape = (b, h_q, s_q, v.shape[3]) if num_splits == 1 else (num_splits, b, h_q, s_q, v.shape[3])
+        shape = (b, h_q, s_q, d) if num_splits == 1 else (num_splits, b, h_q, s_q, d)
         o = torch.empty(shape, dtype=out_dtype, device=dev)
     o4 = o if o.dim() == 4 else o[0]
     if num_splits > 1:
@@ -381,6 +412,11 @@ def attn_combine(o_parts: torch.Tensor, lse_parts: torch.Tensor,
     part_stride = o_parts.stride(0) if n > 1 else b * h * s * d
     if out_dtype is None:
         out_dtype = o_parts.dtype
+    if o is not None and (tuple(o.shape) != (b, h, s, d) or not o.is_contiguous()):
+        raise SpargeError(SPARGE_ERR_INVALID, f"o must be contiguous {(b, h, s, d)} (got {tuple(o.shape)})")
+    if lse is not None and (tuple(lse.shape) != (b, h, s) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise SpargeError(SPARGE_ERR_INVALID, f"lse must be contiguous float32 {(b, h, s)}")
     if o is None:
         o = torch.empty((b, h, s, d), dtype=out_dtype, device=dev)
     if lse is None and return_lse:

@@ -204,16 +204,18 @@ size_t sparge_build_block_map_workspace(int b, int h, int s_q, int s_k, int d,
  *
  * pv_threshold (block mode; CK page, "Status vs Upstream": pv_threshold, a
  * per-Q-tile skip in the attention kernel): 0 = off.  A value tau > 0 drops
- * P.V products that cannot matter much.  Each chunk's blocks are visited in
- * list order; a block pair is cut into four units of 32 query rows x 32 keys
- * (keys 64 kb + [0, 32) and 64 kb + [32, 64)); for each unit and each of its
- * rows i, M_i is the running maximum of s over that key half of the blocks
- * visited so far in the chunk, this one included, and r_i the maximum of s
- * over the unit's keys (-inf where masked).  The unit's P.V product is
- * skipped when r_i < M_i - tau for all 32 rows.  Skipped keys still count in
- * the softmax denominator and in LSE: LSE is the exact one, and O_i moves by
- * at most (skipped keys of row i) * exp(-tau) * max |v|.  The decision is
- * taken in fp32.  tau must be finite and >= 0; token-list mode takes 0 only.
+ * P.V products that cannot matter much.  The unit is one Q-tile (64 query
+ * rows, fewer in a partial last tile) against one listed block (64 keys).
+ * The row's blocks are visited in list order; for each block and each query
+ * row i of the tile, r_i is the maximum of s over the block's keys (-inf
+ * where masked) and M_i the running maximum of s over the blocks visited so
+ * far, this one included.  The block's P.V product is skipped for the whole
+ * tile when r_i < M_i - tau for every row i.  Skipped keys still count in the
+ * softmax denominator and in LSE: LSE is the exact one, and O_i moves by at
+ * most (skipped keys of row i) * exp(-tau) * max |v|.  The decision is taken
+ * in fp32.  tau must be finite and >= 0; token-list mode takes 0 only, and a
+ * tau > 0 needs num_splits = 1 (SPARGE_ERR_UNSUPPORTED otherwise: a split
+ * would not know the maximum of the blocks before it).
  */
 sparge_status sparse_fmha_fwd(
     const void* q, const void* k, const void* v, void* o, float* lse,

@@ -169,6 +169,7 @@ def _fmha(lib, **kw):
     (dict(pv=float("inf")), ops.SPARGE_ERR_INVALID),
     (dict(pv=float("nan")), ops.SPARGE_ERR_INVALID),
     (dict(pv=4.0, bq=1, bk=1, cnt=None, lh=2), ops.SPARGE_ERR_UNSUPPORTED),   # token mode
+    (dict(pv=4.0, splits=2, sst=8 * 512 * 128), ops.SPARGE_ERR_UNSUPPORTED),   # one pass per row
     # token-list mode
     (dict(bq=1, bk=1, lut=None, cnt=None), ops.SPARGE_ERR_INVALID),
     (dict(bq=1, bk=1, cnt=FAKE, lh=2), ops.SPARGE_ERR_INVALID),
@@ -255,6 +256,41 @@ def test_python_binding_rejects_cpu_tensors(lib):
         ops.sparse_fmha_fwd(q, q, q)
     with pytest.raises(ops.SpargeError):
         ops.build_block_map(q, q, [0.5], [0.001])
+
+
+def _meta(*shape, dtype=torch.float16):
+    return torch.empty(shape, dtype=dtype, device="meta")
+
+
+@pytest.mark.parametrize("case", [
+    dict(k=_meta(2, 2, 256, 64)),                       # k batch differs from q
+    dict(k=_meta(1, 2, 256, 128), v=_meta(1, 2, 256, 128)),   # k head dim differs
+    dict(v=_meta(1, 2, 200, 64)),                       # v shorter than k
+    dict(v=_meta(1, 4, 256, 64)),                       # v heads differ from k
+    dict(v=_meta(1, 2, 256, 128)),                      # v head dim differs
+    dict(o=_meta(1, 4, 128, 64)),                       # o too short
+    dict(o=_meta(1, 4, 256, 64), splits=2),             # split partials need [S, ...]
+    dict(o=_meta(3, 1, 4, 256, 64), splits=2),          # wrong split count
+    dict(lse=_meta(1, 4, 255, dtype=torch.float32)),    # lse too short
+    dict(lse=_meta(1, 4, 256, dtype=torch.float16)),    # lse not fp32
+    dict(lse=_meta(1, 4, 256, dtype=torch.float32), splits=2),
+    dict(lse=_meta(256, 4, dtype=torch.float32).t()[None]),   # not contiguous
+])
+def test_binding_rejects_mismatched_attention_shapes(case):
+    # q [1, 4, 256, 64]; k, v [1, 2, 256, 64].  The C ABI takes one b, s_k and
+    # d for all tensors, so the binding must refuse anything else before a
+    # launch could read or write past a buffer.
+    a = dict(k=_meta(1, 2, 256, 64), v=_meta(1, 2, 256, 64), o=None, lse=None, splits=1)
+    a.update(case)
+    with pytest.raises(ops.SpargeError):
+        ops._check_attn_shapes(_meta(1, 4, 256, 64), a["k"], a["v"], a["o"], a["lse"], a["splits"])
+
+
+def test_binding_accepts_matching_attention_shapes():
+    q, k = _meta(1, 4, 256, 64), _meta(1, 2, 256, 64)
+    ops._check_attn_shapes(q, k, k, _meta(1, 4, 256, 64), _meta(1, 4, 256, dtype=torch.float32), 1)
+    ops._check_attn_shapes(q, k, k, _meta(3, 1, 4, 256, 64, dtype=torch.float32),
+                           _meta(3, 1, 4, 256, dtype=torch.float32), 3)
 
 
 def test_missing_library_fails_loudly(tmp_path):

@@ -1,14 +1,15 @@
 """GPU parity for the pv_threshold skip in the block-mode FMHA.
 
 CK page, "Status vs Upstream", not-yet-ported list: pv_threshold, a per-Q-tile
-skip inside the attention kernel.  The kernel takes the decision per 32-query x
-32-key unit against that key half's running maximum within the chunk (the
-oracle's q_unit = k_unit = 32).  Its output is compared with the oracle's
-skip rule at the bars of the other attention tests (O atol 4e-2 / rtol 1e-2,
-LSE 2e-3 nats).  Row groups with a unit whose decision lies within 1e-3 nats
-of the threshold are left out: there fp32 and fp64 scores may decide
-differently.  Each case also checks that the skips it exercises move O by
-more than the tolerance, so a kernel that never skipped would fail.
+skip inside the attention kernel.  The kernel takes one decision per (Q-tile,
+listed block), from all 64 query rows of the tile against their running
+maxima over the row's whole list, as the oracle's rule does.  Its output is
+compared with the oracle's skip rule at the bars of the other attention tests
+(O atol 4e-2 / rtol 1e-2, LSE 2e-3 nats).  Q-tiles with a block whose
+decision lies within 1e-3 nats of the threshold are left out: there fp32 and
+fp64 scores may decide differently.  Each case also checks that the skips it
+exercises move O by more than the tolerance, so a kernel that never skipped
+would fail.
 """
 import math
 
@@ -37,16 +38,15 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _compare(o_gpu, lse_gpu, q, k, v, lut, cnt, tau, splits=1, causal=False, per_kv=False,
-             sensitive=True):
+def _compare(o_gpu, lse_gpu, q, k, v, lut, cnt, tau, causal=False, per_kv=False, sensitive=True):
     qn, kn, vn = np64(q), np64(k), np64(v)
     lut_n = None if lut is None else lut.cpu().numpy()
     cnt_n = None if cnt is None else cnt.cpu().numpy()
     ro, rl, ns, nu, near = oracle.block_sparse_attention_pv_skip(
-        qn, kn, vn, lut_n, cnt_n, tau, q_unit=32, k_unit=32, num_splits=splits,
-        lut_per_kv_head=per_kv, causal=causal, return_skips=True, return_margins=True)
+        qn, kn, vn, lut_n, cnt_n, tau, lut_per_kv_head=per_kv, causal=causal, return_skips=True,
+        return_margins=True)
     assert 0 < ns < nu, (ns, nu)
-    keep = np.repeat(near >= NEAR, 32, axis=-1).reshape(ro.shape[:3])     # [b, h, s_q]
+    keep = np.repeat(near >= NEAR, 64, axis=-1)[..., :ro.shape[2]]    # [b, h, s_q]
     assert keep.mean() > 0.8
     og, lg = np64(o_gpu), np64(lse_gpu)
     err = np.abs(og - ro)[keep]
@@ -65,7 +65,7 @@ def _compare(o_gpu, lse_gpu, q, k, v, lut, cnt, tau, splits=1, causal=False, per
 
 def _decaying(dev, b, h, s, d, dtype, seed, rate=0.5):
     """K block t scaled by 2^(-rate t): later blocks score lower, so many of
-    their units fall below the running maximum."""
+    them fall below the running maximum of every row of a tile."""
     g = torch.Generator(device=dev).manual_seed(seed)
     q = (4.0 * torch.randn(b, h, s, d, generator=g, device=dev)).to(dtype)
     scale = torch.pow(2.0, -rate * (torch.arange(s, device=dev) // 64).float())
@@ -84,13 +84,12 @@ def test_pv_skip_dense_decaying_keys(dev, dtype, d, causal, tau):
     _compare(o, lse, q, k, v, None, None, tau, causal=causal)
 
 
-@pytest.mark.parametrize("splits", [2, 3])
-def test_pv_skip_with_splits_then_combine(dev, splits):
-    q, k, v = _decaying(dev, 1, 2, 1024, 128, torch.float16, 7)
-    op, lp = ops.sparse_fmha_fwd(q, k, v, None, None, num_splits=splits, pv_threshold=2.0)
-    o, lse = ops.attn_combine(op, lp, out_dtype=q.dtype)
-    torch.cuda.synchronize()
-    _compare(o, lse, q, k, v, None, None, 2.0, splits=splits)
+def test_pv_skip_takes_one_pass_per_row(dev):
+    # The rule compares each block with the maximum over the blocks before it
+    # in the row, so a split of the row is refused on the host.
+    q, k, v = _decaying(dev, 1, 2, 256, 128, torch.float16, 7)
+    with pytest.raises(ops.SpargeError):
+        ops.sparse_fmha_fwd(q, k, v, None, None, num_splits=2, pv_threshold=2.0)
 
 
 @pytest.mark.parametrize("tau", [0.25, 0.5])
@@ -126,15 +125,17 @@ def test_pv_threshold_zero_is_the_plain_kernel(dev):
     assert torch.equal(o0, o2) and torch.equal(l0, l2)
 
 
-def test_pv_skip_headline_sampled_heads(dev):
-    # Headline workload at topk 0.4 and tau 4: the flattest (h 0) and most
-    # peaked (h 31) heads of both batches against the oracle.
+@pytest.mark.parametrize("tau", [2.0, 4.0])
+def test_pv_skip_headline_sampled_heads(dev, tau):
+    # Headline workload at topk 0.4: the flattest (h 0, nothing dropped) and
+    # most peaked (h 31, 43% of its pairs dropped at tau 4 and 67% at tau 2)
+    # heads of both batches against the oracle.
     case = synth.headline_case(dev, topk=0.4)
     bm = ops.build_block_map(case.q, case.k, case.topk, case.simthreshd1)
-    o, lse = ops.sparse_fmha_fwd(case.q, case.k, case.v, bm["lut"], bm["count"], pv_threshold=4.0)
+    o, lse = ops.sparse_fmha_fwd(case.q, case.k, case.v, bm["lut"], bm["count"], pv_threshold=tau)
     torch.cuda.synchronize()
     heads = [0, 31]
     frac = _compare(o[:, heads], lse[:, heads], case.q[:, heads], case.k[:, heads],
-                    case.v[:, heads], bm["lut"][:, heads], bm["count"][:, heads], 4.0,
+                    case.v[:, heads], bm["lut"][:, heads], bm["count"][:, heads], tau,
                     sensitive=False)
-    print(f"headline tau 4: {frac:.3f} of the 32x32 units of heads 0 and 31 skipped")
+    print(f"headline tau {tau}: {frac:.3f} of the (tile, block) pairs of heads 0 and 31 dropped")

@@ -219,8 +219,9 @@ def test_fmha_empty_rows_and_no_write_past_the_end(dev):
 
 @pytest.mark.parametrize("tau", [0.5, 1.5])
 def test_pv_threshold(dev, tau):
-    # Keys that decay block by block, so many 32 x 32 units fall below the
-    # running maximum; a partial Q-tile of 40 rows and a partial K block of 44.
+    # Keys that decay block by block, so many blocks fall below the running
+    # maximum of every row of a tile; a partial Q-tile of 40 rows and a
+    # partial K block of 44.
     b, h, s_q, s_k, d = 1, 2, 424, 940, 128
     g = torch.Generator(device=dev).manual_seed(41)
     q = (4.0 * torch.randn(b, h, s_q, d, generator=g, device=dev)).half()
@@ -230,10 +231,9 @@ def test_pv_threshold(dev, tau):
     o, lse = ops.sparse_fmha_fwd(q, k, v, None, None, pv_threshold=tau)
     torch.cuda.synchronize()
     ro, rl, ns, nu, near = oracle.block_sparse_attention_pv_skip(
-        np64(q), np64(k), np64(v), None, None, tau, q_unit=32, k_unit=32, return_skips=True,
-        return_margins=True)
+        np64(q), np64(k), np64(v), None, None, tau, return_skips=True, return_margins=True)
     assert 0 < ns < nu
-    keep = np.repeat(near >= 1e-3, 32, axis=-1).reshape(b, h, -1)[:, :, :s_q]
+    keep = np.repeat(near >= 1e-3, 64, axis=-1)[:, :, :s_q]
     assert keep.mean() > 0.8
     check_o(o, ro, keep=np.broadcast_to(keep[..., None], ro.shape))
     check_lse(lse, rl)

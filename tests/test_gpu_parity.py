@@ -572,10 +572,13 @@ def test_headline_full_size(dev, topk):
     assert np.array_equal(res["lut"].cpu().numpy(), lut)
     assert np.array_equal(res["count"].cpu().numpy(), cnt)
     assert np.array_equal(res["bitmap"].cpu().numpy(), bm)
-    # sampled heads: pooled stage and attention against the oracle
-    heads = [0, 10, 21, 31]
+    # sampled heads: pooled stage and attention against the oracle.  With the
+    # mixed per-head topk (head h takes {0.1, 0.2, 0.4, 0.6, 0.8}[h mod 5])
+    # the sample covers every topk value: 0.1 (0, 10), 0.2 (21, 31), 0.4 (2),
+    # 0.6 (3, 28) and 0.8 (4, 29); the flattest and most peaked heads too.
+    heads = [0, 2, 3, 4, 10, 21, 28, 29, 31] if topk == "mixed" else [0, 10, 21, 31]
     qn, kn, vn = np64(case.q[:, heads]), np64(case.k[:, heads]), np64(case.v[:, heads])
-    ref = oracle.block_map(qn, kn, topk=[case.topk[h] for h in heads], simthreshd1=[0.001] * 4)
+    ref = oracle.block_map(qn, kn, topk=[case.topk[h] for h in heads], simthreshd1=[0.001] * len(heads))
     assert (np.abs(gp[:, heads] - ref["prob"]) <= 1e-3 * np.abs(ref["prob"]) + 1e-7).all()
     ro, rl = oracle.block_sparse_attention(qn, kn, vn, res["lut"][:, heads].cpu().numpy(),
                                            res["count"][:, heads].cpu().numpy())

@@ -8,6 +8,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include <algorithm>
@@ -79,11 +80,41 @@ BlockMapLayout block_map_layout(int b, int h, int s_q, int s_k, int d) {
   return l;
 }
 
+// Device scratch of sparge_build_block_map_noalloc: one copy per GPU, held
+// until the process ends.  In host code `scratch` is only a host-side handle;
+// its device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[SPARGE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of this device's scratch array (looked up on the first call made
+// with that device current; no allocation).
+sparge_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SPARGE_ERR_UNSUPPORTED, "device %d is beyond the %d devices the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(SPARGE_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPARGE_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int sparge_abi_version(void) { return 5; }
+int sparge_abi_version(void) { return 6; }
 
 const char* sparge_last_error(void) { return g_error.c_str(); }
 
@@ -93,13 +124,20 @@ size_t sparge_build_block_map_workspace(int b, int h, int s_q, int s_k, int d, i
   return block_map_layout(b, h, s_q, s_k, d).total;
 }
 
-sparge_status sparge_build_block_map(
+}  // extern "C"
+
+namespace {
+
+// Both block-map entry points.  With use_scratch the workspace arguments are
+// ignored and, once every argument has passed the host checks, this device's
+// scratch array serves as the workspace.
+sparge_status block_map_impl(
     const void* q, const void* k, sparge_dtype dt, int b, int h, int h_kv, int s_q, int s_k, int d,
     const int64_t q_strides[3], const int64_t k_strides[3], int blk_q, int blk_k,
     const float* topk, const float* cdfthreshd, const float* simthreshd1, float softmax_scale,
     unsigned flags, int32_t* lut, int32_t* lut_count, uint8_t* block_map, float* pooled_prob, uint8_t* sim_q,
     uint8_t* sim_k, float* q_mean, float* k_mean, int8_t* q_i8, float* q_i8_scale, int8_t* k_i8,
-    float* k_i8_scale, void* workspace, size_t workspace_bytes, void* stream) {
+    float* k_i8_scale, void* workspace, size_t workspace_bytes, bool use_scratch, void* stream) {
   if (!q || !k) return fail(SPARGE_ERR_INVALID, "q and k must be non-null");
   if (!lut || !lut_count) return fail(SPARGE_ERR_INVALID, "lut and lut_count must be non-null");
   if (!topk || !simthreshd1) return fail(SPARGE_ERR_INVALID, "topk and simthreshd1 must be non-null");
@@ -127,9 +165,17 @@ sparge_status sparge_build_block_map(
   if (causal && s_q != s_k)
     return fail(SPARGE_ERR_UNSUPPORTED, "causal block map needs s_q = s_k (got %d, %d)", s_q, s_k);
   const BlockMapLayout lay = block_map_layout(b, h, s_q, s_k, d);
-  if (!workspace || workspace_bytes < lay.total)
-    return fail(SPARGE_ERR_INVALID, "workspace of %zu bytes needed (got %zu)", lay.total, workspace_bytes);
-  if (((uintptr_t)workspace & 255u) != 0) return fail(SPARGE_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (use_scratch) {
+    if (lay.total > (size_t)SPARGE_NOALLOC_SCRATCH_BYTES)
+      return fail(SPARGE_ERR_UNSUPPORTED,
+                  "these sizes need %zu bytes of scratch; the allocation-free entry point holds %zu "
+                  "(use sparge_build_block_map with a workspace)",
+                  lay.total, (size_t)SPARGE_NOALLOC_SCRATCH_BYTES);
+  } else {
+    if (!workspace || workspace_bytes < lay.total)
+      return fail(SPARGE_ERR_INVALID, "workspace of %zu bytes needed (got %zu)", lay.total, workspace_bytes);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(SPARGE_ERR_INVALID, "workspace must be 256-byte aligned");
+  }
   if ((q_mean && ((uintptr_t)q_mean & 15u)) || (k_mean && ((uintptr_t)k_mean & 15u)))
     return fail(SPARGE_ERR_INVALID, "q_mean/k_mean must be 16-byte aligned");
   const int n_i8 = (q_i8 != nullptr) + (q_i8_scale != nullptr) + (k_i8 != nullptr) + (k_i8_scale != nullptr);
@@ -162,6 +208,11 @@ sparge_status sparge_build_block_map(
     }
   }
   for (int i = h; i < SPARGE_MAX_HEADS; ++i) { pa.thr[i] = 0.f; sa.thr[i] = 0.f; sa.nsel[i] = 1; sa.cdf[i] = 0.f; }
+  if (use_scratch) {
+    // Every argument is valid: only now touch the device.
+    const sparge_status sst = scratch_for_current_device(&workspace);
+    if (sst != SPARGE_OK) return sst;
+  }
 
   char* ws = reinterpret_cast<char*>(workspace);
   pa.q = q;
@@ -196,6 +247,35 @@ sparge_status sparge_build_block_map(
   if (e != hipSuccess) return hip_status(e, "pool_sim launch");
   e = launch_score_select(sa, d, s);
   return hip_status(e, "score_select launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+sparge_status sparge_build_block_map(
+    const void* q, const void* k, sparge_dtype dt, int b, int h, int h_kv, int s_q, int s_k, int d,
+    const int64_t q_strides[3], const int64_t k_strides[3], int blk_q, int blk_k,
+    const float* topk, const float* cdfthreshd, const float* simthreshd1, float softmax_scale,
+    unsigned flags, int32_t* lut, int32_t* lut_count, uint8_t* block_map, float* pooled_prob, uint8_t* sim_q,
+    uint8_t* sim_k, float* q_mean, float* k_mean, int8_t* q_i8, float* q_i8_scale, int8_t* k_i8,
+    float* k_i8_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return block_map_impl(q, k, dt, b, h, h_kv, s_q, s_k, d, q_strides, k_strides, blk_q, blk_k, topk, cdfthreshd,
+                        simthreshd1, softmax_scale, flags, lut, lut_count, block_map, pooled_prob, sim_q, sim_k,
+                        q_mean, k_mean, q_i8, q_i8_scale, k_i8, k_i8_scale, workspace, workspace_bytes, false,
+                        stream);
+}
+
+sparge_status sparge_build_block_map_noalloc(
+    const void* q, const void* k, sparge_dtype dt, int b, int h, int h_kv, int s_q, int s_k, int d,
+    const int64_t q_strides[3], const int64_t k_strides[3], int blk_q, int blk_k,
+    const float* topk, const float* cdfthreshd, const float* simthreshd1, float softmax_scale,
+    unsigned flags, int32_t* lut, int32_t* lut_count, uint8_t* block_map, float* pooled_prob, uint8_t* sim_q,
+    uint8_t* sim_k, float* q_mean, float* k_mean, int8_t* q_i8, float* q_i8_scale, int8_t* k_i8,
+    float* k_i8_scale, void* stream) {
+  return block_map_impl(q, k, dt, b, h, h_kv, s_q, s_k, d, q_strides, k_strides, blk_q, blk_k, topk, cdfthreshd,
+                        simthreshd1, softmax_scale, flags, lut, lut_count, block_map, pooled_prob, sim_q, sim_k,
+                        q_mean, k_mean, q_i8, q_i8_scale, k_i8, k_i8_scale, nullptr, 0, true, stream);
 }
 
 sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

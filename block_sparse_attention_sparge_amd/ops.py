@@ -23,14 +23,15 @@ LIB_PATH = os.path.join(_PKG, "libsparge.so")
 SPARGE_OK, SPARGE_ERR_INVALID, SPARGE_ERR_UNSUPPORTED, SPARGE_ERR_HIP = 0, 1, 2, 3
 SPARGE_F16, SPARGE_BF16, SPARGE_F32 = 0, 1, 2
 SPARGE_FLAG_SMOOTH_K, SPARGE_FLAG_CAUSAL, SPARGE_FLAG_ATTN_SINK = 1, 2, 4
-ABI_VERSION = 5
+ABI_VERSION = 6
+NOALLOC_SCRATCH_BYTES = 32 << 20
 MAX_HEADS = 128
 MAX_KBLOCKS = 1024
 
 EXPORTED_SYMBOLS = (
     "sparge_abi_version", "sparge_last_error", "sparge_build_block_map",
     "sparge_build_block_map_workspace", "sparse_fmha_fwd", "sparse_fmha_fwd_qk_int8", "attn_combine",
-    "sparge_validate_lut",
+    "sparge_validate_lut", "sparge_build_block_map_noalloc",
 )
 
 
@@ -78,6 +79,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         lib.sparge_build_block_map.argtypes = [
             _p, _p, _i, _i, _i, _i, _i, _i, _i, _I64x3, _I64x3, _i, _i,
             _p, _p, _p, _f, _u, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
+        lib.sparge_build_block_map_noalloc.restype = _i
+        lib.sparge_build_block_map_noalloc.argtypes = [
+            _p, _p, _i, _i, _i, _i, _i, _i, _i, _I64x3, _I64x3, _i, _i,
+            _p, _p, _p, _f, _u, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]
         lib.sparse_fmha_fwd.restype = _i
         lib.sparse_fmha_fwd.argtypes = [
             _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
@@ -198,6 +203,26 @@ def build_block_map(q: torch.Tensor, k: torch.Tensor, topk, simthreshd1, cdfthre
                     return_debug: bool = False, workspace: Optional[torch.Tensor] = None,
                     out: Optional[dict] = None, smooth_k: bool = False, causal: bool = False,
                     attention_sink: bool = False, quantize_int8: bool = False) -> dict:
+    return _block_map(q, k, topk, simthreshd1, cdfthreshd, softmax_scale, blk_q, blk_k, return_debug,
+                      workspace, out, smooth_k, causal, attention_sink, quantize_int8, noalloc=False)
+
+
+def build_block_map_noalloc(q: torch.Tensor, k: torch.Tensor, topk, simthreshd1, cdfthreshd=None,
+                            softmax_scale: float = 0.0, blk_q: int = 64, blk_k: int = 64,
+                            return_debug: bool = False, out: Optional[dict] = None,
+                            smooth_k: bool = False, causal: bool = False,
+                            attention_sink: bool = False, quantize_int8: bool = False) -> dict:
+    """build_block_map through sparge_build_block_map_noalloc: the library's
+    static per-GPU scratch (NOALLOC_SCRATCH_BYTES) replaces the workspace.
+    Outputs not given in `out` are still allocated here by torch; pass them
+    all in `out` for a call that allocates nothing (e.g. under graph capture).
+    Calls whose work overlaps on one GPU share the scratch and race."""
+    return _block_map(q, k, topk, simthreshd1, cdfthreshd, softmax_scale, blk_q, blk_k, return_debug,
+                      None, out, smooth_k, causal, attention_sink, quantize_int8, noalloc=True)
+
+
+def _block_map(q, k, topk, simthreshd1, cdfthreshd, softmax_scale, blk_q, blk_k, return_debug,
+               workspace, out, smooth_k, causal, attention_sink, quantize_int8, noalloc) -> dict:
     """Stage 1 (sparge_build_block_map).  q [b, h, s_q, d], k [b, h_kv, s_k, d]
     with h a multiple of h_kv (query head j reads K head j // (h / h_kv)).
 
@@ -249,23 +274,28 @@ def build_block_map(q: torch.Tensor, k: torch.Tensor, topk, simthreshd1, cdfthre
         for key in ("q_i8", "k_i8"):
             if not qz[key].is_contiguous():
                 raise SpargeError(SPARGE_ERR_INVALID, f"{key} must be contiguous")
+    args = (_ptr(q), _ptr(k), _dt(q.dtype), b, h, h_kv, s_q, s_k, d, _strides(q), _strides(k), blk_q, blk_k,
+            _f32_array(topk, h, "topk"), _f32_array(cdfthreshd, h, "cdfthreshd"),
+            _f32_array(simthreshd1, h, "simthreshd1"), float(softmax_scale),
+            _flags(smooth_k=smooth_k, causal=causal, attention_sink=attention_sink),
+            _ptr(lut), _ptr(count), _ptr(dbg.get("bitmap")), _ptr(dbg.get("prob")),
+            _ptr(dbg.get("sim_q")), _ptr(dbg.get("sim_k")), _ptr(dbg.get("q_mean")),
+            _ptr(dbg.get("k_mean")), _ptr(qz.get("q_i8")), _ptr(qz.get("q_i8_scale")),
+            _ptr(qz.get("k_i8")), _ptr(qz.get("k_i8_scale")))
+    if noalloc:
+        _check(lib.sparge_build_block_map_noalloc(*args, _stream(dev)))
+        res = dict(lut=lut, count=count)
+        res.update(dbg)
+        res.update(qz)
+        return res
     ws_bytes = lib.sparge_build_block_map_workspace(b, h, s_q, s_k, d, blk_q, blk_k)
     if workspace is None:
         workspace = out.get("workspace")
     if workspace is None:
         workspace = torch.empty(max(int(ws_bytes), 256), dtype=torch.uint8, device=dev)
         out["workspace"] = workspace
-    st = lib.sparge_build_block_map(
-        _ptr(q), _ptr(k), _dt(q.dtype), b, h, h_kv, s_q, s_k, d, _strides(q), _strides(k), blk_q, blk_k,
-        _f32_array(topk, h, "topk"), _f32_array(cdfthreshd, h, "cdfthreshd"),
-        _f32_array(simthreshd1, h, "simthreshd1"), float(softmax_scale),
-        _flags(smooth_k=smooth_k, causal=causal, attention_sink=attention_sink),
-        _ptr(lut), _ptr(count), _ptr(dbg.get("bitmap")), _ptr(dbg.get("prob")),
-        _ptr(dbg.get("sim_q")), _ptr(dbg.get("sim_k")), _ptr(dbg.get("q_mean")),
-        _ptr(dbg.get("k_mean")), _ptr(qz.get("q_i8")), _ptr(qz.get("q_i8_scale")),
-        _ptr(qz.get("k_i8")), _ptr(qz.get("k_i8_scale")), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(dev))
-    _check(st)
+    _check(lib.sparge_build_block_map(*args, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(dev)))
     res = dict(lut=lut, count=count, workspace=workspace)
     res.update(dbg)
     res.update(qz)

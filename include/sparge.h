@@ -69,7 +69,12 @@ typedef enum {
 #define SPARGE_FLAG_CAUSAL 2u     /* block map and block-mode FMHA: causal masks   */
 #define SPARGE_FLAG_ATTN_SINK 4u  /* block map: K block 0 selected in every row    */
 
-/* Library ABI version (this header: 5). */
+/* Device scratch held by sparge_build_block_map_noalloc on each GPU it runs
+ * on (32 MiB: enough for the block map of b2 h32 s16384 d128, which needs
+ * 16.6 MiB). */
+#define SPARGE_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* Library ABI version (this header: 6). */
 int sparge_abi_version(void);
 
 /* Message for the last failed call on this thread ("" if none). */
@@ -151,6 +156,33 @@ sparge_status sparge_build_block_map(
     uint8_t* sim_q, uint8_t* sim_k, float* q_mean, float* k_mean,
     int8_t* q_i8, float* q_i8_scale, int8_t* k_i8, float* k_i8_scale,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sparge_build_block_map without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Arguments, outputs and results
+ * are those of sparge_build_block_map; the scratch it needs lives in a
+ * static device array of SPARGE_NOALLOC_SCRATCH_BYTES held by the library on
+ * each GPU until the process ends.  The call allocates nothing: the first
+ * call with a given device current looks the array's address up
+ * (hipGetSymbolAddress) and keeps it.  Sizes whose workspace
+ * (sparge_build_block_map_workspace) exceeds SPARGE_NOALLOC_SCRATCH_BYTES
+ * return SPARGE_ERR_UNSUPPORTED with nothing enqueued.  Every call on one GPU
+ * shares that array: calls whose work overlaps on one GPU (other streams,
+ * other threads) race and give undefined results; calls ordered on one stream
+ * are safe.  The array's contents on entry are ignored.
+ */
+sparge_status sparge_build_block_map_noalloc(
+    const void* q, const void* k, sparge_dtype dt,
+    int b, int h, int h_kv, int s_q, int s_k, int d,
+    const int64_t q_strides[3], const int64_t k_strides[3],
+    int blk_q, int blk_k,
+    const float* topk, const float* cdfthreshd, const float* simthreshd1,
+    float softmax_scale, unsigned flags,
+    int32_t* lut, int32_t* lut_count, uint8_t* block_map, float* pooled_prob,
+    uint8_t* sim_q, uint8_t* sim_k, float* q_mean, float* k_mean,
+    int8_t* q_i8, float* q_i8_scale, int8_t* k_i8, float* k_i8_scale,
+    void* stream);
 
 /* Bytes of device workspace sparge_build_block_map needs for these sizes
  * (0 if the sizes are invalid); enough for any h_kv dividing h. */

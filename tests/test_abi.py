@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert lib.sparge_abi_version() == ops.ABI_VERSION == 5
+    assert lib.sparge_abi_version() == ops.ABI_VERSION == 6
 
 
 def _s3(a, b, c):
@@ -122,6 +122,43 @@ def test_block_map_rejections(lib, kw, status):
     st = _bm(lib, **kw)
     assert st == status, _err(lib)
     assert _err(lib) != ""
+
+
+def _bm_noalloc(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, dt=ops.SPARGE_F16, b=1, h=2, hkv=2, s_q=512, s_k=512, d=64,
+                qs=_s3(65536, 32768, 64), ks=_s3(65536, 32768, 64), blk_q=64, blk_k=64,
+                topk=_arr([0.5, 0.5]), cdf=None, sim=_arr([0.001, 0.001]), scale=0.0, flags=0,
+                lut=FAKE, cnt=FAKE)
+    args.update(kw)
+    h = args["h"]
+    return lib.sparge_build_block_map_noalloc(
+        args["q"], args["k"], args["dt"], args["b"], h, args["hkv"], args["s_q"], args["s_k"], args["d"],
+        args["qs"], args["ks"], args["blk_q"], args["blk_k"], args["topk"], args["cdf"], args["sim"],
+        args["scale"], args["flags"], args["lut"], args["cnt"], None, None, None, None, None, None,
+        None, None, None, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ops.SPARGE_ERR_INVALID),
+    (dict(d=96), ops.SPARGE_ERR_UNSUPPORTED),
+    (dict(b=0), ops.SPARGE_ERR_INVALID),
+    (dict(topk=_arr([1.5, 0.5])), ops.SPARGE_ERR_INVALID),
+    (dict(flags=8), ops.SPARGE_ERR_INVALID),
+    # b4 h32 s16384 d128 needs about 34 MiB of scratch, beyond the 32 MiB held
+    (dict(b=4, h=32, hkv=32, s_q=16384, s_k=16384, d=128, qs=_s3(32 << 21, 1 << 21, 128),
+          ks=_s3(32 << 21, 1 << 21, 128), topk=_arr([0.4] * 32), sim=_arr([0.001] * 32)),
+     ops.SPARGE_ERR_UNSUPPORTED),
+])
+def test_block_map_noalloc_rejections(lib, kw, status):
+    # Host validation runs in full before the scratch array is looked up, so
+    # none of these reaches the device.
+    assert _bm_noalloc(lib, **kw) == status, _err(lib)
+    assert _err(lib) != ""
+
+
+def test_noalloc_scratch_fits_the_headline_block_map(lib):
+    need = lib.sparge_build_block_map_workspace(2, 32, 16384, 16384, 128, 64, 64)
+    assert need <= ops.NOALLOC_SCRATCH_BYTES < lib.sparge_build_block_map_workspace(4, 32, 16384, 16384, 128, 64, 64)
 
 
 def _fmha(lib, **kw):

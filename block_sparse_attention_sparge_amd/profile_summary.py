@@ -1,32 +1,33 @@
-"""Summarise rocprofv3 CSV output of a bench.py run into short markdown files.
+"""Summarise rocprofv3 CSV output of bench.py runs into short markdown files.
 
-Two reports:
+Reports:
 
-  trace    kernel statistics (rocprofv3 --kernel-trace --stats) plus the
-           per-arm durations of the sparse FMHA launches;
-  traffic  HBM bytes per sparse FMHA launch from two counter runs
-           (--pmc FETCH_SIZE, then --pmc WRITE_SIZE), each scaled by what the
-           same counter reads for a plain device-to-device copy of known size.
+  trace     kernel statistics (rocprofv3 --kernel-trace --stats) of a default
+            bench.py run, plus the durations of the sparse FMHA launches of
+            its timed headline region: bench.py runs that region first, so
+            they are FMHA dispatches warmup .. warmup + steps - 1;
+  traffic   HBM bytes per sparse FMHA launch from two counter runs
+            (--pmc FETCH_SIZE, then --pmc WRITE_SIZE) of
+            `bench.py --profile-arm ARM`, whose only FMHA launches are that
+            arm's; each counter is scaled by what it reads for a plain
+            device-to-device copy of known size;
+  bytes     copy-calibrated HBM bytes per dispatch for every kernel of the
+            library in two counter runs, grouped by kernel and grid;
+  counters  the mean of every counter of one --pmc run over the FMHA
+            launches of a --profile-arm run (e.g. MfmaUtil, LdsUtil,
+            SQ_INSTS_VALU_MFMA_MOPS_F16, whose count times 512 is the MFMA
+            flops), next to the launch's algorithmic flops.
 
-bench.py times its arms in a fixed order (topk 0.4, topk 0.1, dense), each
-arm calling the FMHA 2 * (warmup + steps) times (FMHA alone, then block map +
-FMHA), and the dense arm 2 + max(5, steps // 2) times; dispatches are assigned
-to arms in that order.  The traffic report records the SHA-256 of the FMHA
-source so that bench.py stops quoting it once the kernel changes.
-
-A third report, bytes, gives copy-calibrated HBM bytes per dispatch for
-every kernel of the library in two counter runs, grouped by kernel and grid.
-A fourth, counters, gives the per-arm mean of every counter of one --pmc run
-over the sparse FMHA launches (e.g. MfmaUtil, LdsUtil, LDSBankConflict and
-SQ_INSTS_VALU_MFMA_MOPS_F16, whose count times 512 is the MFMA flops), next
-to the launch's algorithmic flops when the arm's block pairs are given.
+In every report the first `--warmup` FMHA dispatches are the untimed warmup
+and are left out.  The traffic report records the SHA-256 of the FMHA source
+so that bench.py stops quoting it once the kernel changes.
 
 Usage:
   python -m block_sparse_attention_sparge_amd.profile_summary trace DIR \
       --steps K --warmup W --command "..." > profiles/x.md
   python -m block_sparse_attention_sparge_amd.profile_summary traffic \
-      --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \
-      --copy-bytes N --steps K --warmup W --command "..." > profiles/y.md
+      --arm "topk 0.4" FETCH_DIR WRITE_DIR [--arm ...] --copy-fetch DIR --copy-write DIR \
+      --copy-bytes N --warmup W --command "..." > profiles/y.md
 """
 from __future__ import annotations
 
@@ -57,12 +58,6 @@ def _one(dirpath: str, pattern: str) -> str:
     return max(hits, key=os.path.getmtime)
 
 
-def arm_slices(steps: int, warmup: int):
-    per = 2 * (warmup + steps)
-    dense = 2 + max(5, steps // 2)
-    return [("topk 0.4", 0, per), ("topk 0.1", per, 2 * per), ("dense", 2 * per, 2 * per + dense)]
-
-
 def _fmha_dispatches(rows, key="Dispatch_Id"):
     sel = [r for r in rows if FMHA_KERNEL in r["Kernel_Name"]]
     sel.sort(key=lambda r: int(r[key]))
@@ -82,59 +77,49 @@ def trace_report(dirpath: str, steps: int, warmup: int, command: str) -> str:
         out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
     fm = _fmha_dispatches(trace)
     dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in fm]
-    out += ["", f"Sparse FMHA launches by bench arm (dispatch order; steps {steps}, warmup {warmup}):", "",
-            "| arm | launches | mean us | median us | min us |", "|---|---|---|---|---|"]
-    for name, a, b in arm_slices(steps, warmup):
-        d = dur[a:b]
-        if d:
-            out.append(f"| {name} | {len(d)} | {statistics.mean(d):.1f} | {statistics.median(d):.1f} | {min(d):.1f} |")
+    d = dur[warmup:warmup + steps]
+    out += ["", f"Sparse FMHA launches of the timed headline region (topk 0.4; FMHA dispatches {warmup} .. "
+                f"{warmup + steps - 1} of the run):", "",
+            "| launches | mean us | median us | min us | max us |", "|---|---|---|---|---|"]
+    if d:
+        out.append(f"| {len(d)} | {statistics.mean(d):.1f} | {statistics.median(d):.1f} | {min(d):.1f} | "
+                   f"{max(d):.1f} |")
     return "\n".join(out) + "\n"
 
 
-def _counter_means(dirpath: str, steps: int, warmup: int):
+def _counter_mean(dirpath: str, warmup: int) -> float:
+    """Mean per FMHA launch (counter values summed over a dispatch's rows)
+    after the warmup launches."""
     rows = list(csv.DictReader(open(_one(dirpath, "*counter_collection.csv"))))
-    fm = _fmha_dispatches(rows)
     vals = {}
-    for r in fm:
+    for r in _fmha_dispatches(rows):
         vals.setdefault(int(r["Dispatch_Id"]), 0.0)
         vals[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
-    ordered = [vals[k] for k in sorted(vals)]
-    res = {}
-    for name, a, b in arm_slices(steps, warmup):
-        v = ordered[a:b]
-        if v:
-            res[name] = sum(v) / len(v)
-    return res
+    ordered = [vals[k] for k in sorted(vals)][warmup:]
+    if not ordered:
+        raise SystemExit(f"no FMHA dispatch after the warmup in {dirpath}")
+    return sum(ordered) / len(ordered)
 
 
-def counters_report(dirpath: str, steps: int, warmup: int, command: str, pairs: dict,
+def counters_report(dirpath: str, warmup: int, command: str, arm: str, pairs: int,
                     flops_per_pair: float) -> str:
     rows = list(csv.DictReader(open(_one(dirpath, "*counter_collection.csv"))))
-    fm = _fmha_dispatches(rows)
     per = {}
-    for r in fm:
+    for r in _fmha_dispatches(rows):
         d = per.setdefault(int(r["Dispatch_Id"]), {})
         d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-    ids = sorted(per)
-    names = sorted({n for d in per.values() for n in d})
+    sel = [per[i] for i in sorted(per)][warmup:]
+    names = sorted({n for d in sel for n in d})
     out = ["# Hardware counters of the sparse FMHA (rocprofv3 --pmc)", "", "Command:", "", "```",
            command, "```", "",
-           f"Per-arm means over the FMHA launches of the bench (dispatch order; steps {steps}, warmup {warmup}).",
-           "", "| arm | launches | " + " | ".join(names) + " |",
-           "|---|---|" + "---|" * len(names)]
-    extra = []
-    for name, a, b in arm_slices(steps, warmup):
-        sel = [per[i] for i in ids[a:b]]
-        if not sel:
-            continue
-        means = {n: statistics.fmean(d.get(n, 0.0) for d in sel) for n in names}
-        out.append(f"| {name} | {len(sel)} | " + " | ".join(f"{means[n]:.4g}" for n in names) + " |")
-        if "SQ_INSTS_VALU_MFMA_MOPS_F16" in means and name in pairs:
-            alg = flops_per_pair * pairs[name]
-            extra.append(f"- {name}: MFMA flops counted {means['SQ_INSTS_VALU_MFMA_MOPS_F16'] * 512:.4e}, "
-                         f"algorithmic {alg:.4e} ({pairs[name]} block pairs x {flops_per_pair:.4g})")
-    if extra:
-        out += ["", "MFMA work per launch against the algorithmic work:", ""] + extra
+           f"Means over the {len(sel)} FMHA launches of the run after {warmup} warmup launches, arm {arm}.",
+           "", "| counter | mean per launch |", "|---|---|"]
+    means = {n: statistics.fmean(d.get(n, 0.0) for d in sel) for n in names}
+    out += [f"| {n} | {means[n]:.4g} |" for n in names]
+    if "SQ_INSTS_VALU_MFMA_MOPS_F16" in means and pairs:
+        alg = flops_per_pair * pairs
+        out += ["", f"MFMA flops counted {means['SQ_INSTS_VALU_MFMA_MOPS_F16'] * 512:.4e}, algorithmic "
+                    f"{alg:.4e} ({pairs} block pairs x {flops_per_pair:.4g})."]
     return "\n".join(out) + "\n"
 
 
@@ -148,10 +133,9 @@ def _copy_kib(dirpath: str) -> float:
     return statistics.median(vals)
 
 
-def traffic_report(fetch: str, write: str, copy_fetch: str, copy_write: str, copy_bytes: int,
-                   steps: int, warmup: int, command: str) -> str:
-    fe = _counter_means(fetch, steps, warmup)
-    wr = _counter_means(write, steps, warmup)
+def traffic_report(arms, copy_fetch: str, copy_write: str, copy_bytes: int, warmup: int,
+                   command: str) -> str:
+    """arms: list of (arm name, FETCH_SIZE run dir, WRITE_SIZE run dir)."""
     cf, cw = _copy_kib(copy_fetch), _copy_kib(copy_write)
     fetch_scale = copy_bytes / 1024.0 / cf
     write_scale = copy_bytes / 1024.0 / cw
@@ -162,10 +146,11 @@ def traffic_report(fetch: str, write: str, copy_fetch: str, copy_write: str, cop
            f"{fetch_scale:.3f} (fetch) and {write_scale:.3f} (write).", "",
            "| arm | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled bytes per launch |", "|---|---|---|---|"]
     summary = {}
-    for arm in fe:
-        b = fe[arm] * fetch_scale * 1024 + wr.get(arm, 0.0) * write_scale * 1024
+    for arm, fdir, wdir in arms:
+        fe, wr = _counter_mean(fdir, warmup), _counter_mean(wdir, warmup)
+        b = fe * fetch_scale * 1024 + wr * write_scale * 1024
         summary[arm] = b
-        out.append(f"| {arm} | {fe[arm]:.0f} | {wr.get(arm, 0.0):.0f} | {b:.4g} |")
+        out.append(f"| {arm} | {fe:.0f} | {wr:.0f} | {b:.4g} |")
     rec = {"kernel": FMHA_KERNEL, "source_sha256": source_sha256(), "fetch_scale": fetch_scale,
            "write_scale": write_scale, "bytes_per_launch": summary}
     out += ["", "Machine-readable line read by bench.py:", "", "traffic_json: " + json.dumps(rec)]
@@ -223,25 +208,22 @@ def main(argv=None) -> int:
     sub = ap.add_subparsers(dest="cmd", required=True)
     t = sub.add_parser("trace")
     t.add_argument("dir")
-    for p in (t,):
-        p.add_argument("--steps", type=int, required=True)
-        p.add_argument("--warmup", type=int, required=True)
-        p.add_argument("--command", required=True)
+    t.add_argument("--steps", type=int, required=True)
+    t.add_argument("--warmup", type=int, required=True)
+    t.add_argument("--command", required=True)
     f = sub.add_parser("traffic")
-    f.add_argument("--fetch", required=True)
-    f.add_argument("--write", required=True)
+    f.add_argument("--arm", nargs=3, action="append", required=True, metavar=("NAME", "FETCH_DIR", "WRITE_DIR"))
     f.add_argument("--copy-fetch", required=True)
     f.add_argument("--copy-write", required=True)
     f.add_argument("--copy-bytes", type=int, required=True)
-    f.add_argument("--steps", type=int, required=True)
     f.add_argument("--warmup", type=int, required=True)
     f.add_argument("--command", required=True)
     c = sub.add_parser("counters")
     c.add_argument("dir")
-    c.add_argument("--steps", type=int, required=True)
     c.add_argument("--warmup", type=int, required=True)
     c.add_argument("--command", required=True)
-    c.add_argument("--pairs", default="{}", help='JSON {"topk 0.4": pairs, ...}')
+    c.add_argument("--arm", required=True)
+    c.add_argument("--pairs", type=int, default=0)
     c.add_argument("--flops-per-pair", type=float, default=4.0 * 64 * 64 * 128)
     bt = sub.add_parser("bytes")
     for opt in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--command"):
@@ -251,13 +233,11 @@ def main(argv=None) -> int:
     if a.cmd == "trace":
         sys.stdout.write(trace_report(a.dir, a.steps, a.warmup, a.command))
     elif a.cmd == "counters":
-        sys.stdout.write(counters_report(a.dir, a.steps, a.warmup, a.command, json.loads(a.pairs),
-                                         a.flops_per_pair))
+        sys.stdout.write(counters_report(a.dir, a.warmup, a.command, a.arm, a.pairs, a.flops_per_pair))
     elif a.cmd == "bytes":
         sys.stdout.write(bytes_report(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes, a.command))
     else:
-        sys.stdout.write(traffic_report(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes,
-                                        a.steps, a.warmup, a.command))
+        sys.stdout.write(traffic_report(a.arm, a.copy_fetch, a.copy_write, a.copy_bytes, a.warmup, a.command))
     return 0
 
 

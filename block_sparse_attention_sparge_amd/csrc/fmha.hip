@@ -27,9 +27,12 @@
 //     in the attention kernel), the workgroup drops the PV product of a whole
 //     listed block when every one of the tile's 64 query rows scores, over
 //     the block's 64 keys, more than the threshold below that row's running
-//     maximum over the blocks already visited; the four wavefronts pool
-//     their row maxima in LDS and all take the same decision, and a dropped
-//     block reads no V^T either; its P still count in the row sum;
+//     maximum over the blocks already visited; its P still count in the row
+//     sum.  The four wavefronts post their row maxima to LDS; in this
+//     variant the block's one barrier comes after the softmax, so it
+//     publishes them, and every wave then takes the same decision and runs
+//     the block's PV product from registers (its operands were read from LDS
+//     before the barrier), so the test adds no barrier;
 //   * workgroups are renumbered so that consecutive rows of one head land on
 //     one XCD and share its L2 (aiter 4919 page: workgroups round-robin over
 //     the 8 XCDs by linear id); causal rows are taken last tile first.
@@ -99,9 +102,10 @@ void fmha_block_kernel(FmhaArgs a) {
   __shared__ __attribute__((aligned(16))) T sK[2 * TILE];
   __shared__ __attribute__((aligned(16))) T sV[2 * TILE];
   __shared__ float s_ml[128];                // (m, l) of the kh = 1 waves, per query half
-  // pv_threshold vote: (block maximum, running maximum) of each wave's 32
-  // query rows over its 32 keys, scaled base-2 units.
-  __shared__ float2v s_vote[PVSKIP ? 128 : 1];
+  // pv_threshold votes: (block maximum, running maximum) of each wave's 32
+  // query rows over its 32 keys, scaled base-2 units; two slots by block
+  // parity, so a block's votes are read while the next block's are written.
+  __shared__ float2v s_vote[PVSKIP ? 256 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -258,6 +262,18 @@ void fmha_block_kernel(FmhaArgs a) {
   int kb_ahead = nloc > 1 ? kb_of(1) : 0;
   int kb_cur = MASKED ? kb_of(0) : 0;
 
+  // pv_threshold: the decision on the block whose votes are in `slot`: query
+  // row i of the tile (lane i) has r_i = its maximum over the block's 64
+  // keys and M_i its running maximum over the blocks visited so far, this
+  // one included; the block is dropped when r_i < M_i - tau for all 64 rows.
+  // Every wave reads the same values and takes the same decision.
+  auto pv_keep_block = [&](int slot) {
+    const int vq = lane >> 5, vr = lane & 31;
+    const float2v h0 = s_vote[slot * 128 + vq * 32 + vr], h1 = s_vote[slot * 128 + (2 + vq) * 32 + vr];
+    const float r_i = fmaxf(h0[0], h1[0]), m_i = fmaxf(h0[1], h1[1]);
+    return __any(!(r_i < m_i - a.pv_tau2));
+  };
+
   // One 64-key block out of LDS buffer `cur` (a compile-time constant, so
   // every LDS address is a fixed register plus an immediate offset).
   auto step = [&](int it, auto cur_tag) {
@@ -266,6 +282,18 @@ void fmha_block_kernel(FmhaArgs a) {
     const SPARGE_LDS T* vt = (const SPARGE_LDS T*)&sV[cur * TILE];
 
     asm volatile("" ::"s"(kb_ahead));   // the LUT load of the previous step has landed
+  // pv_threshold: the decision on the block whose votes are in `slot`: query
+  // row i of the tile (lane i) has r_i = its maximum over the block's 64
+  // keys and M_i its running maximum over the blocks visited so far, this
+  // one included; the block is dropped when r_i < M_i - tau for all 64 rows.
+  // Every wave reads the same values and takes the same decision.
+  auto pv_keep_block = [&](int slot) {
+    const int vq = lane >> 5, vr = lane & 31;
+    const float2v h0 = s_vote[slot * 128 + vq * 32 + vr], h1 = s_vote[slot * 128 + (2 + vq) * 32 + vr];
+    const float r_i = fmaxf(h0[0], h1[0]), m_i = fmaxf(h0[1], h1[1]);
+    return __any(!(r_i < m_i - a.pv_tau2));
+  };
+
     // LDS operands are requested early so that their latency overlaps the
     // MFMAs: the 8 K reads and the first half of V^T before S^T, the second
     // half of V^T right after it (16 reads in flight is as deep as the LDS
@@ -293,15 +321,14 @@ void fmha_block_kernel(FmhaArgs a) {
         }
       }
     };
-    // (With a pv_threshold the V^T reads wait for the tile's decision.)
-    if constexpr (!PVSKIP) read_vt(0);
+    read_vt(0);
     __builtin_amdgcn_sched_barrier(0);
 
     // S^T (32 keys x 32 queries) = K Q^T.
     floatx16 s = floatx16{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) s = mfma32<E>(kf[kk], qf[kk], s);
-    if constexpr (!PVSKIP) read_vt(1);
+    read_vt(1);
     __builtin_amdgcn_sched_barrier(0);
     // The other buffer held block it-1, released by the last barrier.
     if (it + 1 < nloc) issue_block(kb_ahead, 1 - cur);
@@ -343,8 +370,8 @@ void fmha_block_kernel(FmhaArgs a) {
     // carried by one key would move the LSE by up to 4e-3 nats.
     // Masked rows may still have no key (m_run = -inf): their P is 0.
     //
-    // O^T += V^T P^T over this wave's 32 keys, unless the tile skips the
-    // block (pv_threshold).  The four
+    // O^T += V^T P^T over this wave's 32 keys (with a pv_threshold, after
+    // the barrier, unless the tile drops the block).  The four
     // PV MFMAs of k-step 0 are issued as soon as its 8 P values exist, so the
     // exponentials of k-step 1 run in their shadow.  From the first PV MFMA to
     // the last the wave runs at raised priority: of the two wavefronts sharing
@@ -354,25 +381,13 @@ void fmha_block_kernel(FmhaArgs a) {
     // at topk 0.1; the split issue 1% and 2% more; priority on the S MFMAs as
     // well gains nothing).
     const float mref = MASKED && m_run == -INFINITY ? 0.f : m_run;
-    bool pv = true;
     if constexpr (PVSKIP) {
-      // Query row i of the tile (lane i of each wave after the exchange):
-      // r_i = its maximum over the block's 64 keys, M_i = its running
-      // maximum over the blocks visited so far, this one included.  The
-      // block is dropped when r_i < M_i - tau for all 64 rows; every wave
-      // reads the same values and takes the same decision.  The vote slots
-      // are rewritten only after the barrier that ends this step.
+      // This wave's votes on the block, for its 32 query rows over its 32
+      // keys: the block maximum and the running maximum, this block
+      // included.  Slot `cur` was last read right after the barrier of two
+      // blocks ago, before the previous barrier.
       m_top = fmaxf(m_top, m_cand);
-      if (hl == 0) s_vote[wave * 32 + l32] = float2v{m_cand, m_top};
-      __syncthreads();
-      const int vq = lane >> 5, vr = lane & 31;
-      const float2v h0 = s_vote[vq * 32 + vr], h1 = s_vote[(2 + vq) * 32 + vr];
-      const float r_i = fmaxf(h0[0], h1[0]), m_i = fmaxf(h0[1], h1[1]);
-      pv = __any(!(r_i < m_i - a.pv_tau2));
-      if (pv) {
-        read_vt(0);
-        read_vt(1);
-      }
+      if (hl == 0) s_vote[cur * 128 + wave * 32 + l32] = float2v{m_cand, m_top};
     }
     u32x4 pf[2];
     float p[16];
@@ -389,7 +404,7 @@ void fmha_block_kernel(FmhaArgs a) {
         __builtin_amdgcn_s_setprio(1);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (pv) {
+      if constexpr (!PVSKIP) {
 #pragma unroll
         for (int md = 0; md < NMD; ++md) acc_o[md] = mfma32<E>(vf[ks][md], pf[ks], acc_o[md]);
       }
@@ -410,6 +425,19 @@ void fmha_block_kernel(FmhaArgs a) {
     // Block it+1 must have landed before the barrier hands the buffers over.
     wait_dma();
     __syncthreads();
+    if constexpr (PVSKIP) {
+      // Every wave's votes on this block are visible now, and its V^T
+      // operands are in registers (the barrier waited for every LDS read),
+      // so the next block's loads may overwrite its buffers.
+      if (pv_keep_block(cur)) {
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int md = 0; md < NMD; ++md) acc_o[md] = mfma32<E>(vf[ks][md], pf[ks], acc_o[md]);
+        __builtin_amdgcn_s_setprio(0);
+      }
+    }
     if constexpr (MASKED) kb_cur = kb_ahead;
     kb_ahead = kb_next;
   };

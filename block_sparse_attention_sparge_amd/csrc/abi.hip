@@ -361,6 +361,13 @@ sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void*
   }
   // token-list mode
   if (!lut) return fail(SPARGE_ERR_INVALID, "token-list mode needs an index list");
+  {
+    // Rows are gathered with 32-bit byte offsets into one (b, KV head) slice.
+    const int64_t kspan = (int64_t)s_k * k_strides[2] * 2, vspan = (int64_t)s_k * v_strides[2] * 2;
+    if (std::max(kspan, vspan) >= (int64_t(1) << 31))
+      return fail(SPARGE_ERR_UNSUPPORTED, "token-list mode: a (b, KV head) slice of K or V spans %lld bytes "
+                  "(limit 2^31)", (long long)std::max(kspan, vspan));
+  }
   if (lut_count) return fail(SPARGE_ERR_INVALID, "token-list mode takes no lut_count");
   if (lut_heads != h_kv)
     return fail(SPARGE_ERR_UNSUPPORTED, "token-list mode needs one list per KV head (lut_heads = h_kv)");

@@ -84,6 +84,11 @@ __device__ __forceinline__ float half_swap_max(float x) {
   return fmaxf(a, b);
 }
 
+// Word 3 of a raw buffer resource on gfx9-family parts (gfx950): 32-bit
+// data format, no swizzle, so offsets count bytes and an access at or past
+// the record count reads zero.
+constexpr int kBufferWord3 = 0x00020000;
+
 // Compile-time buffer index for the two-way unrolled block loop.
 template <int N>
 struct Buf {

@@ -6,6 +6,14 @@
 // head j / ratio) over an index list in which -1 entries are skipped (aiter
 // 4919 page).  Keys are gathered 64 at a time; scores and the PV update run
 // on the vector ALUs in fp32.
+//
+// The K and V rows are gathered with buffer loads: one resource per (batch,
+// KV head) slice and a 32-bit byte offset per row (the host keeps a slice
+// below 2^31 bytes; aiter 4919 page: the 32-bit offset limit of buffer
+// loads).  A -1 entry takes the offset 2^31, past the slice, which the
+// buffer range check turns into zeros (aiter 6841 page: an out-of-range read
+// clamped by the descriptor's record count), so the loaded data needs no
+// select.
 #include "attn_common.h"
 #include "common.h"
 #include "kernels.h"
@@ -76,6 +84,12 @@ __global__ __launch_bounds__(256) void fmha_tokens_kernel(FmhaArgs a) {
 
   const T* kbase = reinterpret_cast<const T*>(a.k) + bb * a.ks[0] + hk * a.ks[1];
   const T* vbase = reinterpret_cast<const T*>(a.v) + bb * a.vs[0] + hk * a.vs[1];
+  // Raw buffer resources over the slice (records counted in bytes).
+  const uint32_t krow_b = (uint32_t)(a.ks[2] * (int64_t)sizeof(T)), vrow_b = (uint32_t)(a.vs[2] * (int64_t)sizeof(T));
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(kbase), (short)0, (int)(krow_b * (uint32_t)a.sk), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(vbase), (short)0, (int)(vrow_b * (uint32_t)a.sk), kBufferWord3);
   const float c2 = a.scale_log2;
   const int qj = tid >> 2, qq = tid & 3;        // QK phase: key slot, quarter
   const int pc = tid % CPR, ps = tid / CPR;     // PV phase: d chunk, key subset
@@ -85,13 +99,15 @@ __global__ __launch_bounds__(256) void fmha_tokens_kernel(FmhaArgs a) {
   // Each thread reads only the list entries it gathers: key slot qj for K and
   // key slots ps + NS*i for V.
   auto tok = [&](int pos) { return pos < end ? list[pos] : -1; };
+  auto row_off = [](int t, uint32_t row_b) { return t >= 0 ? (uint32_t)t * row_b : 0x80000000u; };
   auto load_chunk = [&](int tk, const int (&tv)[KPS], u32x4 (&kr)[QW / 8], u32x4 (&vr)[KPS]) {
+    const uint32_t ko = row_off(tk, krow_b) + 16u * qq;
 #pragma unroll
     for (int i = 0; i < QW / 8; ++i)
-      kr[i] = tk >= 0 ? load16(kbase + (int64_t)tk * a.ks[2] + 32 * i + 8 * qq) : u32x4{0u, 0u, 0u, 0u};
+      kr[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)(ko + 64u * i), 0, 0);
 #pragma unroll
     for (int i = 0; i < KPS; ++i)
-      vr[i] = tv[i] >= 0 ? load16(vbase + (int64_t)tv[i] * a.vs[2] + pc * 8) : u32x4{0u, 0u, 0u, 0u};
+      vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)(row_off(tv[i], vrow_b) + 16u * pc), 0, 0);
   };
   int tk_cur = tok(beg + qj), tv_cur[KPS];
 #pragma unroll
@@ -118,17 +134,18 @@ __global__ __launch_bounds__(256) void fmha_tokens_kernel(FmhaArgs a) {
     // segment of its row (thread qq holds d = 32i + 8qq .. +7), so each
     // segment is requested once (measured 5% faster than contiguous quarters,
     // whose loads touched four segments of every row per instruction).
+    // Rows two at a time: the query words of at most two rows are live (all
+    // of them at once would hold 16 registers per row).
     float part[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) part[r] = 0.f;
+    for (int r = 0; r < R; ++r) {
+      part[r] = 0.f;
 #pragma unroll
-    for (int i = 0; i < QW / 8; ++i) {
+      for (int i = 0; i < QW / 8; ++i) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int d2 = 16 * i + 4 * qq + w;
-#pragma unroll
-        for (int r = 0; r < R; ++r) part[r] = E::dot2(s_q[r][d2], kr[i][w], part[r]);
+        for (int w = 0; w < 4; ++w) part[r] = E::dot2(s_q[r][16 * i + 4 * qq + w], kr[i][w], part[r]);
       }
+      if (r & 1) __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {

@@ -216,7 +216,8 @@ size_t sparge_build_block_map_workspace(int b, int h, int s_q, int s_k, int d,
  *   lut_count must be NULL; lut_heads must be h_kv (one list per KV head,
  *   shared by its query heads).  The h_q / h_kv * s_q query rows of a KV
  *   head (at most 65536) are served in groups of 8, each group gathering the
- *   listed keys once.
+ *   listed keys once.  s_k rows of one (b, KV head) slice of K or V must
+ *   span less than 2^31 bytes (SPARGE_ERR_UNSUPPORTED otherwise).
  * In block mode lut_heads is h_q (one row per query head) or h_kv (a row
  * shared by the query heads of one KV head).
  *

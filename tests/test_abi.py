@@ -212,6 +212,8 @@ def _fmha(lib, **kw):
     (dict(bq=1, bk=1, cnt=FAKE, lh=2), ops.SPARGE_ERR_INVALID),
     (dict(bq=1, bk=1, cnt=None, lh=8), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(bq=1, bk=1, cnt=None, lh=2, sq=16385), ops.SPARGE_ERR_UNSUPPORTED),   # 65540 rows per KV head (limit 65536)
+    # a (b, KV head) slice of 2^20 rows of 1024-element stride spans 2^31 bytes
+    (dict(bq=1, bk=1, cnt=None, lh=2, sk=1 << 20, ks=_s3(1 << 31, 1 << 30, 1024)), ops.SPARGE_ERR_UNSUPPORTED),
 ])
 def test_fmha_rejections(lib, kw, status):
     st = _fmha(lib, **kw)

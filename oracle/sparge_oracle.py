@@ -570,7 +570,8 @@ def quantize_int8(x: np.ndarray, blk: int = 64):
 
 
 def dequantize_int8(codes: np.ndarray, scales: np.ndarray, blk: int = 64) -> np.ndarray:
-    """codes * scale of their block, in fp64 (exact: an int8 times an fp32)."""
+    """codes * scale of their block, in fp64 (exact: an int8 code, or an fp8
+    e4m3 code value, times an fp32)."""
     per_row = np.repeat(scales.astype(np.float64), blk, axis=2)[:, :, :codes.shape[2]]
     return codes.astype(np.float64) * per_row[..., None]
 
@@ -584,6 +585,105 @@ def block_sparse_attention_qk_int8(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     everything after them as in block_sparse_attention (V unquantised)."""
     cq, sq = quantize_int8(q)
     ck, sk = quantize_int8(k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[3])
+    return block_sparse_attention(dequantize_int8(cq, sq), dequantize_int8(ck, sk), v, lut, count,
+                                  scale=scale, lut_per_kv_head=lut_per_kv_head, causal=causal)
+
+
+E4M3_MAX = 448.0     # largest finite OCP fp8 e4m3 value: 1.75 * 2^8
+
+
+def round_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the OCP fp8 e4m3 grid, to nearest with ties to
+    even, saturating at +-448 (reading R29).
+
+    The grid: 4 exponent bits with bias 7 and 3 mantissa bits; normal values
+    (1 + m/8) * 2^e for e in [-6, 8] (the top binade stops at 1.75 * 2^8 =
+    448), subnormal values m * 2^-9.  In a binade [2^e, 2^(e+1)) the spacing
+    is 2^(e-3); below 2^-6 it is 2^-9.  Values from 464 up (past the
+    midpoint above 448) never arise in the quantisation, whose inputs stay
+    within 448 * (1 + 2^-23); they saturate here.  Returns float64 values on
+    the grid.
+    """
+    x = np.asarray(x, np.float64)
+    a = np.abs(x)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    step = np.where(a >= 2.0 ** -6, 2.0 ** (e - 3), 2.0 ** -9)
+    q = np.round(a / step) * step            # np.round: half to even on the exact quotient
+    q = np.minimum(q, E4M3_MAX)
+    return np.where(a > 0, np.sign(x) * q, 0.0)
+
+
+def e4m3_value(codes: np.ndarray) -> np.ndarray:
+    """Value of OCP fp8 e4m3 bytes (sign, 4 exponent bits with bias 7, 3
+    mantissa bits; exponent 0 is subnormal, 0x7F / 0xFF are NaN)."""
+    b = np.asarray(codes, np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    ex, m = (b >> 3) & 0xF, b & 0x7
+    mag = np.where(ex == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (ex - 7.0))
+    return np.where((b & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def e4m3_code(values: np.ndarray) -> np.ndarray:
+    """The OCP fp8 e4m3 byte of values already on the grid (zero as 0x00)."""
+    v = np.asarray(values, np.float64)
+    table = e4m3_value(np.arange(256, dtype=np.uint8))
+    table = np.where(np.isnan(table), np.inf, table)
+    table[0x80] = np.inf                         # -0 never produced: zero encodes as 0x00
+    idx = np.abs(table[None, :] - v.reshape(-1, 1)).argmin(axis=1)
+    if not np.all(table[idx] == v.reshape(-1)):
+        raise ValueError("values off the e4m3 grid")
+    return idx.astype(np.uint8).reshape(v.shape)
+
+
+def quantize_block_fp8(x_blk: np.ndarray):
+    """fp8 e4m3 codes of one block of tokens, with one fp32 scale.
+
+    CK page, "Status vs Upstream", not-yet-ported list: Q/K quantisation in
+    the pool kernel for a low-precision QK product in the attention kernel;
+    the aiter 6841 page runs fp8 Q/K recipes.  Reading R29, the fp8 twin of
+    R27: the 64-token pooling block, symmetric, scale = absmax / 448 and code =
+    round_e4m3(x * (448 / absmax)), each operation in fp32 (the division
+    correctly rounded), the last rounding to the e4m3 grid to nearest even.
+    An all-zero block has scale 0 and codes 0.  Returns (code values on the
+    e4m3 grid as float64, np.float32 scale).
+    """
+    x = np.asarray(x_blk, np.float32)
+    amax = np.float32(np.abs(x).max()) if x.size else np.float32(0)
+    if amax == 0:
+        return np.zeros(x.shape), np.float32(0)
+    inv = np.float32(E4M3_MAX) / amax
+    return round_e4m3(x * inv), amax / np.float32(E4M3_MAX)
+
+
+def quantize_fp8(x: np.ndarray, blk: int = 64):
+    """quantize_block_fp8 over every block of `blk` tokens of x [b, h, s, d]
+    (a partial last block quantises its own tokens, reading R1).  Returns code
+    values [b, h, s, d] (float64, on the e4m3 grid) and scales
+    [b, h, ceil(s / blk)] fp32."""
+    b, h, s, d = x.shape
+    nb = -(-s // blk)
+    codes = np.zeros((b, h, s, d))
+    scales = np.zeros((b, h, nb), np.float32)
+    for ib in range(b):
+        for ih in range(h):
+            for j in range(nb):
+                rows = slice(j * blk, (j + 1) * blk)
+                codes[ib, ih, rows], scales[ib, ih, j] = quantize_block_fp8(x[ib, ih, rows])
+    return codes, scales
+
+
+def block_sparse_attention_qk_fp8(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                                  lut: Optional[np.ndarray], count: Optional[np.ndarray],
+                                  scale: Optional[float] = None, lut_per_kv_head: bool = False,
+                                  causal: bool = False):
+    """block_sparse_attention with Q and K replaced by their fp8 e4m3 block
+    codes times their scales (reading R29): scores are
+    scale * sq * sk * (cq . ck), everything after them as in
+    block_sparse_attention (V unquantised)."""
+    cq, sq = quantize_fp8(q)
+    ck, sk = quantize_fp8(k)
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[3])
     return block_sparse_attention(dequantize_int8(cq, sq), dequantize_int8(ck, sk), v, lut, count,

@@ -16,7 +16,8 @@ The same line carries:
   * rows outside the headline: the b1 h8 s4096 bf16 config, the two-pass
     combine, the combine on headline-sized partials and the split-K decode
     (short launch sequences timed as HIP graphs, warm and with the caches
-    flushed), causal prefill, pv_threshold, a ragged length, bf16, int8 Q/K;
+    flushed), causal prefill, pv_threshold, a ragged length, bf16, int8 and
+    fp8 Q/K;
   * the fp64 CPU oracle timed on a bounded sample in a process pool.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
@@ -418,24 +419,34 @@ def extras(ops, synth, torch, steps, warmup):
         pairs=pairs, fmha_tflops_computed=pairs * F_BLK / median(t["fmha"]) / 1e9,
         mfma_frac_fmha=pairs * F_BLK / median(t["fmha"]) / 1e9 / PEAK_FP16_TFLOPS)
     del hb, bmb, ob
-    # int8 Q/K at the headline shape: the block map with the fused per-block
-    # quantisation, then the int8-QK sparse FMHA (V and P stay fp16).
+    # int8 and fp8 (e4m3) Q/K at the headline shape: the block map with the
+    # fused per-block quantisation, then the 8-bit-QK sparse FMHA (V and P
+    # stay fp16), against the fp16 FMHA on the same LUT.
     for topk in (0.4, 0.1):
         tk = [topk] * H
         q8 = ops.build_block_map(hc.q, hc.k, tk, hc.simthreshd1, quantize_int8=True)
+        f8 = ops.build_block_map(hc.q, hc.k, tk, hc.simthreshd1, quantize_fp8=True)
         t = interleaved({
             "map8": lambda: ops.build_block_map(hc.q, hc.k, tk, hc.simthreshd1, out=q8, quantize_int8=True),
+            "mapf8": lambda: ops.build_block_map(hc.q, hc.k, tk, hc.simthreshd1, out=f8, quantize_fp8=True),
             "fmha8": lambda: ops.sparse_fmha_fwd_qk_int8(q8["q_i8"], q8["q_i8_scale"], q8["k_i8"], q8["k_i8_scale"],
                                                          hc.v, q8["lut"], q8["count"], o=o, lse=l),
+            "fmhaf8": lambda: ops.sparse_fmha_fwd_qk_fp8(f8["q_fp8"], f8["q_fp8_scale"], f8["k_fp8"],
+                                                         f8["k_fp8_scale"], hc.v, f8["lut"], f8["count"], o=o, lse=l),
             "fmha16": lambda: ops.sparse_fmha_fwd(hc.q, hc.k, hc.v, q8["lut"], q8["count"], o=o, lse=l)},
             steps, warmup, torch)
         pairs = int(q8["count"].sum().item())
-        ft, ft16 = median(t["fmha8"]), median(t["fmha16"])
+        ft, ftf, ft16 = median(t["fmha8"]), median(t["fmhaf8"]), median(t["fmha16"])
         out[f"qk_int8_topk_{topk}"] = dict(
             workload=f"b2 h32 s16384 d128, int8 Q/K codes per 64-token block, fp16 V, topk {topk}",
             block_map_ms=median(t["map8"]), fmha_ms=ft, fmha_fp16_same_lut_ms=ft16,
             fmha_speedup_vs_fp16=ft16 / ft, pairs=pairs, fmha_tflops_computed=pairs * F_BLK / ft / 1e9)
-        del q8
+        out[f"qk_fp8_topk_{topk}"] = dict(
+            workload=f"b2 h32 s16384 d128, fp8 e4m3 Q/K codes per 64-token block, fp16 V, topk {topk}",
+            block_map_ms=median(t["mapf8"]), fmha_ms=ftf, fmha_fp16_same_lut_ms=ft16,
+            fmha_speedup_vs_fp16=ft16 / ftf, pairs=int(f8["count"].sum().item()),
+            fmha_tflops_computed=int(f8["count"].sum().item()) * F_BLK / ftf / 1e9)
+        del q8, f8
     del hc, bm, o, l, ws
     return out
 

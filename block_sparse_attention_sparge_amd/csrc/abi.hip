@@ -114,7 +114,7 @@ sparge_status scratch_for_current_device(void** out) {
 
 extern "C" {
 
-int sparge_abi_version(void) { return 6; }
+int sparge_abi_version(void) { return 7; }
 
 const char* sparge_last_error(void) { return g_error.c_str(); }
 
@@ -159,7 +159,7 @@ sparge_status block_map_impl(
   if (!aligned16(q) || !aligned16(k)) return fail(SPARGE_ERR_INVALID, "q/k must be 16-byte aligned");
   if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale))
     return fail(SPARGE_ERR_INVALID, "softmax_scale must be finite and >= 0");
-  if (flags & ~(SPARGE_FLAG_SMOOTH_K | SPARGE_FLAG_CAUSAL | SPARGE_FLAG_ATTN_SINK))
+  if (flags & ~(SPARGE_FLAG_SMOOTH_K | SPARGE_FLAG_CAUSAL | SPARGE_FLAG_ATTN_SINK | SPARGE_FLAG_QUANT_FP8))
     return fail(SPARGE_ERR_INVALID, "unknown flag bits 0x%x", flags);
   const bool causal = (flags & SPARGE_FLAG_CAUSAL) != 0;
   if (causal && s_q != s_k)
@@ -183,6 +183,8 @@ sparge_status block_map_impl(
     return fail(SPARGE_ERR_INVALID, "q_i8, q_i8_scale, k_i8 and k_i8_scale go together (all or none)");
   if (n_i8 && (!aligned16(q_i8) || !aligned16(k_i8)))
     return fail(SPARGE_ERR_INVALID, "q_i8/k_i8 must be 16-byte aligned");
+  if ((flags & SPARGE_FLAG_QUANT_FP8) && n_i8 != 4)
+    return fail(SPARGE_ERR_INVALID, "SPARGE_FLAG_QUANT_FP8 needs the four code outputs");
 
   PoolArgs pa;
   SelectArgs sa;
@@ -228,6 +230,7 @@ sparge_status block_map_impl(
   pa.km_chunks = lay.km_chunks;
   pa.km_scale = 1.0f / (float)s_k;
   pa.q_i8 = q_i8; pa.k_i8 = k_i8; pa.q_i8_scale = q_i8_scale; pa.k_i8_scale = k_i8_scale;
+  pa.quant_fp8 = (flags & SPARGE_FLAG_QUANT_FP8) ? 1 : 0;
 
   sa.q_mean = pa.q_mean; sa.k_mean = pa.k_mean; sa.sim_q = pa.sim_q; sa.k_sim = pa.k_sim;
   sa.sim_k = sim_k;
@@ -382,14 +385,19 @@ sparge_status sparse_fmha_fwd(const void* q, const void* k, const void* v, void*
                     "sparse_fmha token launch");
 }
 
-sparge_status sparse_fmha_fwd_qk_int8(const int8_t* q, const float* q_scale, const int8_t* k,
-                                      const float* k_scale, const void* v, void* o, float* lse,
-                                      sparge_dtype v_dt, sparge_dtype o_dt, int b, int h_q, int h_kv, int s_q,
-                                      int s_k, int d, const int64_t q_strides[3], const int64_t k_strides[3],
-                                      const int64_t v_strides[3], const int64_t o_strides[3], const int32_t* lut,
-                                      const int32_t* lut_count, int lut_row_len, int lut_heads,
-                                      float softmax_scale, unsigned flags, int num_splits,
-                                      int64_t o_split_stride, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both 8-bit Q/K entry points: int8 codes, or fp8 e4m3 codes (fp8).
+sparge_status fmha_qk8_impl(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                            const void* v, void* o, float* lse, sparge_dtype v_dt, sparge_dtype o_dt, int b,
+                            int h_q, int h_kv, int s_q, int s_k, int d, const int64_t q_strides[3],
+                            const int64_t k_strides[3], const int64_t v_strides[3], const int64_t o_strides[3],
+                            const int32_t* lut, const int32_t* lut_count, int lut_row_len, int lut_heads,
+                            float softmax_scale, unsigned flags, int num_splits, int64_t o_split_stride,
+                            bool fp8, void* stream) {
+  const char* entry = fp8 ? "sparse_fmha_fwd_qk_fp8" : "sparse_fmha_fwd_qk_int8";
   if (!q || !k || !v || !o || !q_scale || !k_scale)
     return fail(SPARGE_ERR_INVALID, "q, q_scale, k, k_scale, v and o must be non-null");
   if (!is_half(v_dt)) return fail(SPARGE_ERR_UNSUPPORTED, "v dtype must be F16 or BF16");
@@ -415,7 +423,7 @@ sparge_status sparse_fmha_fwd_qk_int8(const int8_t* q, const float* q_scale, con
   if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale))
     return fail(SPARGE_ERR_INVALID, "softmax_scale must be finite and >= 0");
   if (flags & ~SPARGE_FLAG_CAUSAL)
-    return fail(SPARGE_ERR_INVALID, "sparse_fmha_fwd_qk_int8 takes only SPARGE_FLAG_CAUSAL (flags 0x%x)", flags);
+    return fail(SPARGE_ERR_INVALID, "%s takes only SPARGE_FLAG_CAUSAL (flags 0x%x)", entry, flags);
   const bool causal = (flags & SPARGE_FLAG_CAUSAL) != 0;
   if (causal && s_q != s_k)
     return fail(SPARGE_ERR_UNSUPPORTED, "causal attention needs s_q = s_k (got %d, %d)", s_q, s_k);
@@ -448,8 +456,37 @@ sparge_status sparse_fmha_fwd_qk_int8(const int8_t* q, const float* q_scale, con
   a.tok_groups = 1;
   a.nqt = (s_q + 63) / 64;
   a.nkb = (s_k + 63) / 64;
-  return hip_status(launch_fmha_qk8(a, v_dt, o_dt, d, reinterpret_cast<hipStream_t>(stream)),
-                    "sparse_fmha_qk_int8 launch");
+  return hip_status(launch_fmha_qk8(a, v_dt, o_dt, d, fp8, reinterpret_cast<hipStream_t>(stream)), entry);
+}
+
+}  // namespace
+
+extern "C" {
+
+sparge_status sparse_fmha_fwd_qk_int8(const int8_t* q, const float* q_scale, const int8_t* k,
+                                      const float* k_scale, const void* v, void* o, float* lse,
+                                      sparge_dtype v_dt, sparge_dtype o_dt, int b, int h_q, int h_kv, int s_q,
+                                      int s_k, int d, const int64_t q_strides[3], const int64_t k_strides[3],
+                                      const int64_t v_strides[3], const int64_t o_strides[3], const int32_t* lut,
+                                      const int32_t* lut_count, int lut_row_len, int lut_heads,
+                                      float softmax_scale, unsigned flags, int num_splits,
+                                      int64_t o_split_stride, void* stream) {
+  return fmha_qk8_impl(q, q_scale, k, k_scale, v, o, lse, v_dt, o_dt, b, h_q, h_kv, s_q, s_k, d, q_strides,
+                       k_strides, v_strides, o_strides, lut, lut_count, lut_row_len, lut_heads, softmax_scale,
+                       flags, num_splits, o_split_stride, false, stream);
+}
+
+sparge_status sparse_fmha_fwd_qk_fp8(const uint8_t* q, const float* q_scale, const uint8_t* k,
+                                     const float* k_scale, const void* v, void* o, float* lse,
+                                     sparge_dtype v_dt, sparge_dtype o_dt, int b, int h_q, int h_kv, int s_q,
+                                     int s_k, int d, const int64_t q_strides[3], const int64_t k_strides[3],
+                                     const int64_t v_strides[3], const int64_t o_strides[3], const int32_t* lut,
+                                     const int32_t* lut_count, int lut_row_len, int lut_heads,
+                                     float softmax_scale, unsigned flags, int num_splits,
+                                     int64_t o_split_stride, void* stream) {
+  return fmha_qk8_impl(q, q_scale, k, k_scale, v, o, lse, v_dt, o_dt, b, h_q, h_kv, s_q, s_k, d, q_strides,
+                       k_strides, v_strides, o_strides, lut, lut_count, lut_row_len, lut_heads, softmax_scale,
+                       flags, num_splits, o_split_stride, true, stream);
 }
 
 sparge_status attn_combine(const void* o_parts, sparge_dtype part_dt, const float* lse_parts, int n_parts,

@@ -186,7 +186,11 @@ __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
   if constexpr (QUANT) {
     // int8 codes of the block as given (not smoothed): scale = absmax / 127,
     // code = round-half-even(x * (127 / absmax)), both divisions correctly
-    // rounded in fp32; an all-zero block gets scale 0 and codes 0.
+    // rounded in fp32; an all-zero block gets scale 0 and codes 0.  With
+    // quant_fp8 the codes are OCP fp8 e4m3 instead: scale = absmax / 448 and
+    // code = x * (448 / absmax) rounded to the e4m3 grid, to nearest even
+    // (v_cvt_pk_fp8_f32; its inputs stay within 448 * (1 + 2^-23), which
+    // rounds to 448).
     // Convert again below rather than keep the 8 NP floats of the statistics
     // loop alive (the compiler would otherwise reuse them).
 #pragma unroll
@@ -202,7 +206,9 @@ __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, m, kWave));
     const float amax = E::lo(amax_bits);
-    const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+    const bool fp8 = a.quant_fp8 != 0;
+    const float qmax = fp8 ? 448.0f : 127.0f;
+    const float inv = amax > 0.f ? qmax / amax : 0.f;
     int8_t* codes = (is_k ? a.k_i8 : a.q_i8) + (bh * ntok + blk * 64 + t0) * (int64_t)D + c * 8;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
@@ -210,18 +216,26 @@ __global__ __launch_bounds__(256) void pool_sim_kernel(PoolArgs a) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         uint32_t acc = 0;
+        if (fp8) {
+          // Element j of the four goes to byte j: bytes 0-1 from the low
+          // word of the conversion, bytes 2-3 from the high word.
+          const uint32_t w0 = raw[p][2 * half], w1 = raw[p][2 * half + 1];
+          acc = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(E::lo(w0) * inv, E::hi(w0) * inv, 0, false);
+          acc = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(E::lo(w1) * inv, E::hi(w1) * inv, (int)acc, true);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t wv = raw[p][2 * half + j / 2];
-          const float x = (j & 1) ? E::hi(wv) : E::lo(wv);
-          const float t = fminf(fmaxf(rintf(x * inv), -127.f), 127.f);
-          acc |= ((uint32_t)(int)t & 0xFFu) << (8 * j);
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t wv = raw[p][2 * half + j / 2];
+            const float x = (j & 1) ? E::hi(wv) : E::lo(wv);
+            const float t = fminf(fmaxf(rintf(x * inv), -127.f), 127.f);
+            acc |= ((uint32_t)(int)t & 0xFFu) << (8 * j);
+          }
         }
         wd[half] = acc;
       }
       if (p * TPP + t0 < cnt) *reinterpret_cast<u32x2*>(codes + (int64_t)(p * TPP) * D) = u32x2{wd[0], wd[1]};
     }
-    if (lane == 0) (is_k ? a.k_i8_scale : a.q_i8_scale)[bh * nb + blk] = amax / 127.0f;
+    if (lane == 0) (is_k ? a.k_i8_scale : a.q_i8_scale)[bh * nb + blk] = amax / qmax;
   }
 }
 

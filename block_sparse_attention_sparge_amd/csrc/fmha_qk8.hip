@@ -23,6 +23,16 @@
 // repeats its last row and stores only its own rows; the MASKED kernel
 // (causal, or a ragged K sequence) repeats the last K/V row in a partial last
 // block and removes keys by position.
+//
+// With fp8 (e4m3) codes instead of int8 (the FP8 instantiation), S^T runs on
+// v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales: two MFMAs per block for
+// d = 128, each lane feeding 32 consecutive codes of its K row and of its Q
+// row (any assignment of the 64 codes of a step to the two half-waves gives
+// the same product as long as K and Q use the same one), accumulated in fp32.
+// The codes occupy the same bytes as int8 codes, so the loads, the LDS layout
+// and everything after the scores are shared.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "common.h"
 #include "kernels.h"
@@ -30,11 +40,20 @@
 namespace sparge {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ i32x16 mfma_i8(const u32x4& a, const u32x4& b, const i32x16& c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c,
                                                0, 0, 0);
+}
+
+// 32x32x64 fp8 (e4m3, format 0) MFMA with unit E8M0 scales (127 = 2^0).
+__device__ __forceinline__ floatx16 mfma_f8(const u32x4& a0, const u32x4& a1, const u32x4& b0, const u32x4& b1,
+                                            const floatx16& c) {
+  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
 // K rows are d bytes: GK 16-byte granules.  Row r's granule g sits in slot
@@ -45,7 +64,7 @@ __device__ __forceinline__ int k8_swz(int r) {
   return (r / (16 / GK)) % GK;
 }
 
-template <class E, int D, bool OUT_F32, bool MASKED>
+template <class E, int D, bool OUT_F32, bool MASKED, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fmha_qk8_kernel(FmhaArgs a) {
   typedef typename E::T T;
@@ -203,7 +222,8 @@ void fmha_qk8_kernel(FmhaArgs a) {
   wait_dma();
   __syncthreads();
   // Q^T codes (B operand): lane (query l32, half hl) holds d = 32kk + 16hl .. +15
-  // of tile row 32 qh + l32.
+  // of tile row 32 qh + l32 (for fp8, k-step kk / 2 takes granules 2kk + hl
+  // and 2kk + 2 + hl: codes 64(kk/2) + 16hl .. +15 and + 32 .. +47).
   u32x4 qf[NKK];
   {
     const int qrow = 32 * qh + l32, qsw = k8_swz<GK>(qrow);
@@ -256,12 +276,19 @@ void fmha_qk8_kernel(FmhaArgs a) {
     // SIMD, the one starting a block goes first; measured 1.8% faster at topk
     // 0.4 and 2.5% at topk 0.1, bit-identical.  The fp16 / bf16 kernel, with
     // twice the S^T MFMAs, gains instead from raising it for PV).
-    i32x16 si = i32x16{};
+    // fp8: step j of 64 codes pairs the reads kk = 2j and 2j + 1.
+    typedef typename std::conditional<FP8, floatx16, i32x16>::type SAcc;
+    SAcc si = SAcc{};
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (FP8) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) si = mfma_i8(kf[kk], qf[kk], si);
+      for (int j = 0; j < NKK / 2; ++j) si = mfma_f8(kf[2 * j], kf[2 * j + 1], qf[2 * j], qf[2 * j + 1], si);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) si = mfma_i8(kf[kk], qf[kk], si);
+    }
     read_vt(1);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
@@ -413,24 +440,31 @@ void fmha_qk8_kernel(FmhaArgs a) {
   }
 }
 
-template <class E, int D>
+template <class E, int D, bool FP8>
 static hipError_t launch_qk8_t(const FmhaArgs& a, bool out_f32, hipStream_t st) {
   const int64_t G = (int64_t)a.nqt * a.hq * a.b * a.splits;
   const dim3 grid((unsigned)(((G + 7) / 8) * 8));
   if (a.causal || a.sk % 64) {
-    if (out_f32) hipLaunchKernelGGL((fmha_qk8_kernel<E, D, true, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((fmha_qk8_kernel<E, D, false, true>), grid, dim3(256), 0, st, a);
+    if (out_f32) hipLaunchKernelGGL((fmha_qk8_kernel<E, D, true, true, FP8>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((fmha_qk8_kernel<E, D, false, true, FP8>), grid, dim3(256), 0, st, a);
   } else {
-    if (out_f32) hipLaunchKernelGGL((fmha_qk8_kernel<E, D, true, false>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((fmha_qk8_kernel<E, D, false, false>), grid, dim3(256), 0, st, a);
+    if (out_f32) hipLaunchKernelGGL((fmha_qk8_kernel<E, D, true, false, FP8>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((fmha_qk8_kernel<E, D, false, false, FP8>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_fmha_qk8(const FmhaArgs& a, sparge_dtype v_dt, sparge_dtype o_dt, int d, hipStream_t st) {
+template <bool FP8>
+static hipError_t launch_qk8_c(const FmhaArgs& a, sparge_dtype v_dt, bool f32, int d, hipStream_t st) {
+  if (v_dt == SPARGE_F16)
+    return d == 128 ? launch_qk8_t<F16, 128, FP8>(a, f32, st) : launch_qk8_t<F16, 64, FP8>(a, f32, st);
+  return d == 128 ? launch_qk8_t<BF16, 128, FP8>(a, f32, st) : launch_qk8_t<BF16, 64, FP8>(a, f32, st);
+}
+
+hipError_t launch_fmha_qk8(const FmhaArgs& a, sparge_dtype v_dt, sparge_dtype o_dt, int d, bool fp8,
+                           hipStream_t st) {
   const bool f32 = o_dt == SPARGE_F32;
-  if (v_dt == SPARGE_F16) return d == 128 ? launch_qk8_t<F16, 128>(a, f32, st) : launch_qk8_t<F16, 64>(a, f32, st);
-  return d == 128 ? launch_qk8_t<BF16, 128>(a, f32, st) : launch_qk8_t<BF16, 64>(a, f32, st);
+  return fp8 ? launch_qk8_c<true>(a, v_dt, f32, d, st) : launch_qk8_c<false>(a, v_dt, f32, d, st);
 }
 
 }  // namespace sparge

@@ -34,6 +34,7 @@ struct PoolArgs {
   int8_t* k_i8;
   float* q_i8_scale;
   float* k_i8_scale;
+  int quant_fp8;     // the codes are fp8 e4m3 bytes (scale absmax / 448), not int8
   float thr[SPARGE_MAX_HEADS];
 };
 
@@ -103,7 +104,7 @@ hipError_t launch_pool_sim(const PoolArgs& a, sparge_dtype dt, int d, hipStream_
 hipError_t launch_score_select(const SelectArgs& a, int d, hipStream_t st);
 hipError_t launch_fmha_block(const FmhaArgs& a, sparge_dtype dt, sparge_dtype o_dt, int d,
                              hipStream_t st);
-hipError_t launch_fmha_qk8(const FmhaArgs& a, sparge_dtype v_dt, sparge_dtype o_dt, int d,
+hipError_t launch_fmha_qk8(const FmhaArgs& a, sparge_dtype v_dt, sparge_dtype o_dt, int d, bool fp8,
                            hipStream_t st);
 hipError_t launch_fmha_tokens(const FmhaArgs& a, sparge_dtype dt, sparge_dtype o_dt, int d,
                               int rows_per_group, hipStream_t st);

@@ -22,8 +22,8 @@ LIB_PATH = os.path.join(_PKG, "libsparge.so")
 
 SPARGE_OK, SPARGE_ERR_INVALID, SPARGE_ERR_UNSUPPORTED, SPARGE_ERR_HIP = 0, 1, 2, 3
 SPARGE_F16, SPARGE_BF16, SPARGE_F32 = 0, 1, 2
-SPARGE_FLAG_SMOOTH_K, SPARGE_FLAG_CAUSAL, SPARGE_FLAG_ATTN_SINK = 1, 2, 4
-ABI_VERSION = 6
+SPARGE_FLAG_SMOOTH_K, SPARGE_FLAG_CAUSAL, SPARGE_FLAG_ATTN_SINK, SPARGE_FLAG_QUANT_FP8 = 1, 2, 4, 8
+ABI_VERSION = 7
 NOALLOC_SCRATCH_BYTES = 32 << 20
 MAX_HEADS = 128
 MAX_KBLOCKS = 1024
@@ -31,7 +31,7 @@ MAX_KBLOCKS = 1024
 EXPORTED_SYMBOLS = (
     "sparge_abi_version", "sparge_last_error", "sparge_build_block_map",
     "sparge_build_block_map_workspace", "sparse_fmha_fwd", "sparse_fmha_fwd_qk_int8", "attn_combine",
-    "sparge_validate_lut", "sparge_build_block_map_noalloc",
+    "sparge_validate_lut", "sparge_build_block_map_noalloc", "sparse_fmha_fwd_qk_fp8",
 )
 
 
@@ -91,6 +91,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         lib.sparse_fmha_fwd_qk_int8.argtypes = [
             _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
             _I64x3, _I64x3, _I64x3, _I64x3, _p, _p, _i, _i, _f, _u, _i, _i64, _p]
+        lib.sparse_fmha_fwd_qk_fp8.restype = _i
+        lib.sparse_fmha_fwd_qk_fp8.argtypes = lib.sparse_fmha_fwd_qk_int8.argtypes
         lib.attn_combine.restype = _i
         lib.attn_combine.argtypes = [_p, _i, _p, _i, _i, _i, _i, _i, _i64, _p, _i, _p, _p]
         lib.sparge_validate_lut.restype = _i
@@ -157,9 +159,10 @@ def _f32_array(vals: Optional[Sequence[float]], n: int, name: str):
     return (ctypes.c_float * n)(*vals)
 
 
-def _flags(smooth_k: bool = False, causal: bool = False, attention_sink: bool = False) -> int:
+def _flags(smooth_k: bool = False, causal: bool = False, attention_sink: bool = False,
+           quant_fp8: bool = False) -> int:
     return ((SPARGE_FLAG_SMOOTH_K if smooth_k else 0) | (SPARGE_FLAG_CAUSAL if causal else 0) |
-            (SPARGE_FLAG_ATTN_SINK if attention_sink else 0))
+            (SPARGE_FLAG_ATTN_SINK if attention_sink else 0) | (SPARGE_FLAG_QUANT_FP8 if quant_fp8 else 0))
 
 
 def _check_lut_rows(lut, count, b, nq):
@@ -202,27 +205,8 @@ def build_block_map(q: torch.Tensor, k: torch.Tensor, topk, simthreshd1, cdfthre
                     softmax_scale: float = 0.0, blk_q: int = 64, blk_k: int = 64,
                     return_debug: bool = False, workspace: Optional[torch.Tensor] = None,
                     out: Optional[dict] = None, smooth_k: bool = False, causal: bool = False,
-                    attention_sink: bool = False, quantize_int8: bool = False) -> dict:
-    return _block_map(q, k, topk, simthreshd1, cdfthreshd, softmax_scale, blk_q, blk_k, return_debug,
-                      workspace, out, smooth_k, causal, attention_sink, quantize_int8, noalloc=False)
-
-
-def build_block_map_noalloc(q: torch.Tensor, k: torch.Tensor, topk, simthreshd1, cdfthreshd=None,
-                            softmax_scale: float = 0.0, blk_q: int = 64, blk_k: int = 64,
-                            return_debug: bool = False, out: Optional[dict] = None,
-                            smooth_k: bool = False, causal: bool = False,
-                            attention_sink: bool = False, quantize_int8: bool = False) -> dict:
-    """build_block_map through sparge_build_block_map_noalloc: the library's
-    static per-GPU scratch (NOALLOC_SCRATCH_BYTES) replaces the workspace.
-    Outputs not given in `out` are still allocated here by torch; pass them
-    all in `out` for a call that allocates nothing (e.g. under graph capture).
-    Calls whose work overlaps on one GPU share the scratch and race."""
-    return _block_map(q, k, topk, simthreshd1, cdfthreshd, softmax_scale, blk_q, blk_k, return_debug,
-                      None, out, smooth_k, causal, attention_sink, quantize_int8, noalloc=True)
-
-
-def _block_map(q, k, topk, simthreshd1, cdfthreshd, softmax_scale, blk_q, blk_k, return_debug,
-               workspace, out, smooth_k, causal, attention_sink, quantize_int8, noalloc) -> dict:
+                    attention_sink: bool = False, quantize_int8: bool = False,
+                    quantize_fp8: bool = False) -> dict:
     """Stage 1 (sparge_build_block_map).  q [b, h, s_q, d], k [b, h_kv, s_k, d]
     with h a multiple of h_kv (query head j reads K head j // (h / h_kv)).
 
@@ -235,8 +219,34 @@ def _block_map(q, k, topk, simthreshd1, cdfthreshd, softmax_scale, blk_q, blk_k,
     per-block int8 codes 'q_i8' [b, h, s_q, d], 'k_i8' [b, h_kv, s_k, d] and their
     scales 'q_i8_scale' [b, h, nq], 'k_i8_scale' [b, h_kv, nk]; 'k_mean' is
     [b, h_kv, nk, d] and 'sim_k' [b, h, nk] (the K gate as each query head
-    sees it).
+    sees it).  quantize_fp8 returns fp8 e4m3 codes instead (uint8 bytes) under
+    'q_fp8', 'k_fp8' with 'q_fp8_scale', 'k_fp8_scale' (SPARGE_FLAG_QUANT_FP8).
     """
+    return _block_map(q, k, topk, simthreshd1, cdfthreshd, softmax_scale, blk_q, blk_k, return_debug,
+                      workspace, out, smooth_k, causal, attention_sink, quantize_int8, noalloc=False,
+                      quantize_fp8=quantize_fp8)
+
+
+def build_block_map_noalloc(q: torch.Tensor, k: torch.Tensor, topk, simthreshd1, cdfthreshd=None,
+                            softmax_scale: float = 0.0, blk_q: int = 64, blk_k: int = 64,
+                            return_debug: bool = False, out: Optional[dict] = None,
+                            smooth_k: bool = False, causal: bool = False,
+                            attention_sink: bool = False, quantize_int8: bool = False,
+                            quantize_fp8: bool = False) -> dict:
+    """build_block_map through sparge_build_block_map_noalloc: the library's
+    static per-GPU scratch (NOALLOC_SCRATCH_BYTES) replaces the workspace.
+    Outputs not given in `out` are still allocated here by torch; pass them
+    all in `out` for a call that allocates nothing (e.g. under graph capture).
+    Calls whose work overlaps on one GPU share the scratch and race."""
+    return _block_map(q, k, topk, simthreshd1, cdfthreshd, softmax_scale, blk_q, blk_k, return_debug,
+                      None, out, smooth_k, causal, attention_sink, quantize_int8, noalloc=True,
+                      quantize_fp8=quantize_fp8)
+
+
+def _block_map(q, k, topk, simthreshd1, cdfthreshd, softmax_scale, blk_q, blk_k, return_debug,
+               workspace, out, smooth_k, causal, attention_sink, quantize_int8, noalloc,
+               quantize_fp8=False) -> dict:
+    """The implementation of build_block_map and build_block_map_noalloc."""
     lib = load_library()
     dev = _on_gpu(q, k)
     b, h, s_q, d = q.shape
@@ -266,22 +276,30 @@ def _block_map(q, k, topk, simthreshd1, cdfthreshd, softmax_scale, blk_q, blk_k,
                    q_mean=get("q_mean", (b, h, nq, d), torch.float32),
                    k_mean=get("k_mean", (b, h_kv, nk, d), torch.float32))
     qz = {}
+    if quantize_int8 and quantize_fp8:
+        raise SpargeError(SPARGE_ERR_INVALID, "quantize_int8 and quantize_fp8 exclude each other")
     if quantize_int8:
         qz = dict(q_i8=get("q_i8", (b, h, s_q, d), torch.int8),
                   q_i8_scale=get("q_i8_scale", (b, h, nq), torch.float32),
                   k_i8=get("k_i8", (b, h_kv, s_k, d), torch.int8),
                   k_i8_scale=get("k_i8_scale", (b, h_kv, nk), torch.float32))
-        for key in ("q_i8", "k_i8"):
-            if not qz[key].is_contiguous():
-                raise SpargeError(SPARGE_ERR_INVALID, f"{key} must be contiguous")
+    if quantize_fp8:
+        qz = dict(q_fp8=get("q_fp8", (b, h, s_q, d), torch.uint8),
+                  q_fp8_scale=get("q_fp8_scale", (b, h, nq), torch.float32),
+                  k_fp8=get("k_fp8", (b, h_kv, s_k, d), torch.uint8),
+                  k_fp8_scale=get("k_fp8_scale", (b, h_kv, nk), torch.float32))
+    for key in ("q_i8", "k_i8", "q_fp8", "k_fp8"):
+        if key in qz and not qz[key].is_contiguous():
+            raise SpargeError(SPARGE_ERR_INVALID, f"{key} must be contiguous")
+    codes = ("q_fp8", "q_fp8_scale", "k_fp8", "k_fp8_scale") if quantize_fp8 else \
+        ("q_i8", "q_i8_scale", "k_i8", "k_i8_scale")
     args = (_ptr(q), _ptr(k), _dt(q.dtype), b, h, h_kv, s_q, s_k, d, _strides(q), _strides(k), blk_q, blk_k,
             _f32_array(topk, h, "topk"), _f32_array(cdfthreshd, h, "cdfthreshd"),
             _f32_array(simthreshd1, h, "simthreshd1"), float(softmax_scale),
-            _flags(smooth_k=smooth_k, causal=causal, attention_sink=attention_sink),
+            _flags(smooth_k=smooth_k, causal=causal, attention_sink=attention_sink, quant_fp8=quantize_fp8),
             _ptr(lut), _ptr(count), _ptr(dbg.get("bitmap")), _ptr(dbg.get("prob")),
             _ptr(dbg.get("sim_q")), _ptr(dbg.get("sim_k")), _ptr(dbg.get("q_mean")),
-            _ptr(dbg.get("k_mean")), _ptr(qz.get("q_i8")), _ptr(qz.get("q_i8_scale")),
-            _ptr(qz.get("k_i8")), _ptr(qz.get("k_i8_scale")))
+            _ptr(dbg.get("k_mean")), *(_ptr(qz.get(key)) for key in codes))
     if noalloc:
         _check(lib.sparge_build_block_map_noalloc(*args, _stream(dev)))
         res = dict(lut=lut, count=count)
@@ -371,7 +389,7 @@ def sparse_fmha_fwd_qk_int8(q_i8: torch.Tensor, q_scale: torch.Tensor, k_i8: tor
                             softmax_scale: float = 0.0, num_splits: int = 1,
                             out_dtype: Optional[torch.dtype] = None, o: Optional[torch.Tensor] = None,
                             lse: Optional[torch.Tensor] = None, return_lse: bool = True,
-                            causal: bool = False):
+                            causal: bool = False, _fp8: bool = False):
     """Stage 2 on int8 Q/K codes (sparse_fmha_fwd_qk_int8), block mode.
 
     q_i8 [b, h_q, s_q, d] int8 with q_scale [b, h_q, ceil(s_q/64)]; k_i8 [b, h_kv,
@@ -385,8 +403,9 @@ def sparse_fmha_fwd_qk_int8(q_i8: torch.Tensor, q_scale: torch.Tensor, k_i8: tor
         raise SpargeError(SPARGE_ERR_INVALID, f"q_i8 must be [b, h_q, s_q, d], got {tuple(q_i8.shape)}")
     b, h_q, s_q, d = q_i8.shape
     h_kv, s_k = k_i8.shape[1], k_i8.shape[2]
-    if q_i8.dtype != torch.int8 or k_i8.dtype != torch.int8:
-        raise SpargeError(SPARGE_ERR_INVALID, "q_i8 and k_i8 must be int8")
+    code_dt = torch.uint8 if _fp8 else torch.int8
+    if q_i8.dtype != code_dt or k_i8.dtype != code_dt:
+        raise SpargeError(SPARGE_ERR_INVALID, f"the Q and K codes must be {code_dt}")
     _check_attn_shapes(q_i8, k_i8, v, o, lse, num_splits)
     for name, t, shape in (("q_scale", q_scale, (b, h_q, -(-s_q // 64))), ("k_scale", k_scale, (b, h_kv, -(-s_k // 64)))):
         if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shape:
@@ -411,13 +430,24 @@ def sparse_fmha_fwd_qk_int8(q_i8: torch.Tensor, q_scale: torch.Tensor, k_i8: tor
         _check_lut_rows(lut, count, b, -(-s_q // 64))
     if count is not None and (count.dtype != torch.int32 or not count.is_contiguous()):
         raise SpargeError(SPARGE_ERR_INVALID, "count must be contiguous int32")
-    st = lib.sparse_fmha_fwd_qk_int8(
+    entry = lib.sparse_fmha_fwd_qk_fp8 if _fp8 else lib.sparse_fmha_fwd_qk_int8
+    st = entry(
         _ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale), _ptr(v), _ptr(o), _ptr(lse),
         _dt(v.dtype), _dt(o.dtype), b, h_q, h_kv, s_q, s_k, d, _strides(q_i8), _strides(k_i8),
         _strides(v), _strides(o4), _ptr(lut), _ptr(count), lut_row_len, lut_heads,
         float(softmax_scale), _flags(causal=causal), int(num_splits), int(split_stride), _stream(dev))
     _check(st)
     return o, lse
+
+
+def sparse_fmha_fwd_qk_fp8(q_fp8: torch.Tensor, q_scale: torch.Tensor, k_fp8: torch.Tensor,
+                           k_scale: torch.Tensor, v: torch.Tensor,
+                           lut: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None, **kw):
+    """Stage 2 on fp8 (e4m3) Q/K codes (sparse_fmha_fwd_qk_fp8), block mode:
+    q_fp8 / k_fp8 uint8 e4m3 bytes with their per-block scales, as
+    build_block_map(..., quantize_fp8=True) returns them.  Other arguments as
+    sparse_fmha_fwd_qk_int8.  Returns (o, lse)."""
+    return sparse_fmha_fwd_qk_int8(q_fp8, q_scale, k_fp8, k_scale, v, lut, count, _fp8=True, **kw)
 
 
 def dense_fmha_fwd(q, k, v, softmax_scale: float = 0.0, **kw):

@@ -68,13 +68,14 @@ typedef enum {
 #define SPARGE_FLAG_SMOOTH_K 1u   /* block map: pool and gate k - mean_s(k)        */
 #define SPARGE_FLAG_CAUSAL 2u     /* block map and block-mode FMHA: causal masks   */
 #define SPARGE_FLAG_ATTN_SINK 4u  /* block map: K block 0 selected in every row    */
+#define SPARGE_FLAG_QUANT_FP8 8u  /* block map: the Q/K codes are fp8 e4m3, not int8 */
 
 /* Device scratch held by sparge_build_block_map_noalloc on each GPU it runs
  * on (32 MiB: enough for the block map of b2 h32 s16384 d128, which needs
  * 16.6 MiB). */
 #define SPARGE_NOALLOC_SCRATCH_BYTES (32u << 20)
 
-/* Library ABI version (this header: 6). */
+/* Library ABI version (this header: 7). */
 int sparge_abi_version(void);
 
 /* Message for the last failed call on this thread ("" if none). */
@@ -116,6 +117,10 @@ const char* sparge_last_error(void);
  *   CAUSAL     needs s_q = s_k.  S[kb] = -inf for kb > qb; n is clamped to
  *              qb + 1; "all kb" and the forced blocks are limited to kb <= qb.
  *   ATTN_SINK  kb = 0 is added to every row.
+ *   QUANT_FP8  needs the four code outputs: they receive OCP fp8 e4m3 codes
+ *              (bytes) instead of int8, with scale = absmax / 448 and code =
+ *              x * (448 / absmax) rounded to the e4m3 grid to nearest even,
+ *              each step in fp32.  Input to sparse_fmha_fwd_qk_fp8.
  *
  * Inputs:
  *   topk        host float[h]; > 0 selects top-k mode for that head, must be <= 1.
@@ -280,6 +285,26 @@ sparge_status sparse_fmha_fwd(
  */
 sparge_status sparse_fmha_fwd_qk_int8(
     const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
+    const void* v, void* o, float* lse, sparge_dtype v_dt, sparge_dtype o_dt,
+    int b, int h_q, int h_kv, int s_q, int s_k, int d,
+    const int64_t q_strides[3], const int64_t k_strides[3],
+    const int64_t v_strides[3], const int64_t o_strides[3],
+    const int32_t* lut, const int32_t* lut_count, int lut_row_len, int lut_heads,
+    float softmax_scale, unsigned flags, int num_splits, int64_t o_split_stride,
+    void* stream);
+
+/*
+ * Stage 2 with fp8 (e4m3) Q and K codes, as sparge_build_block_map writes
+ * them with SPARGE_FLAG_QUANT_FP8 (CK page, "Status vs Upstream", not-yet-ported
+ * list: Q/K quantisation in the pool kernel for a low-precision QK product;
+ * aiter 6841 page: fp8 Q/K recipes).  Arguments, layouts, limits and errors
+ * as sparse_fmha_fwd_qk_int8, with q and k holding OCP e4m3 bytes (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits); every score is
+ *   s_j = scale * q_scale[tile] * k_scale[block of j] * <q_code_i, k_code_j>,
+ * the code product accumulated in fp32 by the fp8 MFMA.
+ */
+sparge_status sparse_fmha_fwd_qk_fp8(
+    const uint8_t* q, const float* q_scale, const uint8_t* k, const float* k_scale,
     const void* v, void* o, float* lse, sparge_dtype v_dt, sparge_dtype o_dt,
     int b, int h_q, int h_kv, int s_q, int s_k, int d,
     const int64_t q_strides[3], const int64_t k_strides[3],

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert lib.sparge_abi_version() == ops.ABI_VERSION == 6
+    assert lib.sparge_abi_version() == ops.ABI_VERSION == 7
 
 
 def _s3(a, b, c):
@@ -117,6 +117,7 @@ def _bm(lib, **kw):
     (dict(q8=FAKE), ops.SPARGE_ERR_INVALID),                                      # int8 outputs: all or none
     (dict(q8=FAKE, q8s=FAKE, k8=FAKE), ops.SPARGE_ERR_INVALID),
     (dict(q8=FAKE + 8, q8s=FAKE, k8=FAKE, k8s=FAKE), ops.SPARGE_ERR_INVALID),     # misaligned codes
+    (dict(flags=ops.SPARGE_FLAG_QUANT_FP8), ops.SPARGE_ERR_INVALID),              # fp8 codes need the outputs
 ])
 def test_block_map_rejections(lib, kw, status):
     st = _bm(lib, **kw)
@@ -220,14 +221,14 @@ def test_fmha_rejections(lib, kw, status):
     assert st == status, _err(lib)
 
 
-def _fmha8(lib, **kw):
+def _fmha8(lib, entry="sparse_fmha_fwd_qk_int8", **kw):
     a = dict(q=FAKE, qsc=FAKE, k=FAKE, ksc=FAKE, v=FAKE, o=FAKE, lse=FAKE, vdt=ops.SPARGE_BF16,
              odt=ops.SPARGE_BF16, b=1, hq=8, hkv=2, sq=512, sk=512, d=128,
              qs=_s3(8 * 512 * 128, 512 * 128, 128), ks=_s3(2 * 512 * 128, 512 * 128, 128),
              vs=_s3(2 * 512 * 128, 512 * 128, 128), os=_s3(8 * 512 * 128, 512 * 128, 128),
              lut=FAKE, cnt=FAKE, L=8, lh=8, scale=0.0, flags=0, splits=1, sst=0)
     a.update(kw)
-    return lib.sparse_fmha_fwd_qk_int8(a["q"], a["qsc"], a["k"], a["ksc"], a["v"], a["o"], a["lse"],
+    return getattr(lib, entry)(a["q"], a["qsc"], a["k"], a["ksc"], a["v"], a["o"], a["lse"],
                                        a["vdt"], a["odt"], a["b"], a["hq"], a["hkv"], a["sq"], a["sk"],
                                        a["d"], a["qs"], a["ks"], a["vs"], a["os"], a["lut"], a["cnt"],
                                        a["L"], a["lh"], a["scale"], a["flags"], a["splits"], a["sst"], None)
@@ -254,8 +255,9 @@ def _fmha8(lib, **kw):
     (dict(vs=_s3(2 * 512 * 128, 512 * 128, 1 << 24)), ops.SPARGE_ERR_UNSUPPORTED),
     (dict(qs=_s3(8 * 512 * 128, 512 * 128, 1 << 25)), ops.SPARGE_ERR_UNSUPPORTED),   # 64 Q code rows span 2^31 bytes
 ])
-def test_fmha_qk_int8_rejections(lib, kw, status):
-    st = _fmha8(lib, **kw)
+@pytest.mark.parametrize("entry", ["sparse_fmha_fwd_qk_int8", "sparse_fmha_fwd_qk_fp8"])
+def test_fmha_qk_int8_rejections(lib, kw, status, entry):
+    st = _fmha8(lib, entry=entry, **kw)
     assert st == status, _err(lib)
 
 

@@ -1,11 +1,12 @@
-"""Seeded sweep of the int8-QK path against the fp64 oracle.
+"""Seeded sweep of the int8-QK and fp8-QK paths against the fp64 oracle.
 
 Each case draws a shape (ragged s_q / s_k, d 64 or 128, GQA ratio 1 / 2 / 4),
 the V type (fp16 or bf16), a random LUT (per query head or per KV head, empty
 rows) or the dense mode, the causal mask, splits and fp32 output.  The int8
-codes and scales come from the block map's fused quantisation and must equal
-the oracle's bit for bit; attention on them is held to O atol 4e-2 /
-rtol 1e-2 and LSE 2e-3 nats against the oracle's attention on its own codes.
+or fp8 (e4m3) codes and scales come from the block map's fused quantisation
+and must equal the oracle's bit for bit (fp8 codes compared as values);
+attention on them is held to O atol 4e-2 / rtol 1e-2 and LSE 2e-3 nats
+against the oracle's attention on its own codes.
 """
 import numpy as np
 import pytest
@@ -67,35 +68,40 @@ def describe(c):
             f"per_kv={c['per_kv']} splits={c['splits']} out_f32={c['out_f32']} q_scale={c['q_scale']}")
 
 
+@pytest.mark.parametrize("code", ["int8", "fp8"])
 @pytest.mark.parametrize("i", range(N_CASES))
-def test_qk_int8_random_case(dev, i):
+def test_qk_int8_random_case(dev, i, code):
     c = draw_case(i)
     print(describe(c), flush=True)
     h_q = c["h_kv"] * c["ratio"]
     q = synth.normal((c["b"], h_q, c["s_q"], c["d"]), 1100 + i, 1, c["dtype"], dev, scale=c["q_scale"])
     k = synth.normal((c["b"], c["h_kv"], c["s_k"], c["d"]), 1100 + i, 2, c["dtype"], dev)
     v = synth.normal((c["b"], c["h_kv"], c["s_k"], c["d"]), 1100 + i, 3, c["dtype"], dev)
-    bm = ops.build_block_map(q, k, [0.5] * h_q, [0.001] * h_q, quantize_int8=True)
+    fp8 = code == "fp8"
+    bm = ops.build_block_map(q, k, [0.5] * h_q, [0.001] * h_q, quantize_int8=not fp8, quantize_fp8=fp8)
     torch.cuda.synchronize()
-    for x, key in ((q, "q_i8"), (k, "k_i8")):
-        codes, scales = oracle.quantize_int8(x.float().cpu().numpy())
-        assert np.array_equal(bm[key].cpu().numpy(), codes), f"{describe(c)}: {key}"
+    sfx = "fp8" if fp8 else "i8"
+    for x, key in ((q, "q_" + sfx), (k, "k_" + sfx)):
+        xn = x.float().cpu().numpy()
+        codes, scales = oracle.quantize_fp8(xn) if fp8 else oracle.quantize_int8(xn)
+        got = oracle.e4m3_value(bm[key].cpu().numpy()) if fp8 else bm[key].cpu().numpy()
+        assert np.array_equal(got, codes), f"{describe(c)}: {key}"
         assert np.array_equal(bm[key + "_scale"].cpu().numpy(), scales), f"{describe(c)}: {key} scale"
     lut = None if c["dense"] else torch.from_numpy(c["lut"]).to(dev)
     cnt = None if c["dense"] else torch.from_numpy(c["cnt"]).to(dev)
-    args = (bm["q_i8"], bm["q_i8_scale"], bm["k_i8"], bm["k_i8_scale"], v, lut, cnt)
+    args = (bm["q_" + sfx], bm["q_" + sfx + "_scale"], bm["k_" + sfx], bm["k_" + sfx + "_scale"], v, lut, cnt)
+    fmha = ops.sparse_fmha_fwd_qk_fp8 if fp8 else ops.sparse_fmha_fwd_qk_int8
     out_dt = torch.float32 if c["out_f32"] else c["dtype"]
     if c["splits"] == 1:
-        o, lse = ops.sparse_fmha_fwd_qk_int8(*args, causal=c["causal"], out_dtype=out_dt)
+        o, lse = fmha(*args, causal=c["causal"], out_dtype=out_dt)
     else:
-        op, lp = ops.sparse_fmha_fwd_qk_int8(*args, causal=c["causal"], num_splits=c["splits"],
-                                             out_dtype=torch.float32 if c["out_f32"] else c["dtype"])
+        op, lp = fmha(*args, causal=c["causal"], num_splits=c["splits"],
+                      out_dtype=torch.float32 if c["out_f32"] else c["dtype"])
         o, lse = ops.attn_combine(op, lp, out_dtype=out_dt)
     torch.cuda.synchronize()
-    ro, rl = oracle.block_sparse_attention_qk_int8(np64(q), np64(k), np64(v),
-                                                   None if c["dense"] else c["lut"],
-                                                   None if c["dense"] else c["cnt"],
-                                                   lut_per_kv_head=c["per_kv"], causal=c["causal"])
+    ref = oracle.block_sparse_attention_qk_fp8 if fp8 else oracle.block_sparse_attention_qk_int8
+    ro, rl = ref(np64(q), np64(k), np64(v), None if c["dense"] else c["lut"],
+                 None if c["dense"] else c["cnt"], lut_per_kv_head=c["per_kv"], causal=c["causal"])
     g = np64(o)
     err = np.abs(g - ro)
     bad = err > O_ATOL + O_RTOL * np.abs(ro)

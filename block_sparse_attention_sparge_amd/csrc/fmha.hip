@@ -231,7 +231,9 @@ void fmha_block_kernel(FmhaArgs a) {
   // g ^ (r mod G16)) and the rows of a partial last tile repeat its last row.
   // Q and O are touched once, so their loads and stores are non-temporal and
   // leave more of the caches to the K/V blocks that other rows reuse
-  // (measured 1.0-1.3% faster at topk 0.1, bit-identical).
+  // (measured 1.0-1.3% faster at topk 0.1, bit-identical); split partials
+  // small enough to stay in the last-level cache for the combine that reads
+  // them next are the exception (o_nt = 0, set by the host).
   {
     const char* qbase = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.q) + bb * a.qs[0] +
                                                       hh * a.qs[1] + (int64_t)(64 * qt) * a.qs[2]);
@@ -282,17 +284,6 @@ void fmha_block_kernel(FmhaArgs a) {
     const SPARGE_LDS T* vt = (const SPARGE_LDS T*)&sV[cur * TILE];
 
     asm volatile("" ::"s"(kb_ahead));   // the LUT load of the previous step has landed
-  // pv_threshold: the decision on the block whose votes are in `slot`: query
-  // row i of the tile (lane i) has r_i = its maximum over the block's 64
-  // keys and M_i its running maximum over the blocks visited so far, this
-  // one included; the block is dropped when r_i < M_i - tau for all 64 rows.
-  // Every wave reads the same values and takes the same decision.
-  auto pv_keep_block = [&](int slot) {
-    const int vq = lane >> 5, vr = lane & 31;
-    const float2v h0 = s_vote[slot * 128 + vq * 32 + vr], h1 = s_vote[slot * 128 + (2 + vq) * 32 + vr];
-    const float r_i = fmaxf(h0[0], h1[0]), m_i = fmaxf(h0[1], h1[1]);
-    return __any(!(r_i < m_i - a.pv_tau2));
-  };
 
     // LDS operands are requested early so that their latency overlaps the
     // MFMAs: the 8 K reads and the first half of V^T before S^T, the second
@@ -513,15 +504,24 @@ void fmha_block_kernel(FmhaArgs a) {
   const int nrows = min(64, a.sq - 64 * qt);     // rows of a partial last tile
   OT* obase = reinterpret_cast<OT*>(a.o) + (int64_t)split * a.o_split_stride + bb * a.os[0] + hh * a.os[1] +
               (int64_t)(64 * qt) * a.os[2];
+  auto store_rows = [&](auto nt_tag) {
 #pragma unroll
-  for (int k = 0; k < OG / 4; ++k) {
-    const int idx = tid + 256 * k;
-    const int r = idx / OG, gs = idx % OG;
-    if (r < nrows) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * (OG * 16) + ((gs ^ (r % OG)) * 16));
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(obase + (int64_t)r * a.os[2] + gs * (16 / (int)sizeof(OT))));
+    for (int k = 0; k < OG / 4; ++k) {
+      const int idx = tid + 256 * k;
+      const int r = idx / OG, gs = idx % OG;
+      if (r < nrows) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * (OG * 16) + ((gs ^ (r % OG)) * 16));
+        u32x4* dst = reinterpret_cast<u32x4*>(obase + (int64_t)r * a.os[2] + gs * (16 / (int)sizeof(OT)));
+        if constexpr (decltype(nt_tag)::value) __builtin_nontemporal_store(v, dst);
+        else *dst = v;
+      }
     }
-  }
+    // Ends the two store sequences differently, so the compiler does not
+    // merge their last stores (which would drop the non-temporal hint).
+    if constexpr (decltype(nt_tag)::value) asm volatile("" ::: "memory");
+  };
+  if (a.o_nt) store_rows(std::true_type{});
+  else store_rows(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------

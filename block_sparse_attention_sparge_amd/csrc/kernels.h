@@ -79,6 +79,7 @@ struct FmhaArgs {
   float scale_log2;        // softmax scale * log2(e)
   int splits;
   int64_t o_split_stride;  // elements
+  int o_nt;                // block kernel: O rows leave with non-temporal stores
   int causal;              // block mode: key j > query i masked
   float pv_tau2;           // block mode: pv_threshold * log2(e); 0 = no PV skip
   // int8-QK block kernel: q and k hold int8 codes; their per-block scales.

@@ -329,46 +329,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   // element d = 16g + 4k4 + t: each operand is then one 16-byte load per
   // slice, straight from memory into registers.  Wave w computes the columns
   // 64c + 16w .. +15 of the 16 x nk score tile.
+  //
+  // Every load below is unconditional: indices past the end are clamped to
+  // the last row or block, whose finite copies are then masked or never
+  // written.  A load under a branch would make the compiler wait for it at
+  // the join, and so would the copy of a prefetched operand into the
+  // registers the MFMAs read; the column chunks therefore alternate between
+  // two operand sets, and chunk c+1's means load during chunk c's MFMAs.
   const int m16 = lane & 15, k4 = lane >> 4;
   floatx4 qf[NG];
   {
-    const float* qrow = a.q_mean + (bh * a.nq + qb0 + m16) * D + 4 * k4;
+    const float* qrow = a.q_mean + (bh * a.nq + qb0 + min(m16, rows - 1)) * D + 4 * k4;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      qf[g] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (m16 < rows) qf[g] = *reinterpret_cast<const floatx4*>(qrow + 16 * g);
-    }
+    for (int g = 0; g < NG; ++g) qf[g] = *reinterpret_cast<const floatx4*>(qrow + 16 * g);
   }
   const float* km = a.k_mean + bkv * nk * D;
   const float* ksim = a.k_sim + bkv * nk;
-  // The small per-block inputs this wave needs are requested early so that
-  // their latencies overlap the loads of the pooled means: the K gate value
-  // of the column this lane scores (one column step ahead, like the means),
-  // the K gate values of the row elements this lane selects, and the Q gate
-  // flag of row `lane`.
-  auto ksim_at = [&](int kb) { return kb < nk ? ksim[kb] : 0.f; };
-  float ksim_el[KPL];
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) ksim_el[j] = ksim_at(lane * KPL + j);
-  const bool qflag_lane = lane < rows && a.sim_q[bh * a.nq + qb0 + lane] != 0;
-  float ks_cur = ksim_at(16 * wave + m16), ks_nxt = 0.f;
-  auto load_k = [&](floatx4 (&kf)[NG], int kb) {
+  auto ksim_at = [&](int kb) { return ksim[min(kb, nk - 1)]; };
+  // Chunk c's operand: the means of K blocks 64c + 16 wave + m16 and the gate
+  // value of the column this lane scores.
+  auto load_k = [&](floatx4 (&kf)[NG], float& ks, int c) {
+    const int kb = min(64 * c + 16 * wave + m16, nk - 1);
     const float* krow = km + (int64_t)kb * D + 4 * k4;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      kf[g] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (kb < nk) kf[g] = *reinterpret_cast<const floatx4*>(krow + 16 * g);
-    }
+    for (int g = 0; g < NG; ++g) kf[g] = *reinterpret_cast<const floatx4*>(krow + 16 * g);
+    ks = ksim[kb];
   };
-  floatx4 kf[NG], kn[NG];
-  load_k(kf, 16 * wave + m16);
-#pragma unroll 1
-  for (int c = 0; c < KPL; ++c) {
+  auto score_chunk = [&](const floatx4 (&kf)[NG], float ks, int c) {
     const int kb = 64 * c + 16 * wave + m16;
-    if (c + 1 < KPL) {
-      load_k(kn, kb + 64);
-      ks_nxt = ksim_at(kb + 64);
-    }
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -377,31 +365,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     }
     // C: lane holds column kb for rows 4*k4 .. 4*k4+3.  Causal: block kb is
     // in the future of Q-tile qb0 + row when kb > qb0 + row.
-    const bool live = kb < nk && ks_cur > thr;
+    const bool live = kb < nk && ks > thr;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok = live && (!a.causal || kb <= qb0 + 4 * k4 + i);
       s_score[4 * k4 + i][kb] = ok ? acc[i] * a.scale : -INFINITY;
     }
+  };
+  // The scheduling barriers keep each chunk's loads issued ahead of the
+  // MFMAs of the chunk before it (left alone, the scheduler sinks them to
+  // their first use).
+  floatx4 k0[NG], k1[NG];
+  float ks0, ks1;
+  load_k(k0, ks0, 0);
 #pragma unroll
-    for (int g = 0; g < NG; ++g) kf[g] = kn[g];
-    ks_cur = ks_nxt;
+  for (int c = 0; c < KPL; c += 2) {
+    if (c + 1 < KPL) load_k(k1, ks1, c + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    score_chunk(k0, ks0, c);
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 1 < KPL) {
+      if (c + 2 < KPL) load_k(k0, ks0, c + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      score_chunk(k1, ks1, c + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
+  // Inputs only the selection needs, requested now (they land during the
+  // softmax): the K gate values of the row elements this lane selects and
+  // the Q gate flag of row `lane`.
+  float ksim_el[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) ksim_el[j] = ksim_at(lane * KPL + j);
+  const uint8_t qflag_raw = a.sim_q[bh * a.nq + qb0 + min(lane, rows - 1)];
   __syncthreads();
-
-  // Gate flags used by every row of the group, read once.
-  bool kgate[KPL];
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const int e = lane * KPL + j;
-    kgate[j] = e < nk && !(ksim_el[j] > thr);          // K block forced on
-  }
-  if (a.sim_k && qb0 == 0 && wave == 0) {
-#pragma unroll
-    for (int j = 0; j < KPL; ++j)
-      if (lane * KPL + j < nk) a.sim_k[bh * nk + lane * KPL + j] = kgate[j] ? 0 : 1;
-  }
-  const uint64_t qflags = __ballot(qflag_lane);
 
   const int nsel_h = a.nsel[hh];
   const double cdf_h = (double)a.cdf[hh];
@@ -563,6 +560,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
 #pragma unroll
       for (int j = 0; j < KPL; ++j) chosen[i][j] = s_sel[4 * i + wave][lane * KPL + j] != 0;
   }
+
+  // Gate flags used by every row of the group, read once (their loads were issued
+  // before the softmax).
+  bool kgate[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int e = lane * KPL + j;
+    kgate[j] = e < nk && !(ksim_el[j] > thr);          // K block forced on
+  }
+  if (a.sim_k && qb0 == 0 && wave == 0) {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j)
+      if (lane * KPL + j < nk) a.sim_k[bh * nk + lane * KPL + j] = kgate[j] ? 0 : 1;
+  }
+  const uint64_t qflags = __ballot(lane < rows && qflag_raw != 0);
 
   // OR in the gate (within the allowed blocks) and the sink, then write the
   // ascending LUT by a prefix scan.

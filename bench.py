@@ -147,15 +147,18 @@ def graph_cold_ms(fn, torch, flush, replays=10):
 def _oracle_slice(job):
     """One (b, h) slice of the CPU baseline in a worker process: the fp64
     oracle's block map and attention over the selected blocks, on one BLAS
-    thread.  Returns (seconds, selected block pairs)."""
+    thread.  Returns (seconds, selected block pairs, block-map seconds,
+    attention seconds)."""
     q, k, v, topk = job
     from threadpoolctl import threadpool_limits
     import oracle
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         bm = oracle.block_map(q, k, topk=[topk], simthreshd1=[0.001])
+        t1 = time.perf_counter()
         oracle.block_sparse_attention(q, k, v, bm["lut"], bm["count"])
-        return time.perf_counter() - t0, int(bm["count"].sum())
+        t2 = time.perf_counter()
+        return t2 - t0, int(bm["count"].sum()), t1 - t0, t2 - t1
 
 
 def cpu_baseline(topk=0.4, max_workers=16):
@@ -184,7 +187,9 @@ def cpu_baseline(topk=0.4, max_workers=16):
                 sample=f"32 (b, h) slices (b=0, h=0..31) of b2 h32 s16384 d128 at topk {topk}: fp64 oracle "
                        f"block map + attention over the selected blocks, {workers} worker processes with one "
                        f"BLAS thread each, {dt:.1f} s wall ({sum(r[0] for r in res):.0f} s of CPU work)",
-                seconds=dt, cpu_seconds=sum(r[0] for r in res), host_cpus=os.cpu_count())
+                seconds=dt, cpu_seconds=sum(r[0] for r in res),
+                cpu_seconds_block_map=sum(r[2] for r in res), cpu_seconds_attention=sum(r[3] for r in res),
+                host_cpus=os.cpu_count())
 
 
 def step_arms(ops, case, arms, rounds, warmup, torch):

@@ -288,6 +288,50 @@ __device__ __forceinline__ void bitonic_desc(uint64_t (&key)[KPL], int lane) {
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP: shifts by
+// 1, 2, 4 and 8 inside each row of 16 lanes (lanes without a source add 0),
+// then the last lane of row 0 added to row 1 and of row 2 to row 3, then the
+// last lane of row 1 (rows 0 + 1 by now) to rows 2 and 3.
+__device__ __forceinline__ int wave_prefix_sum_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+// Maximum and sum over the 64 lanes of a wavefront, the same DPP steps (a
+// lane without a source keeps -inf, or adds 0), read from the last lane.
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  const int ninf = __builtin_bit_cast(int, -INFINITY);
+#define SPARGE_MAX_STEP(ctrl, rows)                                                                      \
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(ninf, __builtin_bit_cast(int, x), ctrl, \
+                                                                     rows, 0xF, false)))
+  SPARGE_MAX_STEP(0x111, 0xF);
+  SPARGE_MAX_STEP(0x112, 0xF);
+  SPARGE_MAX_STEP(0x114, 0xF);
+  SPARGE_MAX_STEP(0x118, 0xF);
+  SPARGE_MAX_STEP(0x142, 0xA);
+  SPARGE_MAX_STEP(0x143, 0xC);
+#undef SPARGE_MAX_STEP
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+#define SPARGE_SUM_STEP(ctrl, rows, bc) \
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, rows, 0xF, bc))
+  SPARGE_SUM_STEP(0x111, 0xF, true);
+  SPARGE_SUM_STEP(0x112, 0xF, true);
+  SPARGE_SUM_STEP(0x114, 0xF, true);
+  SPARGE_SUM_STEP(0x118, 0xF, true);
+  SPARGE_SUM_STEP(0x142, 0xA, false);
+  SPARGE_SUM_STEP(0x143, 0xC, false);
+#undef SPARGE_SUM_STEP
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
 // Number of this wave's valid keys (bits of probabilities) that are >= t.
 template <int KPL>
 __device__ __forceinline__ int count_at_least(const uint32_t (&pb)[KPL], const bool (&valid)[KPL],
@@ -436,9 +480,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     for (int j = 1; j < KPL; ++j) mx[i] = fmaxf(mx[i], p[i][j]);
   }
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1)
-#pragma unroll
-    for (int i = 0; i < RW; ++i) mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], m, kWave));
+  for (int i = 0; i < RW; ++i) mx[i] = wave_max_dpp(mx[i]);
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
     sum[i] = 0.f;
@@ -449,9 +491,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     }
   }
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1)
-#pragma unroll
-    for (int i = 0; i < RW; ++i) sum[i] += __shfl_xor(sum[i], m, kWave);
+  for (int i = 0; i < RW; ++i) sum[i] = wave_sum_dpp(sum[i]);
 #pragma unroll
   for (int i = 0; i < RW; ++i)
 #pragma unroll
@@ -473,27 +513,98 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   // >= +0, so their bit patterns order like their values.
   bool chosen[RW][KPL];
   if (nsel_h > 0) {
-    // top-k: T = the n-th largest probability (bits), by bisection on
-    // count(>= lo) >= n > count(>= hi); 31 halvings close a range of 2^31.
-    uint32_t lo[RW], hi[RW];
-#pragma unroll
-    for (int i = 0; i < RW; ++i) { lo[i] = 0u; hi[i] = 0x7F800000u; }
-#pragma unroll 1
-    for (int round = 0; round < 31; ++round) {
+    // top-k: T = the n-th largest probability (bits).  Probabilities are >= +0,
+    // so their bit patterns order like their values.
+    uint32_t thr_bits[RW];
+    if constexpr (KPL >= 4) {
+      // Radix select from the most significant byte, four rounds: a histogram
+      // of the next byte over the keys that share the bytes decided so far,
+      // then a prefix count over the 256 bins, largest byte first, finds the
+      // byte of the n-th largest and how many keys lie above it.  Each wave
+      // keeps its rows' histograms in its own rows of s_score (256 bins fit,
+      // and in this mode the scores are in registers by now), built with LDS
+      // atomics; bin 255 - byte, so lane l holds the bins of bytes
+      // 255 - 4l .. 252 - 4l and the count from the top is a prefix sum over
+      // the lanes (DPP row shifts and row broadcasts, no LDS traffic).
+      uint32_t rank[RW];
 #pragma unroll
       for (int i = 0; i < RW; ++i) {
-        const uint32_t mid = lo[i] + ((hi[i] - lo[i]) >> 1);
-        int c = 0;
-#pragma unroll
-        for (int j = 0; j < KPL; ++j)
-          c += __popcll(__ballot(valid[j] && __builtin_bit_cast(uint32_t, p[i][j]) >= mid));
-        if (c >= min(nsel_h, limit[i])) lo[i] = mid;
-        else hi[i] = mid;
+        thr_bits[i] = 0u;
+        rank[i] = (uint32_t)min(nsel_h, limit[i]);
       }
+#pragma unroll 1
+      for (int rnd = 0; rnd < 4; ++rnd) {
+        const int shift = 24 - 8 * rnd;
+        const uint32_t pmask = rnd == 0 ? 0u : 0xFFFFFFFFu << (shift + 8);
+#pragma unroll
+        for (int i = 0; i < RW; ++i)
+          reinterpret_cast<u32x4*>(&s_score[4 * i + wave][0])[lane] = u32x4{0u, 0u, 0u, 0u};
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+          uint32_t* hist = reinterpret_cast<uint32_t*>(&s_score[4 * i + wave][0]);
+#pragma unroll
+          for (int j = 0; j < KPL; ++j) {
+            const uint32_t pb = __builtin_bit_cast(uint32_t, p[i][j]);
+            if (valid[j] && (pb & pmask) == thr_bits[i]) atomicAdd(&hist[255u - ((pb >> shift) & 255u)], 1u);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+          const u32x4 h = reinterpret_cast<const u32x4*>(&s_score[4 * i + wave][0])[lane];
+          const int lsum = (int)(h[0] + h[1] + h[2] + h[3]);
+          const int pre = wave_prefix_sum_dpp(lsum);          // keys with byte >= 252 - 4 lane
+          // The first lane whose prefix reaches the rank holds the byte.
+          const int L = (int)__builtin_amdgcn_readfirstlane(
+              (int)__builtin_ctzll(__ballot(pre >= (int)rank[i])));
+          int cum = pre - lsum, byte = 0, above = 0;
+          if (cum + (int)h[0] >= (int)rank[i]) {
+            byte = 255 - 4 * lane;
+            above = cum;
+          } else if (cum + (int)(h[0] + h[1]) >= (int)rank[i]) {
+            byte = 254 - 4 * lane;
+            above = cum + (int)h[0];
+          } else if (cum + (int)(h[0] + h[1] + h[2]) >= (int)rank[i]) {
+            byte = 253 - 4 * lane;
+            above = cum + (int)(h[0] + h[1]);
+          } else {
+            byte = 252 - 4 * lane;
+            above = cum + (int)(h[0] + h[1] + h[2]);
+          }
+          thr_bits[i] |= (uint32_t)__builtin_amdgcn_readlane(byte, L) << shift;
+          rank[i] -= (uint32_t)__builtin_amdgcn_readlane(above, L);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+      }
+    } else {
+      // Short rows (nk <= 128): bisection on count(>= lo) >= n > count(>= hi);
+      // 31 halvings close a range of 2^31.
+      uint32_t lo[RW], hi[RW];
+#pragma unroll
+      for (int i = 0; i < RW; ++i) { lo[i] = 0u; hi[i] = 0x7F800000u; }
+#pragma unroll 1
+      for (int round = 0; round < 31; ++round) {
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+          const uint32_t mid = lo[i] + ((hi[i] - lo[i]) >> 1);
+          int c = 0;
+#pragma unroll
+          for (int j = 0; j < KPL; ++j)
+            c += __popcll(__ballot(valid[j] && __builtin_bit_cast(uint32_t, p[i][j]) >= mid));
+          if (c >= min(nsel_h, limit[i])) lo[i] = mid;
+          else hi[i] = mid;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < RW; ++i) thr_bits[i] = lo[i];
     }
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
-      const uint32_t t = lo[i];
+      const uint32_t t = thr_bits[i];
       int above = 0, ties = 0;
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
@@ -502,7 +613,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
         ties += (valid[j] && pb == t) ? 1 : 0;
       }
       const int need = min(nsel_h, limit[i]) - above;            // ties at T to take
-      int tie_rank = wave_inclusive_scan(ties) - ties;           // ties before this lane
+      int tie_rank = wave_prefix_sum_dpp(ties) - ties;           // ties before this lane
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
         const uint32_t pb = __builtin_bit_cast(uint32_t, p[i][j]);
@@ -593,17 +704,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     incl[i] = cnt[i];
   }
 #pragma unroll
-  for (int off = 1; off < kWave; off <<= 1)
-#pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      const int t = __shfl_up(incl[i], off, kWave);
-      if (lane >= off) incl[i] += t;
-    }
+  for (int i = 0; i < RW; ++i) incl[i] = wave_prefix_sum_dpp(incl[i]);
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
     if (4 * i + wave >= rows) continue;
     const int64_t row = bh * a.nq + qb0 + 4 * i + wave;
-    const int total = __shfl(incl[i], kWave - 1, kWave);
+    const int total = __builtin_amdgcn_readlane(incl[i], kWave - 1);
     int32_t* lrow = a.lut + row * nk;
     int pos = incl[i] - cnt[i];
 #pragma unroll

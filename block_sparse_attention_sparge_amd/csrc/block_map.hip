@@ -5,10 +5,10 @@
 // BlockMap LUT, with per-head topk / simthreshd1 / cdfthreshd.  The same page
 // lists sort-based top-k as the replacement for an O(nk^2) argmax that hurts
 // at long sequences.  Here the top-k count needs no full sort: the n-th
-// largest probability is found by bisection on its bits with wavefront
-// ballots (about 31 rounds of popcounts), and ties at it go to the lower
-// block index; the cdf rule needs the order itself and sorts each row with a
-// bitonic network held in the registers of one wavefront.
+// largest probability is found by a radix select on its bits (four rounds of
+// 8-bit histograms), and ties at it go to the lower block index; the cdf rule
+// needs the order itself and sorts each row with a bitonic network held in
+// the registers of one wavefront.
 //
 // Two kernels:
 //   pool_sim     one wavefront per 64-token block of Q or K: reads the block
@@ -19,10 +19,10 @@
 //                memory, fp32 softmax, then the selection in the order
 //                (probability descending, block index ascending), the four
 //                rows of each wavefront interleaved step by step:
-//                top-k finds the n-th largest probability by bisection on its
-//                bits with wavefront ballots and takes ties at it by ascending
-//                index; cdf needs the order itself and sorts the row with a
-//                64-bit-key bitonic network.  The ascending LUT is written by
+//                top-k finds the n-th largest probability by a radix select
+//                on its bits (bisection for rows of at most 128 blocks) and
+//                takes ties at it by ascending index; cdf needs the order
+//                itself and sorts the row with a 64-bit-key bitonic network.  The ascending LUT is written by
 //                a prefix scan (no atomics, so the output is deterministic).
 #include "common.h"
 #include "kernels.h"

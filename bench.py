@@ -300,10 +300,11 @@ def extras(ops, synth, torch, steps, warmup):
     out["combine_headline_partials"] = dict(workload="2 x [2,32,16384,128] fp32 -> fp16", ms=cm,
                                             gbs=comb_bytes / cm / 1e6, frac_hbm=comb_bytes / cm / 1e6 / PEAK_HBM_GBS)
     del parts, lses, oc, lc
-    # Decode GQA, b64 h_q32 h_kv8 s_k32768 d128 bf16, 2048-entry lists, 8 splits + combine.
+    # Decode GQA, b64 h_q32 h_kv8 s_k32768 d128 bf16, 2048-entry lists, 4 splits + combine
+    # (split + combine measured fastest at 4 splits for this shape, of 2 to 16).
     log("decode")
     dc = synth.decode_case(dev)
-    S_SPLIT = 8
+    S_SPLIT = 4
     op = torch.empty((S_SPLIT, 64, 32, 1, 128), device=dev)
     lp = torch.empty((S_SPLIT, 64, 32, 1), device=dev)
     od = torch.empty_like(dc.q)
@@ -331,7 +332,7 @@ def extras(ops, synth, torch, steps, warmup):
     neff = (1.0 / (p * p).sum(-1)).flatten().sort().values.cpu()
     del kg, qg, p
     out["decode_gqa"] = dict(
-        workload="b64 h_q32 h_kv8 s_k32768 d128 bf16, 2048 listed keys, 8 splits + combine",
+        workload="b64 h_q32 h_kv8 s_k32768 d128 bf16, 2048 listed keys, 4 splits + combine",
         ms=dm, fmha_ms=dfm, gathered_gbs=gathered / dm / 1e6, frac_hbm=gathered / dm / 1e6 / PEAK_HBM_GBS,
         fmha_gathered_gbs=gathered / dfm / 1e6,
         cold_ms=dm_cold, cold_fmha_ms=dfm_cold, cold_gathered_gbs=gathered / dm_cold / 1e6,

@@ -66,16 +66,48 @@ struct BF16 {
   }
 };
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP: shifts by
+// 1, 2, 4 and 8 inside each row of 16 lanes (lanes without a source add 0),
+// then the last lane of row 0 added to row 1 and of row 2 to row 3, then the
+// last lane of row 1 (rows 0 + 1 by now) to rows 2 and 3.
+__device__ __forceinline__ int wave_prefix_sum_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
   return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
+// Maximum and sum over the 64 lanes of a wavefront, the same DPP steps (a
+// lane without a source keeps -inf, or adds 0), read from the last lane.
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  const int ninf = __builtin_bit_cast(int, -INFINITY);
+#define SPARGE_MAX_STEP(ctrl, rows)                                                                      \
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(ninf, __builtin_bit_cast(int, x), ctrl, \
+                                                                     rows, 0xF, false)))
+  SPARGE_MAX_STEP(0x111, 0xF);
+  SPARGE_MAX_STEP(0x112, 0xF);
+  SPARGE_MAX_STEP(0x114, 0xF);
+  SPARGE_MAX_STEP(0x118, 0xF);
+  SPARGE_MAX_STEP(0x142, 0xA);
+  SPARGE_MAX_STEP(0x143, 0xC);
+#undef SPARGE_MAX_STEP
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+#define SPARGE_SUM_STEP(ctrl, rows, bc) \
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, rows, 0xF, bc))
+  SPARGE_SUM_STEP(0x111, 0xF, true);
+  SPARGE_SUM_STEP(0x112, 0xF, true);
+  SPARGE_SUM_STEP(0x114, 0xF, true);
+  SPARGE_SUM_STEP(0x118, 0xF, true);
+  SPARGE_SUM_STEP(0x142, 0xA, false);
+  SPARGE_SUM_STEP(0x143, 0xC, false);
+#undef SPARGE_SUM_STEP
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
 // Workgroups are dispatched to the 8 XCDs round-robin by linear id; give every

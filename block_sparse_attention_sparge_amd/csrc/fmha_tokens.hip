@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void fmha_tokens_kernel(FmhaArgs a) {
       const int r = wave + 4 * i;
       if (r < R) {
         const float x = s_p[r][lane];
-        const float cm = wave_max(x);
+        const float cm = wave_max_dpp(x);
         const float m_new = fmaxf(m_run[i], cm);
         float alpha, p;
         if (m_new == -INFINITY) {
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256) void fmha_tokens_kernel(FmhaArgs a) {
           p = __builtin_amdgcn_exp2f(x - m_new);
         }
         m_run[i] = m_new;
-        l_run[i] = fmaf(l_run[i], alpha, wave_sum(p));
+        l_run[i] = fmaf(l_run[i], alpha, wave_sum_dpp(p));
         s_p[r][lane] = p;
         if (lane == 0) s_alpha[r] = alpha;
       }

@@ -288,16 +288,6 @@ __device__ __forceinline__ void bitonic_desc(uint64_t (&key)[KPL], int lane) {
   }
 }
 
-// Number of this wave's valid keys (bits of probabilities) that are >= t.
-template <int KPL>
-__device__ __forceinline__ int count_at_least(const uint32_t (&pb)[KPL], const bool (&valid)[KPL],
-                                              uint32_t t) {
-  int c = 0;
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) c += __popcll(__ballot(valid[j] && pb[j] >= t));
-  return c;
-}
-
 template <int D, int KPL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void score_select_kernel(SelectArgs a) {
   constexpr int NKP = 64 * KPL;

@@ -137,17 +137,6 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    int t = __shfl_up(v, off, kWave);
-    if (lane >= off) v += t;
-  }
-  return v;
-}
-
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

@@ -94,3 +94,26 @@ def test_causal_ties(dev):
     gp, cnt = _check(res, topk, None, causal=True)
     tied = [_cut_is_tied(gp[0, ih, qb], int(cnt[0, ih, qb])) for ih in range(h) for qb in range(s // 64)]
     assert np.mean(tied) > 0.5, f"only {np.mean(tied):.2f} of the rows cut inside a tie group"
+
+
+@pytest.mark.parametrize("nk", [256, 384, 1024])
+def test_topk_ties_on_long_rows(dev, nk):
+    # Rows of more than 128 blocks take the radix select (histograms of the
+    # probabilities' bytes) instead of the bisection, with 4, 8 and 16 key
+    # slots per lane (384 blocks fill 6 of the 8).  K repeats 4 distinct
+    # blocks along the row and the cuts fall inside groups of equal
+    # probabilities.
+    b, h, sq, d = 1, 4, 1024, 64
+    sk = 64 * nk
+    q = synth.centroid_noise(b, h, sq, d, 64, [1.5] * h, 0.5, 21, 1, torch.float16, dev)
+    k0 = synth.centroid_noise(b, h, 64 * 4, d, 64, [1.5] * h, 0.5, 21, 2, torch.float16, dev)
+    src = torch.randperm(4, generator=torch.Generator().manual_seed(nk))[torch.arange(nk) % 4].to(dev)
+    k = k0.view(b, h, 4, 64, d)[:, :, src].reshape(b, h, sk, d).contiguous()
+    cuts = [37, nk // 3 + 5, nk // 2 + 3, nk - 11]
+    topk = [(n + 0.5) / nk for n in cuts]
+    res = ops.build_block_map(q, k, topk, [0.001] * h, return_debug=True)
+    torch.cuda.synchronize()
+    gp, cnt = _check(res, topk, None)
+    assert np.array_equal(cnt[0], np.array(cuts)[:, None].repeat(sq // 64, 1))
+    tied = [_cut_is_tied(gp[0, ih, qb], int(cnt[0, ih, qb])) for ih in range(h) for qb in range(sq // 64)]
+    assert np.mean(tied) > 0.9, f"only {np.mean(tied):.2f} of the rows cut inside a tie group"

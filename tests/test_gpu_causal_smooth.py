@@ -132,6 +132,31 @@ def test_block_map_causal_cdf_mode(dev):
                             causal=True, attention_sink=True)
 
 
+@pytest.mark.parametrize("s", [16384, 24576])
+def test_block_map_causal_long_rows(dev, s):
+    # Causal rows of up to 256 and 384 blocks take the radix select (rows of
+    # at most 128 blocks take the bisection), with the allowed-block limit,
+    # K smoothing and the sink.
+    b, h, d = 1, 2, 64
+    q = synth.centroid_noise(b, h, s, d, 64, [1.0, 2.0], 0.5, 23, 1, torch.float16, dev)
+    k = _offset_keys(synth.centroid_noise(b, h, s, d, 64, [1.0, 2.0], 0.5, 23, 2, torch.float16, dev), 72)
+    res, _ = _block_map_with_options(dev, q, k, [0.1, 0.4], [0.001, 0.001], causal=True,
+                                     attention_sink=True, smooth_k=True)
+    lut = res["lut"].cpu().numpy()
+    for qb in range(0, lut.shape[2], 17):
+        sel = lut[:, :, qb]
+        assert ((sel <= qb) | (sel == -1)).all() and (sel[..., 0] == 0).all()
+
+
+@pytest.mark.parametrize("sk", [16384, 65536])
+def test_block_map_cdf_long_rows(dev, sk):
+    # cdf rows of 256 and 1024 blocks: the bitonic sort with 4 and 16 keys per lane.
+    b, h, d = 1, 2, 64
+    q = synth.centroid_noise(b, h, 1024, d, 64, [1.0, 2.0], 0.5, 24, 1, torch.float16, dev)
+    k = synth.centroid_noise(b, h, sk, d, 64, [1.0, 2.0], 0.5, 24, 2, torch.float16, dev)
+    _block_map_with_options(dev, q, k, [0.0, 0.0], [0.001, 0.001], cdf=[0.5, 0.9])
+
+
 # ---------------------------------------------------------------------------
 # causal attention
 # ---------------------------------------------------------------------------

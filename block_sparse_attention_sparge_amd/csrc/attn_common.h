@@ -73,6 +73,29 @@ __device__ __forceinline__ void dma16_nt(const void* gbase, uint32_t goff, uint3
                : "memory", "m0");
 }
 
+// Word 3 of a raw buffer resource on gfx9-family parts (gfx950): 32-bit
+// data format, no swizzle, so offsets count bytes and an access at or past
+// the record count reads zero.
+constexpr int kBufferWord3 = 0x00020000;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// A raw buffer resource over `bytes` bytes from `base` (wave-uniform).
+__device__ __forceinline__ i32x4 raw_rsrc(const void* base, int bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  return i32x4{(int)(uint32_t)p, (int)(uint32_t)(p >> 32), bytes, kBufferWord3};
+}
+
+// 16 bytes through a buffer resource at (per-lane 32-bit offset) into LDS at
+// (wave-uniform base) + 16 * lane; an offset at or past the resource's record
+// count delivers zeros.
+__device__ __forceinline__ void dma16_buf(i32x4 rsrc, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(off), "s"(rsrc)
+               : "memory", "m0");
+}
+
 // max(x, x of lane l ^ 32).  v_permlane32_swap exchanges lanes 32..63 of its
 // first operand with lanes 0..31 of its second; with x in both, every lane
 // then holds its own value in one register and its partner's in the other.
@@ -83,11 +106,6 @@ __device__ __forceinline__ float half_swap_max(float x) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   return fmaxf(a, b);
 }
-
-// Word 3 of a raw buffer resource on gfx9-family parts (gfx950): 32-bit
-// data format, no swizzle, so offsets count bytes and an access at or past
-// the record count reads zero.
-constexpr int kBufferWord3 = 0x00020000;
 
 // Compile-time buffer index for the two-way unrolled block loop.
 template <int N>

@@ -12,9 +12,9 @@
 // O^T += V^T P^T on the 32x32x16 fp16/bf16 MFMA:
 //   * Q^T stays in registers as the B operand for the whole row; the Q tile
 //     itself arrives by direct global->LDS loads, whole rows per instruction;
-//   * K and V blocks arrive by direct global->LDS loads into double buffers;
-//     K is read row-major (A operand of S^T), V through the transposing LDS
-//     read (A operand of O^T);
+//   * K and V blocks arrive by direct global->LDS loads, K into one buffer and
+//     V into two; K is read row-major (A operand of S^T), V through the
+//     transposing LDS read (A operand of O^T);
 //   * the S^T accumulator already has the layout of the P^T B operand, so P
 //     goes from softmax to the PV MFMA without leaving registers, and every
 //     row reduction is in-lane plus one exchange with the partner half-wave;
@@ -28,11 +28,11 @@
 //     listed block when every one of the tile's 64 query rows scores, over
 //     the block's 64 keys, more than the threshold below that row's running
 //     maximum over the blocks already visited; its P still count in the row
-//     sum.  The four wavefronts post their row maxima to LDS; in this
-//     variant the block's one barrier comes after the softmax, so it
-//     publishes them, and every wave then takes the same decision and runs
-//     the block's PV product from registers (its operands were read from LDS
-//     before the barrier), so the test adds no barrier;
+//     sum.  The four wavefronts post their row maxima to LDS; the block's
+//     closing barrier comes after the softmax, so it publishes them, and
+//     every wave then takes the same decision and runs the block's PV
+//     product from registers (its operands were read from LDS before that
+//     barrier), so the test adds no barrier;
 //   * workgroups are renumbered so that consecutive rows of one head land on
 //     one XCD and share its L2 (aiter 4919 page: workgroups round-robin over
 //     the 8 XCDs by linear id); causal rows are taken last tile first.
@@ -51,15 +51,20 @@ namespace sparge {
 // 64-key block, keeping its own running maximum, row sum and O^T; the two
 // key halves are merged in LDS at the end (the LSE combine of two partials).
 //
-// K and V blocks are double-buffered in LDS and arrive by direct global->LDS
-// loads (no registers on the way; on gfx950 this path moves gathered blocks
-// out of L2 much faster than loads into VGPRs).  The loads of block i+1 are
-// issued in the middle of block i, once its operand reads have been issued:
-// the buffer they fill was released by the barrier that ended block i-1, and
-// their LDS writes then meet the softmax and the PV MFMAs rather than the
-// burst of operand reads at the start of a block.  One barrier per block.  These loads are issued from
-// inline assembly so the compiler does not guard every LDS read with a wait
-// for them; the kernel waits for them itself (vmcnt) before that barrier.
+// Three workgroups share a CU (168 VGPRs, 48.5 KB of LDS each; measured 6-9%
+// faster than two workgroups with both K and V double-buffered, bit-identical).
+// K blocks arrive in one LDS buffer and V blocks in two, by direct loads from
+// memory into LDS (no registers on the way; on gfx950 this path moves
+// gathered blocks out of L2 much faster than loads into VGPRs, and it stays
+// faster than loads into VGPRs followed by LDS writes).  Each block has two
+// barriers: the first, right after the S^T MFMAs, says every wave has read
+// the block's K, and the loads of block i+1 (K into the one K buffer, V into
+// the V buffer that block i-1 used) are issued there; the second ends the
+// block once those loads have landed.  The loads go through buffer resources
+// that end at the block's last existing row, so the rows past the end of a
+// ragged K sequence read as zeros.  They are issued from inline assembly so
+// the compiler does not guard every LDS read with a wait for them; the kernel
+// waits for them itself (vmcnt) before the closing barrier.
 //   * K is stored row-major with the 16-byte granules of row r XOR-swizzled
 //     by r mod 16, so S^T operand reads of 32 consecutive rows hit distinct
 //     banks.
@@ -77,8 +82,8 @@ namespace sparge {
 // Lengths need not be multiples of 64.  A partial last Q-tile loads its
 // missing rows as copies of its last row and stores only its own rows.  The
 // MASKED kernel removes keys by position: past the query (causal) and past
-// the end of a ragged K sequence, whose last block is loaded with its missing
-// rows repeating its last row (finite values whose scores are then -inf).
+// the end of a ragged K sequence, whose last block has zeros in its missing
+// rows (finite values whose scores are then -inf, with P = 0 against zero V).
 // Element type of O: fp32 partials or the input type.
 template <class T, bool F32>
 struct OutType {
@@ -90,7 +95,9 @@ struct OutType<T, true> {
 };
 
 template <class E, int D, bool OUT_F32, bool MASKED, bool PVSKIP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// With a pv_threshold the block's V^T operands and P stay in registers past
+// the closing barrier, which does not fit three waves per SIMD.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PVSKIP ? 2 : 3, PVSKIP ? 2 : 3)))
 void fmha_block_kernel(FmhaArgs a) {
   typedef typename E::T T;
   constexpr int G16 = D / 8;                 // 16-byte granules per K/V row
@@ -99,7 +106,7 @@ void fmha_block_kernel(FmhaArgs a) {
   constexpr int TILE = 64 * D;               // elements per K or V buffer
   constexpr int NDMA = 64 * G16 / 256;       // direct loads per thread per tile
   constexpr int VSW = G16 / 4;               // V row r's granules are XOR-swizzled by VSW * r
-  __shared__ __attribute__((aligned(16))) T sK[2 * TILE];
+  __shared__ __attribute__((aligned(16))) T sK[TILE];
   __shared__ __attribute__((aligned(16))) T sV[2 * TILE];
   __shared__ float s_ml[128];                // (m, l) of the kh = 1 waves, per query half
   // pv_threshold votes: (block maximum, running maximum) of each wave's 32
@@ -179,28 +186,23 @@ void fmha_block_kernel(FmhaArgs a) {
     koff[j] = (uint32_t)((r * a.ks[2] + (sl ^ (r % G16)) * 8) * (int64_t)sizeof(T));
     voff[j] = (uint32_t)((r * a.vs[2] + (sl ^ ((VSW * r) % G16)) * 8) * (int64_t)sizeof(T));
   }
+  const int krow_b = (int)(a.ks[2] * (int64_t)sizeof(T)), vrow_b = (int)(a.vs[2] * (int64_t)sizeof(T));
+  // K of block kb into the K buffer, V into V buffer `buf`.  The resources
+  // cover the block's existing rows, so rows past the end of a ragged K
+  // sequence read as zeros.
   auto issue_block = [&](int kb, int buf) {
-    const char* kp = kbase + kb * kblk;
-    const char* vp = vbase + kb * vblk;
-    if (MASKED && 64 * kb + 64 > a.sk) {
-      // The last block of a ragged K sequence: LDS row r takes global row
-      // min(r, last), swizzled for its own position r.
-      const int last = a.sk - 1 - 64 * kb;
-#pragma unroll
-      for (int j = 0; j < NDMA; ++j) {
-        const int gi = 64 * (wave * NDMA + j) + lane;
-        const int r = gi / G16, sl = gi % G16, rc = min(r, last);
-        const uint32_t off = (uint32_t)((buf * TILE + (wave * NDMA + j) * 64 * 8) * sizeof(T));
-        dma16(kp, (uint32_t)((rc * a.ks[2] + (sl ^ (r % G16)) * 8) * (int64_t)sizeof(T)), sk_lds + off);
-        dma16(vp, (uint32_t)((rc * a.vs[2] + (sl ^ ((VSW * r) % G16)) * 8) * (int64_t)sizeof(T)), sv_lds + off);
-      }
-      return;
+    int krec = (int)kblk, vrec = (int)vblk;
+    if constexpr (MASKED) {
+      const int rows = min(64, a.sk - 64 * kb);
+      krec = rows * krow_b;
+      vrec = rows * vrow_b;
     }
+    const i32x4 kr = raw_rsrc(kbase + kb * kblk, krec), vr = raw_rsrc(vbase + kb * vblk, vrec);
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
-      const uint32_t off = (uint32_t)((buf * TILE + (wave * NDMA + j) * 64 * 8) * sizeof(T));
-      dma16(kp, koff[j], sk_lds + off);
-      dma16(vp, voff[j], sv_lds + off);
+      const uint32_t off = (uint32_t)((wave * NDMA + j) * 64 * 8 * sizeof(T));
+      dma16_buf(kr, koff[j], sk_lds + off);
+      dma16_buf(vr, voff[j], sv_lds + off + (uint32_t)(buf * TILE * sizeof(T)));
     }
   };
   // LUT entries come through the scalar cache (the LUT is read-only here).
@@ -280,15 +282,15 @@ void fmha_block_kernel(FmhaArgs a) {
   // every LDS address is a fixed register plus an immediate offset).
   auto step = [&](int it, auto cur_tag) {
     constexpr int cur = decltype(cur_tag)::value;
-    const T* kt = &sK[cur * TILE];
+    const T* kt = &sK[0];
     const SPARGE_LDS T* vt = (const SPARGE_LDS T*)&sV[cur * TILE];
 
     asm volatile("" ::"s"(kb_ahead));   // the LUT load of the previous step has landed
 
-    // LDS operands are requested early so that their latency overlaps the
-    // MFMAs: the 8 K reads and the first half of V^T before S^T, the second
-    // half of V^T right after it (16 reads in flight is as deep as the LDS
-    // wait counter can express).
+    // The 8 K reads go out together, ahead of the S^T MFMAs; the V^T reads
+    // follow once the next block's loads are issued (first half) and just
+    // before the first PV MFMAs (second half), which keeps the registers
+    // within three waves per SIMD.
     u32x4 kf[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -312,17 +314,19 @@ void fmha_block_kernel(FmhaArgs a) {
         }
       }
     };
-    read_vt(0);
     __builtin_amdgcn_sched_barrier(0);
 
     // S^T (32 keys x 32 queries) = K Q^T.
     floatx16 s = floatx16{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) s = mfma32<E>(kf[kk], qf[kk], s);
-    read_vt(1);
     __builtin_amdgcn_sched_barrier(0);
-    // The other buffer held block it-1, released by the last barrier.
+    // Every wave has read this block's K: the K buffer, and the V buffer of
+    // block it-1 (released by the last closing barrier), take block it+1.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (it + 1 < nloc) issue_block(kb_ahead, 1 - cur);
+    read_vt(0);
+    __builtin_amdgcn_sched_barrier(0);
 
     if constexpr (MASKED) {
       // Key 64 kb + 32 kh + 8 (r/4) + 4 hl + r%4 of register r against query
@@ -365,9 +369,9 @@ void fmha_block_kernel(FmhaArgs a) {
     // the barrier, unless the tile drops the block).  The four
     // PV MFMAs of k-step 0 are issued as soon as its 8 P values exist, so the
     // exponentials of k-step 1 run in their shadow.  From the first PV MFMA to
-    // the last the wave runs at raised priority: of the two wavefronts sharing
-    // a SIMD (one from each resident workgroup), the one about to finish its
-    // block goes first and the other's softmax fills the MFMA shadows
+    // the last the wave runs at raised priority: of the wavefronts sharing a
+    // SIMD (one from each resident workgroup), the one about to finish its
+    // block goes first and the others' softmax fills the MFMA shadows
     // (measured, bit-identical: the priority 1.5-2.4% at topk 0.4 and about 4%
     // at topk 0.1; the split issue 1% and 2% more; priority on the S MFMAs as
     // well gains nothing).
@@ -389,11 +393,13 @@ void fmha_block_kernel(FmhaArgs a) {
         p[8 * ks + 2 * w] = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w], c2, -mref));
         p[8 * ks + 2 * w + 1] = __builtin_amdgcn_exp2f(fmaf(s[8 * ks + 2 * w + 1], c2, -mref));
         pf[ks][w] = E::pack2(p[8 * ks + 2 * w], p[8 * ks + 2 * w + 1]);
+        l_run += p[8 * ks + 2 * w] + p[8 * ks + 2 * w + 1];
       }
       __builtin_amdgcn_sched_barrier(0);
       if (ks == 0) {
         __builtin_amdgcn_s_setprio(1);
         __builtin_amdgcn_sched_barrier(0);
+        read_vt(1);
       }
       if constexpr (!PVSKIP) {
 #pragma unroll
@@ -402,9 +408,6 @@ void fmha_block_kernel(FmhaArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int w = 0; w < 8; ++w) l_run += p[2 * w] + p[2 * w + 1];
 
     // The LUT entry of block it+2 is requested only now, after this block's
     // last LDS wait: scalar loads share the LDS wait counter but may return
@@ -450,9 +453,11 @@ void fmha_block_kernel(FmhaArgs a) {
   typedef typename OutType<T, OUT_F32>::type OT;
   constexpr int OG = D * (int)sizeof(OT) / 16;   // 16-byte granules per O row
   const float l_w = l_run + __shfl_xor(l_run, 32, kWave);
-  float* mrg = reinterpret_cast<float*>(sK) + qh * (NMD * 16 * 64);
+  float* mrg = reinterpret_cast<float*>(sV) + qh * (NMD * 16 * 64);
   float* ml = s_ml + qh * 64;
-  char* stg = reinterpret_cast<char*>(sV);
+  // 16-bit rows are staged in the K buffer while the merge reads the V
+  // buffers; fp32 rows (32 KB) go to the V buffers once it has read them.
+  char* stg = OUT_F32 ? reinterpret_cast<char*>(sV) : reinterpret_cast<char*>(sK);
   if (kh == 1) {
 #pragma unroll
     for (int md = 0; md < NMD; ++md)
@@ -489,8 +494,8 @@ void fmha_block_kernel(FmhaArgs a) {
         }
         // Columns 32 md + 8 g + 4 hl .. +3.
         if constexpr (OUT_F32) {
-          const int gr = 8 * md + 2 * g + hl;
-          *reinterpret_cast<floatx4*>(srow + ((gr ^ (tr % OG)) * 16)) = floatx4{x[0], x[1], x[2], x[3]};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc_o[md][4 * g + i] = x[i];
         } else {
           const int gr = 4 * md + g;
           *reinterpret_cast<u32x2*>(srow + ((gr ^ (tr % OG)) * 16) + 8 * hl) =
@@ -499,6 +504,22 @@ void fmha_block_kernel(FmhaArgs a) {
       }
     }
     if (lse_row && hl == 0 && row_ok) lse_row[q0 + l32] = empty ? -INFINITY : (m + __log2f(l_tot)) * kLn2;
+  }
+  if constexpr (OUT_F32) {
+    __syncthreads();
+    if (kh == 0) {
+      const int tr = 32 * qh + l32;
+      char* srow = stg + tr * (OG * 16);
+#pragma unroll
+      for (int md = 0; md < NMD; ++md)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          // Columns 32 md + 8 g + 4 hl .. +3.
+          const int gr = 8 * md + 2 * g + hl;
+          *reinterpret_cast<floatx4*>(srow + ((gr ^ (tr % OG)) * 16)) =
+              floatx4{acc_o[md][4 * g], acc_o[md][4 * g + 1], acc_o[md][4 * g + 2], acc_o[md][4 * g + 3]};
+        }
+    }
   }
   __syncthreads();
   const int nrows = min(64, a.sq - 64 * qt);     // rows of a partial last tile

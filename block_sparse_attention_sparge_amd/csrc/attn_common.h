@@ -86,13 +86,13 @@ __device__ __forceinline__ i32x4 raw_rsrc(const void* base, int bytes) {
   return i32x4{(int)(uint32_t)p, (int)(uint32_t)(p >> 32), bytes, kBufferWord3};
 }
 
-// 16 bytes through a buffer resource at (per-lane 32-bit offset) into LDS at
-// (wave-uniform base) + 16 * lane; an offset at or past the resource's record
-// count delivers zeros.
-__device__ __forceinline__ void dma16_buf(i32x4 rsrc, uint32_t off, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+// 16 bytes through a buffer resource at (per-lane 32-bit offset) + (wave-
+// uniform offset) into LDS at (wave-uniform base) + 16 * lane; an offset at
+// or past the resource's record count delivers zeros.
+__device__ __forceinline__ void dma16_buf(i32x4 rsrc, uint32_t off, uint32_t soff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(lds_base), "v"(off), "s"(rsrc)
+               : "s"(lds_base), "v"(off), "s"(rsrc), "s"(soff)
                : "memory", "m0");
 }
 

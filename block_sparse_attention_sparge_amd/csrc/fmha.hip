@@ -28,11 +28,10 @@
 //     listed block when every one of the tile's 64 query rows scores, over
 //     the block's 64 keys, more than the threshold below that row's running
 //     maximum over the blocks already visited; its P still count in the row
-//     sum.  The four wavefronts post their row maxima to LDS; the block's
-//     closing barrier comes after the softmax, so it publishes them, and
-//     every wave then takes the same decision and runs the block's PV
-//     product from registers (its operands were read from LDS before that
-//     barrier), so the test adds no barrier;
+//     sum.  The four wavefronts post their row maxima to LDS before the
+//     block's first barrier, which publishes them; every wave then takes the
+//     same decision, and a dropped block skips its V^T reads and PV MFMAs,
+//     so the test adds no barrier;
 //   * workgroups are renumbered so that consecutive rows of one head land on
 //     one XCD and share its L2 (aiter 4919 page: workgroups round-robin over
 //     the 8 XCDs by linear id); causal rows are taken last tile first.
@@ -95,9 +94,7 @@ struct OutType<T, true> {
 };
 
 template <class E, int D, bool OUT_F32, bool MASKED, bool PVSKIP>
-// With a pv_threshold the block's V^T operands and P stay in registers past
-// the closing barrier, which does not fit three waves per SIMD.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PVSKIP ? 2 : 3, PVSKIP ? 2 : 3)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void fmha_block_kernel(FmhaArgs a) {
   typedef typename E::T T;
   constexpr int G16 = D / 8;                 // 16-byte granules per K/V row
@@ -110,9 +107,9 @@ void fmha_block_kernel(FmhaArgs a) {
   __shared__ __attribute__((aligned(16))) T sV[2 * TILE];
   __shared__ float s_ml[128];                // (m, l) of the kh = 1 waves, per query half
   // pv_threshold votes: (block maximum, running maximum) of each wave's 32
-  // query rows over its 32 keys, scaled base-2 units; two slots by block
-  // parity, so a block's votes are read while the next block's are written.
-  __shared__ float2v s_vote[PVSKIP ? 256 : 1];
+  // query rows over its 32 keys, scaled base-2 units.  A block's votes are
+  // written before its first barrier and read before its closing one.
+  __shared__ float2v s_vote[PVSKIP ? 128 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -178,13 +175,23 @@ void fmha_block_kernel(FmhaArgs a) {
   // granule (row r, slot sl) holds global granule sl ^ swz(r).  The byte
   // offsets inside a block are the same for every block (the host keeps a
   // block's span below 2^31 bytes).
-  uint32_t koff[NDMA], voff[NDMA];
+  // Instruction j covers rows RPI (wave NDMA + j) .. +RPI-1.  V's swizzle
+  // depends only on r mod 4, so its offsets differ between instructions by
+  // whole rows, which go into the scalar offset; so do K's when each
+  // instruction covers a multiple of G16 rows (d = 64).  For d = 128 K's
+  // swizzle changes with j and each instruction keeps its own lane offset.
+  constexpr int RPI = 64 / G16;                // rows per load instruction
+  constexpr bool K_ROWSTEP = RPI % G16 == 0;
+  static_assert(RPI % 4 == 0, "V swizzle must repeat every load instruction");
+  uint32_t koff[K_ROWSTEP ? 1 : NDMA], voff;
+  {
+    const int r0 = RPI * wave * NDMA + lane / G16, sl = lane % G16;
+    voff = (uint32_t)((r0 * a.vs[2] + (sl ^ ((VSW * r0) % G16)) * 8) * (int64_t)sizeof(T));
 #pragma unroll
-  for (int j = 0; j < NDMA; ++j) {
-    const int gi = 64 * (wave * NDMA + j) + lane;
-    const int r = gi / G16, sl = gi % G16;
-    koff[j] = (uint32_t)((r * a.ks[2] + (sl ^ (r % G16)) * 8) * (int64_t)sizeof(T));
-    voff[j] = (uint32_t)((r * a.vs[2] + (sl ^ ((VSW * r) % G16)) * 8) * (int64_t)sizeof(T));
+    for (int j = 0; j < (K_ROWSTEP ? 1 : NDMA); ++j) {
+      const int r = r0 + RPI * j;
+      koff[j] = (uint32_t)((r * a.ks[2] + (sl ^ (r % G16)) * 8) * (int64_t)sizeof(T));
+    }
   }
   const int krow_b = (int)(a.ks[2] * (int64_t)sizeof(T)), vrow_b = (int)(a.vs[2] * (int64_t)sizeof(T));
   // K of block kb into the K buffer, V into V buffer `buf`.  The resources
@@ -201,10 +208,12 @@ void fmha_block_kernel(FmhaArgs a) {
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
       const uint32_t off = (uint32_t)((wave * NDMA + j) * 64 * 8 * sizeof(T));
-      dma16_buf(kr, koff[j], sk_lds + off);
-      dma16_buf(vr, voff[j], sv_lds + off + (uint32_t)(buf * TILE * sizeof(T)));
+      if constexpr (K_ROWSTEP) dma16_buf(kr, koff[0], (uint32_t)(RPI * j * krow_b), sk_lds + off);
+      else dma16_buf(kr, koff[j], 0u, sk_lds + off);
+      dma16_buf(vr, voff, (uint32_t)(RPI * j * vrow_b), sv_lds + off + (uint32_t)(buf * TILE * sizeof(T)));
     }
   };
+
   // LUT entries come through the scalar cache (the LUT is read-only here).
   const __attribute__((address_space(4))) int32_t* clist = (const __attribute__((address_space(4))) int32_t*)list;
   auto kb_of = [&](int i) { return list ? clist[beg + i] : beg + i; };
@@ -266,14 +275,14 @@ void fmha_block_kernel(FmhaArgs a) {
   int kb_ahead = nloc > 1 ? kb_of(1) : 0;
   int kb_cur = MASKED ? kb_of(0) : 0;
 
-  // pv_threshold: the decision on the block whose votes are in `slot`: query
-  // row i of the tile (lane i) has r_i = its maximum over the block's 64
-  // keys and M_i its running maximum over the blocks visited so far, this
-  // one included; the block is dropped when r_i < M_i - tau for all 64 rows.
-  // Every wave reads the same values and takes the same decision.
-  auto pv_keep_block = [&](int slot) {
+  // pv_threshold: the decision on the current block: query row i of the
+  // tile (lane i) has r_i = its maximum over the block's 64 keys and M_i its
+  // running maximum over the blocks visited so far, this one included; the
+  // block is dropped when r_i < M_i - tau for all 64 rows.  Every wave reads
+  // the same values and takes the same decision.
+  auto pv_keep_block = [&]() {
     const int vq = lane >> 5, vr = lane & 31;
-    const float2v h0 = s_vote[slot * 128 + vq * 32 + vr], h1 = s_vote[slot * 128 + (2 + vq) * 32 + vr];
+    const float2v h0 = s_vote[vq * 32 + vr], h1 = s_vote[(2 + vq) * 32 + vr];
     const float r_i = fmaxf(h0[0], h1[0]), m_i = fmaxf(h0[1], h1[1]);
     return __any(!(r_i < m_i - a.pv_tau2));
   };
@@ -321,35 +330,55 @@ void fmha_block_kernel(FmhaArgs a) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) s = mfma32<E>(kf[kk], qf[kk], s);
     __builtin_amdgcn_sched_barrier(0);
+
+    // The block's row maximum of this lane's 16 scores (scaled, base 2),
+    // after the position mask.
+    auto block_max = [&]() {
+      if constexpr (MASKED) {
+        // Key 64 kb + 32 kh + 8 (r/4) + 4 hl + r%4 of register r against query
+        // 64 qt + 32 qh + l32: keys past the query (causal) and keys past the
+        // end of the sequence are removed.  Only the diagonal block, blocks
+        // past it (listed by hand) and a partial last block can hold any.
+        if (64 * kb_cur + 64 > a.sk || (a.causal && kb_cur >= qt)) {
+          const int qpos = 64 * qt + 32 * qh + l32;
+          const int lim = a.causal ? min(qpos + 1, a.sk) : a.sk;   // first removed key
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = 64 * kb_cur + 32 * kh + 8 * (r >> 2) + 4 * hl + (r & 3);
+            if (key >= lim) s[r] = -INFINITY;
+          }
+        }
+      }
+
+      float rmax = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) rmax = fmaxf(rmax, s[r]);
+      rmax = half_swap_max(rmax);
+      return rmax * c2;
+    };
+    // Online softmax in base 2.  With a pv_threshold the row maxima are
+    // needed before the first barrier, which publishes them as votes;
+    // without one they are taken after it (measured 1% faster).
+    float m_cand = 0.f;
+    if constexpr (PVSKIP) {
+      m_cand = block_max();
+      // This wave's votes on the block, for its 32 query rows over its 32
+      // keys: the block maximum and the running maximum, this block
+      // included; the barrier below publishes them.
+      m_top = fmaxf(m_top, m_cand);
+      if (hl == 0) s_vote[wave * 32 + l32] = float2v{m_cand, m_top};
+    }
     // Every wave has read this block's K: the K buffer, and the V buffer of
     // block it-1 (released by the last closing barrier), take block it+1.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (it + 1 < nloc) issue_block(kb_ahead, 1 - cur);
-    read_vt(0);
+    // With a pv_threshold a dropped block reads no V^T and runs no PV MFMA.
+    bool keep = true;
+    if constexpr (PVSKIP) keep = pv_keep_block();
+    if (keep) read_vt(0);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!PVSKIP) m_cand = block_max();
 
-    if constexpr (MASKED) {
-      // Key 64 kb + 32 kh + 8 (r/4) + 4 hl + r%4 of register r against query
-      // 64 qt + 32 qh + l32: keys past the query (causal) and keys past the
-      // end of the sequence are removed.  Only the diagonal block, blocks
-      // past it (listed by hand) and a partial last block can hold any.
-      if (64 * kb_cur + 64 > a.sk || (a.causal && kb_cur >= qt)) {
-        const int qpos = 64 * qt + 32 * qh + l32;
-        const int lim = a.causal ? min(qpos + 1, a.sk) : a.sk;   // first removed key
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 64 * kb_cur + 32 * kh + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key >= lim) s[r] = -INFINITY;
-        }
-      }
-    }
-
-    // Online softmax in base 2 over this lane's 16 scores.
-    float rmax = s[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) rmax = fmaxf(rmax, s[r]);
-    rmax = half_swap_max(rmax);
-    const float m_cand = rmax * c2;
     const bool need = m_cand > m_run + kRescaleSlack;
     if (__any(need)) {
       const float m_new = need ? m_cand : m_run;
@@ -365,8 +394,8 @@ void fmha_block_kernel(FmhaArgs a) {
     // carried by one key would move the LSE by up to 4e-3 nats.
     // Masked rows may still have no key (m_run = -inf): their P is 0.
     //
-    // O^T += V^T P^T over this wave's 32 keys (with a pv_threshold, after
-    // the barrier, unless the tile drops the block).  The four
+    // O^T += V^T P^T over this wave's 32 keys (unless a pv_threshold drops
+    // the block for the tile).  The four
     // PV MFMAs of k-step 0 are issued as soon as its 8 P values exist, so the
     // exponentials of k-step 1 run in their shadow.  From the first PV MFMA to
     // the last the wave runs at raised priority: of the wavefronts sharing a
@@ -376,14 +405,6 @@ void fmha_block_kernel(FmhaArgs a) {
     // at topk 0.1; the split issue 1% and 2% more; priority on the S MFMAs as
     // well gains nothing).
     const float mref = MASKED && m_run == -INFINITY ? 0.f : m_run;
-    if constexpr (PVSKIP) {
-      // This wave's votes on the block, for its 32 query rows over its 32
-      // keys: the block maximum and the running maximum, this block
-      // included.  Slot `cur` was last read right after the barrier of two
-      // blocks ago, before the previous barrier.
-      m_top = fmaxf(m_top, m_cand);
-      if (hl == 0) s_vote[cur * 128 + wave * 32 + l32] = float2v{m_cand, m_top};
-    }
     u32x4 pf[2];
     float p[16];
 #pragma unroll
@@ -399,9 +420,9 @@ void fmha_block_kernel(FmhaArgs a) {
       if (ks == 0) {
         __builtin_amdgcn_s_setprio(1);
         __builtin_amdgcn_sched_barrier(0);
-        read_vt(1);
+        if (keep) read_vt(1);
       }
-      if constexpr (!PVSKIP) {
+      if (keep) {
 #pragma unroll
         for (int md = 0; md < NMD; ++md) acc_o[md] = mfma32<E>(vf[ks][md], pf[ks], acc_o[md]);
       }
@@ -419,19 +440,6 @@ void fmha_block_kernel(FmhaArgs a) {
     // Block it+1 must have landed before the barrier hands the buffers over.
     wait_dma();
     __syncthreads();
-    if constexpr (PVSKIP) {
-      // Every wave's votes on this block are visible now, and its V^T
-      // operands are in registers (the barrier waited for every LDS read),
-      // so the next block's loads may overwrite its buffers.
-      if (pv_keep_block(cur)) {
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int md = 0; md < NMD; ++md) acc_o[md] = mfma32<E>(vf[ks][md], pf[ks], acc_o[md]);
-        __builtin_amdgcn_s_setprio(0);
-      }
-    }
     if constexpr (MASKED) kb_cur = kb_ahead;
     kb_ahead = kb_next;
   };

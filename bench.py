@@ -381,7 +381,7 @@ def extras(ops, synth, torch, steps, warmup):
     op_ = torch.empty_like(qp)
     lp_ = torch.empty(qp.shape[:3], device=dev)
     fns = {}
-    for tau in (0.0, 2.0, 4.0):
+    for tau in (0.0, 1.0, 2.0, 4.0):
         fns[f"all/{tau}"] = lambda tau=tau: ops.sparse_fmha_fwd(hc.q, hc.k, hc.v, bm["lut"], bm["count"], o=o,
                                                                 lse=l, pv_threshold=tau)
         fns[f"peaked/{tau}"] = lambda tau=tau: ops.sparse_fmha_fwd(qp, kp, vp, lutp, cntp, o=op_, lse=lp_,
@@ -389,9 +389,11 @@ def extras(ops, synth, torch, steps, warmup):
     t = interleaved(fns, steps, warmup, torch)
     pv = {k: median(v) for k, v in t.items()}
     out["pv_skip_headline"] = dict(
-        workload="b2 h32 s16384 d128 fp16, topk 0.4, pv_threshold 0 / 2 / 4; 'peaked' = heads 21..31",
+        workload="b2 h32 s16384 d128 fp16, topk 0.4, pv_threshold 0 / 1 / 2 / 4; 'peaked' = heads 21..31",
         fmha_ms={k: round(v, 4) for k, v in pv.items()},
+        speedup_all_tau1=pv["all/0.0"] / pv["all/1.0"],
         speedup_all_tau2=pv["all/0.0"] / pv["all/2.0"], speedup_all_tau4=pv["all/0.0"] / pv["all/4.0"],
+        speedup_peaked_tau1=pv["peaked/0.0"] / pv["peaked/1.0"],
         speedup_peaked_tau2=pv["peaked/0.0"] / pv["peaked/2.0"],
         speedup_peaked_tau4=pv["peaked/0.0"] / pv["peaked/4.0"])
     del qp, kp, vp, lutp, cntp, op_, lp_

@@ -50,7 +50,7 @@ namespace sparge {
 // 64-key block, keeping its own running maximum, row sum and O^T; the two
 // key halves are merged in LDS at the end (the LSE combine of two partials).
 //
-// Three workgroups share a CU (168 VGPRs, 48.5 KB of LDS each; measured 6-9%
+// Three workgroups share a CU (168 VGPRs, 48.5 KB of LDS each; measured 4-10%
 // faster than two workgroups with both K and V double-buffered, bit-identical).
 // K blocks arrive in one LDS buffer and V blocks in two, by direct loads from
 // memory into LDS (no registers on the way; on gfx950 this path moves
@@ -65,8 +65,8 @@ namespace sparge {
 // the compiler does not guard every LDS read with a wait for them; the kernel
 // waits for them itself (vmcnt) before the closing barrier.
 //   * K is stored row-major with the 16-byte granules of row r XOR-swizzled
-//     by r mod 16, so S^T operand reads of 32 consecutive rows hit distinct
-//     banks.
+//     by r mod G16 (G16 = granules per row: 16 for d = 128), so S^T operand
+//     reads of consecutive rows hit distinct banks.
 //   * V is stored row-major with granules XOR-swizzled by (G16/4) r (4r for
 //     d = 128, 2r for d = 64), and the V^T operand of O^T += V^T P^T is read
 //     with the gfx950 transposing LDS read (ds_read_b64_tr_b16): within each

@@ -107,6 +107,40 @@ __device__ __forceinline__ float half_swap_max(float x) {
   return fmaxf(a, b);
 }
 
+// The order in which the block kernels take their rows.  A row is one Q-tile
+// of one row group (batch, head, split); the 8 XCDs receive workgroups
+// round-robin by id (aiter 4919 page), and each XCD has its own L2.
+//   * Causal launches: each XCD takes a contiguous range of row groups, the
+//     tiles of each last first.  Causal rows grow with the tile index, so an
+//     XCD ends on short rows, and its concurrent rows are neighbouring tiles
+//     of one head, which read nearly the same blocks.
+//   * Otherwise: XCD x takes tiles x, x + 8, x + 16, ... of every row group
+//     in turn, so every XCD gets an equal share of each head whatever its
+//     list lengths (a per-head topk).  With whole heads per XCD the heads of
+//     the per-head topk sweep loaded the XCDs unevenly (measured 0-2.9%
+//     faster on that sweep over three boxes, within 1% elsewhere; on causal
+//     launches 7-20% slower, hence the first order there).
+// block_grid() is the matching grid size; block_row_of() returns false for a
+// workgroup past the end.
+__host__ __device__ inline int64_t block_grid(int nqt, int64_t groups, bool causal) {
+  return causal ? (nqt * groups + 7) / 8 * 8 : 8 * (int64_t)((nqt + 7) / 8) * groups;
+}
+
+__device__ __forceinline__ bool block_row_of(int nqt, int64_t groups, bool causal, int& qt, int64_t& group) {
+  if (causal) {
+    const int64_t lin = xcd_remap(blockIdx.x, gridDim.x);
+    if (lin >= (int64_t)nqt * groups) return false;
+    qt = nqt - 1 - (int)(lin % nqt);
+    group = lin / nqt;
+    return true;
+  }
+  const int per_xcd = (nqt + 7) >> 3;
+  const int64_t j = blockIdx.x >> 3;
+  group = j / per_xcd;
+  qt = (int)(blockIdx.x & 7) + 8 * (int)(j % per_xcd);
+  return group < groups && qt < nqt;
+}
+
 // Compile-time buffer index for the two-way unrolled block loop.
 template <int N>
 struct Buf {

@@ -1,6 +1,7 @@
-// Device helpers shared by the attention kernels (fp16 / bf16 and int8-QK
+// Device helpers shared by the attention kernels (fp16 / bf16 and 8-bit-QK
 // block kernels, token-list kernel): constants, the 32x32 MFMA wrappers, the
-// output store, the direct global->LDS load, the half-wave maximum.
+// output store, the loads from memory straight into LDS, the half-wave
+// maximum, and the order in which the block kernels take their rows.
 #pragma once
 
 #include "common.h"

@@ -32,9 +32,10 @@
 //     block's first barrier, which publishes them; every wave then takes the
 //     same decision, and a dropped block skips its V^T reads and PV MFMAs,
 //     so the test adds no barrier;
-//   * workgroups are renumbered so that consecutive rows of one head land on
-//     one XCD and share its L2 (aiter 4919 page: workgroups round-robin over
-//     the 8 XCDs by linear id); causal rows are taken last tile first.
+//   * rows are dealt to the 8 XCDs (which receive workgroups round-robin by
+//     linear id, aiter 4919 page) so that each gets an equal share of every
+//     head; causal launches give each XCD contiguous heads, last tile first
+//     (block_row_of in attn_common.h).
 // The token-list (decode) kernel is in fmha_tokens.hip.
 #include "attn_common.h"
 #include "common.h"

@@ -357,6 +357,42 @@ def test_fmha_strided_views_and_fp32_out(dev):
     _fmha_vs_oracle(q, k, v, lut, cnt, o, lse)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fmha_strided_views_ragged(dev, d, causal):
+    # Q, K, V as views into a packed (b, s, 3h, d) buffer with a ragged length:
+    # the K/V loads step rows by the packed stride (through the scalar offset
+    # for V, and for K at d = 64), and the last block's buffer records end at
+    # its last existing row of that stride.
+    b, h, s = 1, 3, 1000
+    base = synth.normal((b, s, 3 * h, d), 16 + d, 1, torch.float16, dev)
+    q = base[:, :, 0:h].permute(0, 2, 1, 3)
+    k = base[:, :, h:2 * h].permute(0, 2, 1, 3)
+    v = base[:, :, 2 * h:3 * h].permute(0, 2, 1, 3)
+    nb = (s + 63) // 64
+    lut = cnt = None
+    if not causal:
+        # random ascending rows that all list the ragged last block; 10% empty
+        g = torch.Generator().manual_seed(5 + d)
+        lut = torch.full((b, h, nb, nb), -1, dtype=torch.int32)
+        cnt = torch.zeros((b, h, nb), dtype=torch.int32)
+        for idx in np.ndindex(b, h, nb):
+            if float(torch.rand(1, generator=g)) < 0.1:
+                continue
+            n = int(torch.randint(0, nb, (1,), generator=g))
+            sel = sorted(torch.randperm(nb - 1, generator=g)[:n].tolist() + [nb - 1])
+            lut[idx][:len(sel)] = torch.tensor(sel, dtype=torch.int32)
+            cnt[idx] = len(sel)
+        lut, cnt = lut.to(dev), cnt.to(dev)
+    o, lse = ops.sparse_fmha_fwd(q, k, v, lut, cnt, causal=causal)
+    _sync()
+    ro, rl = oracle.block_sparse_attention(np64(q), np64(k), np64(v),
+                                           None if lut is None else lut.cpu().numpy(),
+                                           None if cnt is None else cnt.cpu().numpy(), causal=causal)
+    check_o(o, ro)
+    check_lse(lse, rl)
+
+
 def _packed_qk(dev, b, h, s, d, seed):
     """Q and K as views into a packed (b, s, 3h, d) buffer, the layout a fused
     QKV projection writes: sequence stride 3hd, head stride d."""

@@ -65,7 +65,7 @@ __device__ __forceinline__ int k8_swz(int r) {
 }
 
 template <class E, int D, bool OUT_F32, bool MASKED, bool FP8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void fmha_qk8_kernel(FmhaArgs a) {
   typedef typename E::T T;
   constexpr int G16 = D / 8;                 // 16-byte granules per V row
@@ -142,48 +142,40 @@ void fmha_qk8_kernel(FmhaArgs a) {
   const uint32_t sk_lds = (uint32_t)(uintptr_t)((SPARGE_LDS void*)sK);
   const uint32_t sv_lds = (uint32_t)(uintptr_t)((SPARGE_LDS void*)sV);
 
-  uint32_t koff[NDMA_K], voff[NDMA_V];
+  // V's swizzle depends only on r mod 4, so V's lane offsets differ between
+  // load instructions by whole rows, which go into the scalar offset.
+  constexpr int RPI_V = 64 / G16;              // V rows per load instruction
+  static_assert(RPI_V % 4 == 0, "V swizzle must repeat every load instruction");
+  uint32_t koff[NDMA_K], voff;
 #pragma unroll
   for (int j = 0; j < NDMA_K; ++j) {
     const int gi = 64 * (wave * NDMA_K + j) + lane;
     const int r = gi / GK, sl = gi % GK;
     koff[j] = (uint32_t)(r * a.ks[2] + (sl ^ k8_swz<GK>(r)) * 16);
   }
-#pragma unroll
-  for (int j = 0; j < NDMA_V; ++j) {
-    const int gi = 64 * (wave * NDMA_V + j) + lane;
-    const int r = gi / G16, sl = gi % G16;
-    voff[j] = (uint32_t)((r * a.vs[2] + (sl ^ ((VSW * r) % G16)) * 8) * (int64_t)sizeof(T));
+  {
+    const int r0 = RPI_V * wave * NDMA_V + lane / G16, sl = lane % G16;
+    voff = (uint32_t)((r0 * a.vs[2] + (sl ^ ((VSW * r0) % G16)) * 8) * (int64_t)sizeof(T));
   }
+  const int krow_b = (int)a.ks[2], vrow_b = (int)(a.vs[2] * (int64_t)sizeof(T));
+  // K codes of block kb into K buffer `buf`, V into V buffer `buf`, through
+  // buffer resources that cover the block's existing rows: rows past the end
+  // of a ragged K sequence read as zeros (their scores are removed below).
   auto issue_block = [&](int kb, int buf) {
-    const char* kp = kbase + kb * kblk;
-    const char* vp = vbase + kb * vblk;
-    if (MASKED && 64 * kb + 64 > a.sk) {
-      // The last block of a ragged K sequence: LDS row r takes global row
-      // min(r, last), swizzled for its own position r.
-      const int last = a.sk - 1 - 64 * kb;
-#pragma unroll
-      for (int j = 0; j < NDMA_K; ++j) {
-        const int gi = 64 * (wave * NDMA_K + j) + lane;
-        const int r = gi / GK, sl = gi % GK, rc = min(r, last);
-        dma16(kp, (uint32_t)(rc * a.ks[2] + (sl ^ k8_swz<GK>(r)) * 16),
-              sk_lds + (uint32_t)(buf * TILE + (wave * NDMA_K + j) * 64 * 16));
-      }
-#pragma unroll
-      for (int j = 0; j < NDMA_V; ++j) {
-        const int gi = 64 * (wave * NDMA_V + j) + lane;
-        const int r = gi / G16, sl = gi % G16, rc = min(r, last);
-        dma16(vp, (uint32_t)((rc * a.vs[2] + (sl ^ ((VSW * r) % G16)) * 8) * (int64_t)sizeof(T)),
-              sv_lds + (uint32_t)((buf * TILE + (wave * NDMA_V + j) * 64 * 8) * sizeof(T)));
-      }
-      return;
+    int krec = (int)kblk, vrec = (int)vblk;
+    if constexpr (MASKED) {
+      const int rows = min(64, a.sk - 64 * kb);
+      krec = rows * krow_b;
+      vrec = rows * vrow_b;
     }
+    const i32x4 kr = raw_rsrc(kbase + kb * kblk, krec), vr = raw_rsrc(vbase + kb * vblk, vrec);
 #pragma unroll
     for (int j = 0; j < NDMA_K; ++j)
-      dma16(kp, koff[j], sk_lds + (uint32_t)(buf * TILE + (wave * NDMA_K + j) * 64 * 16));
+      dma16_buf(kr, koff[j], 0u, sk_lds + (uint32_t)(buf * TILE + (wave * NDMA_K + j) * 64 * 16));
 #pragma unroll
     for (int j = 0; j < NDMA_V; ++j)
-      dma16(vp, voff[j], sv_lds + (uint32_t)((buf * TILE + (wave * NDMA_V + j) * 64 * 8) * sizeof(T)));
+      dma16_buf(vr, voff, (uint32_t)(RPI_V * j * vrow_b),
+                sv_lds + (uint32_t)((buf * TILE + (wave * NDMA_V + j) * 64 * 8) * sizeof(T)));
   };
   const __attribute__((address_space(4))) int32_t* clist = (const __attribute__((address_space(4))) int32_t*)list;
   auto kb_of = [&](int i) { return list ? clist[beg + i] : beg + i; };

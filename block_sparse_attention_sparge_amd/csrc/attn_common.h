@@ -111,27 +111,39 @@ __device__ __forceinline__ float half_swap_max(float x) {
 // The order in which the block kernels take their rows.  A row is one Q-tile
 // of one row group (batch, head, split); the 8 XCDs receive workgroups
 // round-robin by id (aiter 4919 page), and each XCD has its own L2.
-//   * Causal launches: each XCD takes a contiguous range of row groups, the
-//     tiles of each last first.  Causal rows grow with the tile index, so an
-//     XCD ends on short rows, and its concurrent rows are neighbouring tiles
-//     of one head, which read nearly the same blocks.
-//   * Otherwise: XCD x takes tiles x, x + 8, x + 16, ... of every row group
+//   * Contiguous: each XCD takes a contiguous range of row groups, so its
+//     concurrent rows are tiles of one head, which share that head's K/V in
+//     its L2.  Causal launches take each group's tiles last first: causal
+//     rows grow with the tile index, so an XCD ends on short rows.
+//   * Interleaved: XCD x takes tiles x, x + 8, x + 16, ... of every row group
 //     in turn, so every XCD gets an equal share of each head whatever its
 //     list lengths (a per-head topk).  With whole heads per XCD the heads of
 //     the per-head topk sweep loaded the XCDs unevenly (measured 0-2.9%
-//     faster on that sweep over three boxes, within 1% elsewhere; on causal
-//     launches 7-20% slower, hence the first order there).
-// block_grid() is the matching grid size; block_row_of() returns false for a
-// workgroup past the end.
+//     faster on that sweep over three boxes, within 1% elsewhere).
+// Launches of at least kInterleaveRows rows (several rounds of resident
+// workgroups) are interleaved, unless causal: dealt like the others, causal
+// launches ran 7-20% slower, and so did a one-round launch (b1 h8 s4096,
+// 512 rows: 9%), whose balance across XCDs does not matter and whose L2
+// then holds eight heads' K/V instead of one.
+constexpr int64_t kInterleaveRows = 4096;
+
+__host__ __device__ inline bool block_interleaved(int nqt, int64_t groups, bool causal) {
+  return !causal && (int64_t)nqt * groups >= kInterleaveRows;
+}
+
+// block_grid() is the grid size for the order; block_row_of() returns false
+// for a workgroup past the end.
 __host__ __device__ inline int64_t block_grid(int nqt, int64_t groups, bool causal) {
-  return causal ? (nqt * groups + 7) / 8 * 8 : 8 * (int64_t)((nqt + 7) / 8) * groups;
+  return block_interleaved(nqt, groups, causal) ? 8 * (int64_t)((nqt + 7) / 8) * groups
+                                                : ((int64_t)nqt * groups + 7) / 8 * 8;
 }
 
 __device__ __forceinline__ bool block_row_of(int nqt, int64_t groups, bool causal, int& qt, int64_t& group) {
-  if (causal) {
+  if (!block_interleaved(nqt, groups, causal)) {
     const int64_t lin = xcd_remap(blockIdx.x, gridDim.x);
     if (lin >= (int64_t)nqt * groups) return false;
-    qt = nqt - 1 - (int)(lin % nqt);
+    const int t = (int)(lin % nqt);
+    qt = causal ? nqt - 1 - t : t;
     group = lin / nqt;
     return true;
   }

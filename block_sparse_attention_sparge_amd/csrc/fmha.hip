@@ -34,8 +34,8 @@
 //     so the test adds no barrier;
 //   * rows are dealt to the 8 XCDs (which receive workgroups round-robin by
 //     linear id, aiter 4919 page) so that each gets an equal share of every
-//     head; causal launches give each XCD contiguous heads, last tile first
-//     (block_row_of in attn_common.h).
+//     head; causal and one-round launches give each XCD contiguous heads
+//     instead, causal ones last tile first (block_row_of in attn_common.h).
 // The token-list (decode) kernel is in fmha_tokens.hip.
 #include "attn_common.h"
 #include "common.h"

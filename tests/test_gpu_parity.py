@@ -393,6 +393,37 @@ def test_fmha_strided_views_ragged(dev, d, causal):
     check_lse(lse, rl)
 
 
+@pytest.mark.parametrize("h,s,d", [(66, 4000, 64), (64, 4096, 128)])
+def test_fmha_row_order_invariance(dev, h, s, d):
+    # A launch of at least 4096 rows deals its tiles across the XCDs (every
+    # eighth tile of each head per XCD; with 63 tiles per head some workgroups
+    # of the grid have no tile); each half of it, by heads, runs in
+    # contiguous order.  A row's arithmetic does not depend on the order, so
+    # the outputs are bit-identical; a few rows are checked against the
+    # oracle as well.
+    b = 1
+    nb = (s + 63) // 64
+    assert nb * h >= 4096 and nb * (h // 2) < 4096
+    q = synth.normal((b, h, s, d), 40 + d, 1, torch.float16, dev, scale=1.5)
+    k = synth.normal((b, h, s, d), 40 + d, 2, torch.float16, dev, scale=1.5)
+    v = synth.normal((b, h, s, d), 40 + d, 3, torch.float16, dev)
+    lut, cnt = _random_lut(b, h, nb, nb, nb, seed=7 + d, p_empty=0.05, dev=dev)
+    o, lse = ops.sparse_fmha_fwd(q, k, v, lut, cnt)
+    hh = h // 2
+    halves = [ops.sparse_fmha_fwd(q[:, sl].contiguous(), k[:, sl].contiguous(), v[:, sl].contiguous(),
+                                  lut[:, sl].contiguous(), cnt[:, sl].contiguous())
+              for sl in (slice(0, hh), slice(hh, h))]
+    _sync()
+    assert torch.equal(o, torch.cat([halves[0][0], halves[1][0]], dim=1))
+    assert torch.equal(lse, torch.cat([halves[0][1], halves[1][1]], dim=1))
+    for ih in (0, h - 1):
+        sl = slice(ih, ih + 1)
+        ro, rl = oracle.block_sparse_attention(np64(q[:, sl]), np64(k[:, sl]), np64(v[:, sl]),
+                                               lut[:, sl].cpu().numpy(), cnt[:, sl].cpu().numpy())
+        check_o(o[:, sl], ro)
+        check_lse(lse[:, sl], rl)
+
+
 def _packed_qk(dev, b, h, s, d, seed):
     """Q and K as views into a packed (b, s, 3h, d) buffer, the layout a fused
     QKV projection writes: sequence stride 3hd, head stride d."""

@@ -95,7 +95,10 @@ struct OutType<T, true> {
 };
 
 template <class E, int D, bool OUT_F32, bool MASKED, bool PVSKIP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+// Three waves per SIMD at d = 128 (168 VGPRs), four at d = 64.  The hint
+// shapes the compiler's schedule as well as its register budget: d = 64 runs
+// 3-13% faster for (4, 4) than for (3, 3) at the same register count.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 3, D == 64 ? 4 : 3)))
 void fmha_block_kernel(FmhaArgs a) {
   typedef typename E::T T;
   constexpr int G16 = D / 8;                 // 16-byte granules per K/V row

@@ -257,6 +257,43 @@ def test_int8_end_to_end(dev, causal, dtype, d):
     check_lse(lse, rl)
 
 
+def _nan_padded(x):
+    """x viewed at the start of a buffer that holds whole 64-row blocks; the
+    elements past x are NaN."""
+    b, h, s, d = x.shape
+    assert b * h == 1
+    buf = torch.full((-(-s // 64) * 64 * d,), float("nan"), dtype=x.dtype, device=x.device)
+    buf[: s * d] = x.reshape(-1)
+    return buf[: s * d].view(b, h, s, d)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype,d", [(torch.float16, 128), (torch.bfloat16, 64)])
+def test_fmha_tail_rows_read_as_zeros(dev, causal, dtype, d):
+    # K and V sit at the start of buffers whose elements past the sequence
+    # are NaN.  The missing rows of the last 64-key block must arrive as
+    # zeros (the loads' range check ends at the last existing row), never as
+    # the NaN behind them: P = 0 times NaN would make O NaN.
+    s = 1000
+    q, k, v = _qkv(dev, 1, 1, 1, s, s, d, dtype, 71)
+    k, v = _nan_padded(k), _nan_padded(v)
+    o, lse = ops.sparse_fmha_fwd(q, k, v, None, None, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and not torch.isnan(lse).any()
+    ro, rl = oracle.block_sparse_attention(np64(q), np64(k), np64(v), None, None, causal=causal)
+    check_o(o, ro)
+    check_lse(lse, rl)
+    bm = ops.build_block_map(q, k, [1.0], [0.001], causal=causal, quantize_int8=True)
+    o8, l8 = ops.sparse_fmha_fwd_qk_int8(bm["q_i8"], bm["q_i8_scale"], bm["k_i8"], bm["k_i8_scale"], v,
+                                         bm["lut"], bm["count"], causal=causal)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o8).all() and not torch.isnan(l8).any()
+    ro8, rl8 = oracle.block_sparse_attention_qk_int8(np64(q), np64(k), np64(v), bm["lut"].cpu().numpy(),
+                                                     bm["count"].cpu().numpy(), causal=causal)
+    check_o(o8, ro8)
+    check_lse(l8, rl8)
+
+
 @pytest.mark.parametrize("s_q,s_k", [(200, 333), (1, 64), (130, 65)])
 def test_int8_dense_ragged_shapes(dev, s_q, s_k):
     q, k, v = _qkv(dev, 1, 4, 2, s_q, s_k, 128, torch.float16, 61)

@@ -20,10 +20,11 @@
 //                (probability descending, block index ascending), the four
 //                rows of each wavefront interleaved step by step:
 //                top-k finds the n-th largest probability by a radix select
-//                on its bits (bisection for rows of at most 128 blocks) and
-//                takes ties at it by ascending index; cdf needs the order
-//                itself and sorts the row with a 64-bit-key bitonic network.  The ascending LUT is written by
-//                a prefix scan (no atomics, so the output is deterministic).
+//                on its bits and takes ties at it by ascending index; cdf
+//                needs the order itself and sorts the row with a 64-bit-key
+//                bitonic network.  The ascending LUT is written by a prefix
+//                scan (no atomic slot assignment, so the output is
+//                deterministic).
 #include "common.h"
 #include "kernels.h"
 
@@ -297,6 +298,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   __shared__ __attribute__((aligned(16))) float s_score[kSelRows][SP];
   __shared__ uint8_t s_sel[kSelRows][NKP];
   __shared__ float s_sorted[4][NKP];
+  // Radix-select histograms of rows too short to hold 256 bins in their own
+  // s_score row (nk <= 128).
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[KPL < 4 ? kSelRows : 1][KPL < 4 ? 256 : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -462,91 +466,73 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     // top-k: T = the n-th largest probability (bits).  Probabilities are >= +0,
     // so their bit patterns order like their values.
     uint32_t thr_bits[RW];
-    if constexpr (KPL >= 4) {
-      // Radix select from the most significant byte, four rounds: a histogram
-      // of the next byte over the keys that share the bytes decided so far,
-      // then a prefix count over the 256 bins, largest byte first, finds the
-      // byte of the n-th largest and how many keys lie above it.  Each wave
-      // keeps its rows' histograms in its own rows of s_score (256 bins fit,
-      // and in this mode the scores are in registers by now), built with LDS
-      // atomics; bin 255 - byte, so lane l holds the bins of bytes
-      // 255 - 4l .. 252 - 4l and the count from the top is a prefix sum over
-      // the lanes (DPP row shifts and row broadcasts, no LDS traffic).
-      uint32_t rank[RW];
+    // Radix select from the most significant byte, four rounds: a histogram
+    // of the next byte over the keys that share the bytes decided so far,
+    // then a prefix count over the 256 bins, largest byte first, finds the
+    // byte of the n-th largest and how many keys lie above it.  Each wave
+    // keeps its rows' histograms in its own rows of s_score when 256 bins fit
+    // there (nk > 128; in this mode the scores are in registers by now), in
+    // s_hist otherwise, built with LDS atomics; bin 255 - byte, so lane l
+    // holds the bins of bytes 255 - 4l .. 252 - 4l and the count from the top
+    // is a prefix sum over the lanes (DPP row shifts and row broadcasts, no
+    // LDS traffic).
+    auto hist_row = [&](int i) -> uint32_t* {
+      if constexpr (KPL >= 4) return reinterpret_cast<uint32_t*>(&s_score[4 * i + wave][0]);
+      else return &s_hist[4 * i + wave][0];
+    };
+    uint32_t rank[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      thr_bits[i] = 0u;
+      rank[i] = (uint32_t)min(nsel_h, limit[i]);
+    }
+#pragma unroll 1
+    for (int rnd = 0; rnd < 4; ++rnd) {
+      const int shift = 24 - 8 * rnd;
+      const uint32_t pmask = rnd == 0 ? 0u : 0xFFFFFFFFu << (shift + 8);
+#pragma unroll
+      for (int i = 0; i < RW; ++i)
+        reinterpret_cast<u32x4*>(hist_row(i))[lane] = u32x4{0u, 0u, 0u, 0u};
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int i = 0; i < RW; ++i) {
-        thr_bits[i] = 0u;
-        rank[i] = (uint32_t)min(nsel_h, limit[i]);
-      }
-#pragma unroll 1
-      for (int rnd = 0; rnd < 4; ++rnd) {
-        const int shift = 24 - 8 * rnd;
-        const uint32_t pmask = rnd == 0 ? 0u : 0xFFFFFFFFu << (shift + 8);
+        uint32_t* hist = hist_row(i);
 #pragma unroll
-        for (int i = 0; i < RW; ++i)
-          reinterpret_cast<u32x4*>(&s_score[4 * i + wave][0])[lane] = u32x4{0u, 0u, 0u, 0u};
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int i = 0; i < RW; ++i) {
-          uint32_t* hist = reinterpret_cast<uint32_t*>(&s_score[4 * i + wave][0]);
-#pragma unroll
-          for (int j = 0; j < KPL; ++j) {
-            const uint32_t pb = __builtin_bit_cast(uint32_t, p[i][j]);
-            if (valid[j] && (pb & pmask) == thr_bits[i]) atomicAdd(&hist[255u - ((pb >> shift) & 255u)], 1u);
-          }
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int i = 0; i < RW; ++i) {
-          const u32x4 h = reinterpret_cast<const u32x4*>(&s_score[4 * i + wave][0])[lane];
-          const int lsum = (int)(h[0] + h[1] + h[2] + h[3]);
-          const int pre = wave_prefix_sum_dpp(lsum);          // keys with byte >= 252 - 4 lane
-          // The first lane whose prefix reaches the rank holds the byte.
-          const int L = (int)__builtin_amdgcn_readfirstlane(
-              (int)__builtin_ctzll(__ballot(pre >= (int)rank[i])));
-          int cum = pre - lsum, byte = 0, above = 0;
-          if (cum + (int)h[0] >= (int)rank[i]) {
-            byte = 255 - 4 * lane;
-            above = cum;
-          } else if (cum + (int)(h[0] + h[1]) >= (int)rank[i]) {
-            byte = 254 - 4 * lane;
-            above = cum + (int)h[0];
-          } else if (cum + (int)(h[0] + h[1] + h[2]) >= (int)rank[i]) {
-            byte = 253 - 4 * lane;
-            above = cum + (int)(h[0] + h[1]);
-          } else {
-            byte = 252 - 4 * lane;
-            above = cum + (int)(h[0] + h[1] + h[2]);
-          }
-          thr_bits[i] |= (uint32_t)__builtin_amdgcn_readlane(byte, L) << shift;
-          rank[i] -= (uint32_t)__builtin_amdgcn_readlane(above, L);
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-      }
-    } else {
-      // Short rows (nk <= 128): bisection on count(>= lo) >= n > count(>= hi);
-      // 31 halvings close a range of 2^31.
-      uint32_t lo[RW], hi[RW];
-#pragma unroll
-      for (int i = 0; i < RW; ++i) { lo[i] = 0u; hi[i] = 0x7F800000u; }
-#pragma unroll 1
-      for (int round = 0; round < 31; ++round) {
-#pragma unroll
-        for (int i = 0; i < RW; ++i) {
-          const uint32_t mid = lo[i] + ((hi[i] - lo[i]) >> 1);
-          int c = 0;
-#pragma unroll
-          for (int j = 0; j < KPL; ++j)
-            c += __popcll(__ballot(valid[j] && __builtin_bit_cast(uint32_t, p[i][j]) >= mid));
-          if (c >= min(nsel_h, limit[i])) lo[i] = mid;
-          else hi[i] = mid;
+        for (int j = 0; j < KPL; ++j) {
+          const uint32_t pb = __builtin_bit_cast(uint32_t, p[i][j]);
+          if (valid[j] && (pb & pmask) == thr_bits[i]) atomicAdd(&hist[255u - ((pb >> shift) & 255u)], 1u);
         }
       }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int i = 0; i < RW; ++i) thr_bits[i] = lo[i];
+      for (int i = 0; i < RW; ++i) {
+        const u32x4 h = reinterpret_cast<const u32x4*>(hist_row(i))[lane];
+        const int lsum = (int)(h[0] + h[1] + h[2] + h[3]);
+        const int pre = wave_prefix_sum_dpp(lsum);          // keys with byte >= 252 - 4 lane
+        // The first lane whose prefix reaches the rank holds the byte.
+        const int L = (int)__builtin_amdgcn_readfirstlane(
+            (int)__builtin_ctzll(__ballot(pre >= (int)rank[i])));
+        int cum = pre - lsum, byte = 0, above = 0;
+        if (cum + (int)h[0] >= (int)rank[i]) {
+          byte = 255 - 4 * lane;
+          above = cum;
+        } else if (cum + (int)(h[0] + h[1]) >= (int)rank[i]) {
+          byte = 254 - 4 * lane;
+          above = cum + (int)h[0];
+        } else if (cum + (int)(h[0] + h[1] + h[2]) >= (int)rank[i]) {
+          byte = 253 - 4 * lane;
+          above = cum + (int)(h[0] + h[1]);
+        } else {
+          byte = 252 - 4 * lane;
+          above = cum + (int)(h[0] + h[1] + h[2]);
+        }
+        thr_bits[i] |= (uint32_t)__builtin_amdgcn_readlane(byte, L) << shift;
+        rank[i] -= (uint32_t)__builtin_amdgcn_readlane(above, L);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
     }
 #pragma unroll
     for (int i = 0; i < RW; ++i) {

@@ -344,10 +344,21 @@ void fmha_block_kernel(FmhaArgs a) {
         if (64 * kb_cur + 64 > a.sk || (a.causal && kb_cur >= qt)) {
           const int qpos = 64 * qt + 32 * qh + l32;
           const int lim = a.causal ? min(qpos + 1, a.sk) : a.sk;   // first removed key
+          if constexpr (!PVSKIP) {
+            // One value per lane against immediate offsets: this form left
+            // the masked kernel 20 fewer bytes of spills (outside the loop)
+            // and ran 0.5-3% faster; with a pv_threshold it spilled inside
+            // the loop, so that variant keeps the per-key form below.
+            const int rel = lim - (64 * kb_cur + 32 * kh + 4 * hl);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 64 * kb_cur + 32 * kh + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (key >= lim) s[r] = -INFINITY;
+            for (int r = 0; r < 16; ++r)
+              if (8 * (r >> 2) + (r & 3) >= rel) s[r] = -INFINITY;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = 64 * kb_cur + 32 * kh + 8 * (r >> 2) + 4 * hl + (r & 3);
+              if (key >= lim) s[r] = -INFINITY;
+            }
           }
         }
       }

@@ -12,7 +12,9 @@ The same line carries:
   * interleaved arms at topk 0.1, 0.2, 0.4, 0.6, 0.8 and the mixed per-head
     sweep, and the dense FMHA baseline (the same kernel, every block);
   * the roofline of the sparse FMHA kernel, from HIP events around each of
-    its launches in the timed region;
+    its launches in the timed region, with two ceilings measured beside it
+    (the fp16 MFMA rate on realistic operands, and a loop of the FMHA's
+    instruction volume without its dependences);
   * rows outside the headline: the b1 h8 s4096 bf16 config, the two-pass
     combine, the combine on headline-sized partials and the split-K decode
     (short launch sequences timed as HIP graphs, warm and with the caches
@@ -462,6 +464,50 @@ def extras(ops, synth, torch, steps, warmup):
 ARMS = ("0.1", "0.2", "0.4", "0.6", "0.8", "mixed")
 
 
+def attainable(torch, achieved):
+    """Ceilings measured live beside the FMHA, from libsparge_probe.so (the
+    kernels of csrc/ceiling_probe.hip, three workgroups per CU like the
+    FMHA): the fp16 MFMA rate on zero-mean operands held in registers, and
+    the rate of a loop with the FMHA's per-wavefront volume per 64-key block
+    (16 MFMAs, 16 KB of LDS reads feeding them, 8 KB of LDS writes, the
+    softmax's VALU work) but none of its dependences, barriers or memory."""
+    import ctypes
+    from block_sparse_attention_sparge_amd import build as _build
+    if not os.path.exists(_build.PROBE_LIB):
+        raise RuntimeError(f"{_build.PROBE_LIB} not found: build it with "
+                           "`python -m block_sparse_attention_sparge_amd.build`")
+    lib = ctypes.CDLL(_build.PROBE_LIB)
+    lib.sparge_probe_launch.restype = ctypes.c_int
+    lib.sparge_probe_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.sparge_probe_flops.restype = ctypes.c_double
+    lib.sparge_probe_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    wg = 3 * torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 2000
+    out = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for kind, name in ((0, "mfma_only"), (1, "loop_volume")):
+        def launch():
+            rc = lib.sparge_probe_launch(kind, wg, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream))
+            if rc != 0:
+                raise RuntimeError(f"sparge_probe_launch({name}) failed: hip error {rc}")
+        for _ in range(2):
+            launch()
+        ts = []
+        for _ in range(7):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            launch()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        res[f"{name}_tflops"] = round(lib.sparge_probe_flops(wg, iters) / (median(ts) * 1e-3) / 1e12, 1)
+    res["frac_of_mfma_only"] = round(achieved / res["mfma_only_tflops"], 4)
+    res["frac_of_loop_volume"] = round(achieved / res["loop_volume_tflops"], 4)
+    res["probe"] = f"csrc/ceiling_probe.hip, {wg} workgroups x 4 wavefronts x {iters} iterations of 16 MFMAs"
+    return res
+
+
 def _topk_of(name):
     from block_sparse_attention_sparge_amd import synth
     return synth.mixed_topk(H) if name == "mixed" else [float(name)] * H
@@ -563,7 +609,8 @@ def main(argv=None) -> int:
                      "traffic": None if traffic is None else round(traffic),
                      "kernel": "fmha_block_kernel (sparse_fmha_fwd)",
                      "flops_per_launch": F_BLK * pairs, "pairs": pairs,
-                     "avg_launch_ms": round(fmha_mean, 4)},
+                     "avg_launch_ms": round(fmha_mean, 4),
+                     "attainable": attainable(torch, act)},
         "step_wall_ms": round(step_wall, 4),
         "arms": {},
         "dense_fmha_ms": round(dense_ms, 4),

@@ -1,4 +1,6 @@
-"""Build libsparge.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc.
+"""Build libsparge.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc,
+and libsparge_probe.so (the benchmark's throughput probes, not part of the
+attention path).
 
 Usage: python -m block_sparse_attention_sparge_amd.build [--jobs N]
 """
@@ -17,6 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparge.so")
 SOURCES = ["abi.hip", "block_map.hip", "fmha.hip", "fmha_qk8.hip", "fmha_tokens.hip", "combine.hip"]
+PROBE_LIB = os.path.join(PKG, "libsparge_probe.so")
+PROBE_SOURCES = ["ceiling_probe.hip"]
 # Per-source flags.  The fp16/bf16 FMHA takes NaN-free inputs as given (NaN
 # inputs are undefined there), which lets its row maxima drop the
 # NaN-quieting copies in front of every max (10 fewer VALU operations per
@@ -50,18 +54,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 4, verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(lib)} failed:\n{r.stderr}")
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {lib}")
+
+
+def build(jobs: int = 4, verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB, verbose)
     return LIB
 
 

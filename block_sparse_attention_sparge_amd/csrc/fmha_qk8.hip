@@ -296,11 +296,12 @@ void fmha_qk8_kernel(FmhaArgs a) {
       if (64 * kb_cur + 64 > a.sk || (a.causal && kb_cur >= qt)) {
         const int qpos = 64 * qt + 32 * qh + l32;
         const int lim = a.causal ? min(qpos + 1, a.sk) : a.sk;   // first removed key
+        // Register r holds key base + 8 (r / 4) + r % 4: one value per lane
+        // against immediate offsets.
+        const int rel = lim - (64 * kb_cur + 32 * kh + 4 * hl);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 64 * kb_cur + 32 * kh + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key >= lim) s[r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + (r & 3) >= rel) s[r] = -INFINITY;
       }
     }
 

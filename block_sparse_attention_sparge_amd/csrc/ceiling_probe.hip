@@ -19,8 +19,8 @@
 //         the A operands of the 16 MFMAs (K for S, V^T for PV);
 //       - 8 ds_write_b128 (8 KB: one wavefront's share of the 32 KB of K and
 //         V that a block's loads write into LDS);
-//       - the softmax's VALU work on registers of its own: 8 max3, 16 fma,
-//         16 exp2, 8 cvt_pk and 16 add.
+//       - the softmax's VALU work on registers of its own: 7 max3 and a max,
+//         16 fma, 16 exp2, 8 cvt_pk and 16 add.
 //     No barriers, no global memory, and no MFMA waits for the softmax.
 //     The FMHA runs the same volume with all of those, so its throughput
 //     over this one says how much its dependences and memory cost.

@@ -24,6 +24,7 @@ The same line carries:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
        python bench.py --profile-arm {0.1,...,mixed,dense} --steps K --warmup W
+       python bench.py --ceilings-only
 """
 from __future__ import annotations
 
@@ -502,8 +503,9 @@ def attainable(torch, achieved):
             b.synchronize()
             ts.append(a.elapsed_time(b))
         res[f"{name}_tflops"] = round(lib.sparge_probe_flops(wg, iters) / (median(ts) * 1e-3) / 1e12, 1)
-    res["frac_of_mfma_only"] = round(achieved / res["mfma_only_tflops"], 4)
-    res["frac_of_loop_volume"] = round(achieved / res["loop_volume_tflops"], 4)
+    if achieved is not None:
+        res["frac_of_mfma_only"] = round(achieved / res["mfma_only_tflops"], 4)
+        res["frac_of_loop_volume"] = round(achieved / res["loop_volume_tflops"], 4)
     res["probe"] = f"csrc/ceiling_probe.hip, {wg} workgroups x 4 wavefronts x {iters} iterations of 16 MFMAs"
     return res
 
@@ -520,6 +522,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true", help="skip the rows outside the headline")
+    ap.add_argument("--ceilings-only", action="store_true",
+                    help="run only the two throughput probes of roofline.attainable (for profiler runs)")
     ap.add_argument("--profile-arm", choices=ARMS + ("dense",), default=None,
                     help="run only warmup + steps headline steps of this arm (for profiler runs)")
     args = ap.parse_args(argv)
@@ -527,6 +531,10 @@ def main(argv=None) -> int:
         print(f"bench.py runs on one GPU only: this path has no multi-GPU mode (--gpus {args.gpus}).",
               file=sys.stderr)
         return 2
+    if args.ceilings_only:
+        import torch
+        print(json.dumps({"attainable": attainable(torch, None)}), flush=True)
+        return 0
     cpu = None
     if not args.no_cpu and args.profile_arm is None:
         # Before the GPU is touched: the workers are forked.
